@@ -1,0 +1,17 @@
+"""CPU oracle for the TokenGate pruned-prefill hot path (test infrastructure).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It shares no code with the HIP library.
+"""
+
+from .tokengate_oracle import (  # noqa: F401
+    LOG2E,
+    gate_score,
+    gated_layer,
+    gather_kept,
+    keybias_attention,
+    kept_counts,
+    rope,
+    silu,
+    topk_select,
+)

@@ -1,0 +1,284 @@
+"""TokenGate pruned-prefill oracle: plain, slow, obviously correct CPU reference.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module.  The product path (the
+HIP library and its Python binding) never imports, calls or links it, and it
+imports nothing from the product path.
+
+Everything is computed in float64 with numpy.  There is no blocking, fusion or
+reordering beyond what each definition states, apart from chunking the gate
+over rows and the attention over (sequence, head, 512 query rows), which does
+not change any result.
+
+Sources.  The method is described by the TokenGate news pages:
+  [ES] "Investigadores de Stanford y UC Berkeley Presentan TokenGate: La
+       Atención con Compuertas por Token Hace el Prefill de Contexto Largo
+       Hasta 11.3x Más Rápido" (spke.com, Spanish edition of the MarkTechPost
+       article).
+  [GR] "TokenGate: το μοντέλο που διαβάζει στα πεταχτά μακριά κείμενα…"
+       (mainews.gr).
+  [RU] "Researchers from Stanford and UC Berkeley introduce TokenGate"
+       (aikraft.ru), section "Техническая реализация".
+The pages leave several details open; the readings used here are stated in
+each function's docstring.
+
+Parity status per function:
+  gate_score          pinned (torch fp64 linear+silu, closed forms, scalar loop)
+  topk_select         pinned (brute-force sort, exhaustive tiny cases, invariants)
+  gather_kept         pinned (definition, invariants)
+  rope                pinned (complex-rotation form, norm and relative-position
+                      invariants)
+  keybias_attention   pinned (textbook causal SDPA reduction, shift invariance,
+                      pruning == masking, tau placement, GQA, varlen, closed forms)
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+LOG2E = 1.0 / math.log(2.0)
+
+
+# ----------------------------------------------------------------------------
+# Step 1: gate MLP score
+# ----------------------------------------------------------------------------
+def silu(a: np.ndarray) -> np.ndarray:
+    """SiLU(a) = a * sigmoid(a) = a / (1 + exp(-a)), evaluated in float64."""
+    a = np.asarray(a, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return a / (1.0 + np.exp(-a))
+
+
+def gate_score(x, w1, b1, w2, b2, chunk_rows: int = 8192) -> np.ndarray:
+    """Score every token from its layer-L residual with a small two-layer MLP.
+
+    [ES] section "¿Cómo funciona la poda de tokens aprendida de TokenGate?"
+    (gate module phase): an MLP maps each token's post-attention residual at
+    the gate layer to one score.  [GR] section "Πώς αποφασίζει τι θα
+    κρατήσει": the gate scores every token.
+
+    Reading (the pages only say "small MLP"): two layers with SiLU between,
+        s_t = w2 . SiLU(W1 x_t + b1) + b2,
+    W1 in nn.Linear layout [d_hid, d_model].  Every token is scored, document
+    and question alike.  No squashing is applied to the output.
+
+    x: [N, d_model]; w1: [d_hid, d_model]; b1: [d_hid] or None; w2: [d_hid];
+    b2: scalar.  Returns float64 [N].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w1 = np.asarray(w1, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    d_hid = w1.shape[0]
+    b1 = np.zeros(d_hid) if b1 is None else np.asarray(b1, dtype=np.float64)
+    out = np.empty(x.shape[0], dtype=np.float64)
+    for r0 in range(0, x.shape[0], chunk_rows):
+        a = x[r0:r0 + chunk_rows] @ w1.T + b1
+        out[r0:r0 + chunk_rows] = silu(a) @ w2 + float(b2)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Step 2: top-K selection, question always kept
+# ----------------------------------------------------------------------------
+def kept_counts(cu_seqlens, doc_begin, doc_end, k_doc) -> np.ndarray:
+    """Kept tokens per sequence: min(K_s, n_doc_s) + (n_s - n_doc_s).
+
+    [ES] "¿Cómo funciona…?": only the document part of the prompt can be
+    pruned and the question never is.  K_s counts document tokens; a budget
+    larger than the document keeps all of it, K_s = 0 keeps none of it.
+    Returns cu_kept [S+1] (int64).
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    s = len(cu) - 1
+    cu_kept = np.zeros(s + 1, dtype=np.int64)
+    for i in range(s):
+        n = cu[i + 1] - cu[i]
+        n_doc = int(doc_end[i]) - int(doc_begin[i])
+        if not (0 <= doc_begin[i] <= doc_end[i] <= n) or k_doc[i] < 0:
+            raise ValueError(f"sequence {i}: bad document span or budget")
+        cu_kept[i + 1] = cu_kept[i] + min(int(k_doc[i]), n_doc) + (n - n_doc)
+    return cu_kept
+
+
+def _doc_order(scores_doc: np.ndarray) -> np.ndarray:
+    """Positions of document tokens in selection order.
+
+    Order: higher score first; equal scores by lower index first.  Real
+    comparisons are used, so -0.0 equals +0.0 and +-inf order as usual.  NaN
+    scores rank below every number, -inf included, and among themselves by
+    index.  (The pages fix no rule for ties or special values; lowest index
+    wins is the reading adopted here.)
+    """
+    s = np.asarray(scores_doc, dtype=np.float64)
+    idx = np.arange(s.shape[0])
+    nan = np.isnan(s)
+    num_idx = idx[~nan]
+    num_s = s[~nan]
+    # lexsort: last key is primary -> primary = -score ascending, then index.
+    order = num_idx[np.lexsort((num_idx, -num_s))]
+    return np.concatenate([order, idx[nan]])
+
+
+def topk_select(scores, cu_seqlens, doc_begin, doc_end, k_doc):
+    """Keep the K highest-scoring document tokens plus every other token.
+
+    [ES] "¿Cómo funciona…?": a top-K selector keeps the highest-scoring
+    tokens; only the document is prunable, the question is never pruned.
+    [GR] "Πώς αποφασίζει…": only the best-scored tokens stay, and the
+    question always stays whole.
+
+    scores: float32 (or float64) [N_tot], the array given to the selector;
+    cu_seqlens: [S+1]; doc_begin/doc_end: [S], in-sequence document span
+    [doc_begin, doc_end); k_doc: [S] document budget.
+    Tokens outside the document span are always kept.  Kept global indices are
+    returned in ascending order within each sequence, sequences in order.
+    Returns (kept_idx int64 [M_tot], cu_kept int64 [S+1]).
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    sc = np.asarray(scores)
+    cu_kept = kept_counts(cu, doc_begin, doc_end, k_doc)
+    parts = []
+    for i in range(len(cu) - 1):
+        start, n = int(cu[i]), int(cu[i + 1] - cu[i])
+        db, de = int(doc_begin[i]), int(doc_end[i])
+        k_eff = min(int(k_doc[i]), de - db)
+        order = _doc_order(sc[start + db:start + de])
+        kept_doc = order[:k_eff] + db
+        nondoc = np.concatenate([np.arange(0, db), np.arange(de, n)])
+        local = np.sort(np.concatenate([kept_doc, nondoc]).astype(np.int64))
+        parts.append(local + start)
+    kept = np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+    assert kept.shape[0] == cu_kept[-1]
+    return kept, cu_kept
+
+
+# ----------------------------------------------------------------------------
+# Step 3: compaction of the kept set
+# ----------------------------------------------------------------------------
+def gather_kept(x, scores, kept_idx, cu_seqlens, cu_kept):
+    """Compact kept residuals, scores and original positions.
+
+    [ES] "¿Cómo funciona…?" (pruned forward phase): layers above the gate see
+    only the kept tokens and never create KV entries for pruned ones, so every
+    downstream tensor is sized by the kept count.
+
+    pos_kept[m] = kept_idx[m] - cu_seqlens[seq(m)], the token's original
+    position inside its sequence.  Returns (x_kept, s_kept, pos_kept int64).
+    """
+    kept_idx = np.asarray(kept_idx, dtype=np.int64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    ck = np.asarray(cu_kept, dtype=np.int64)
+    pos = np.empty_like(kept_idx)
+    for i in range(len(ck) - 1):
+        pos[ck[i]:ck[i + 1]] = kept_idx[ck[i]:ck[i + 1]] - cu[i]
+    return np.asarray(x)[kept_idx], np.asarray(scores)[kept_idx], pos
+
+
+# ----------------------------------------------------------------------------
+# Step 4: token-gated (key-bias) causal GQA attention over the kept set
+# ----------------------------------------------------------------------------
+def rope(x, pos, base: float) -> np.ndarray:
+    """Rotary position embedding on original positions, float64.
+
+    The pages say nothing about positions.  Reading: rotate-half pairing of
+    channel m with channel m + D/2, angle pos * base^(-2m/D), m in [0, D/2).
+    x: [M, H, D]; pos: [M].  base <= 0 means no rotation.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if base is None or base <= 0:
+        return x.copy()
+    d = x.shape[-1]
+    half = d // 2
+    m = np.arange(half, dtype=np.float64)
+    inv_freq = base ** (-2.0 * m / d)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv_freq[None, :]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def keybias_attention(q, k, v, s_kept, gain, tau, pos, cu_kept,
+                      rope_base: float = 1e6, rows=None, block_rows: int = 512):
+    """Token-gated causal attention over the kept set.
+
+    [ES] "¿Qué es la atención con control de acceso por tokens…?": each kept
+    token's gate score becomes a bias on the attention logits of the layers
+    above the gate; a learnable per-head gain scales it and a learnable
+    temperature corrects for each query seeing fewer keys.  [RU] "Техническая
+    реализация" describes the same router-style bias.
+
+    Reading of the formula (the pages do not print it):
+        l_ij = <R(q_i, pos_i), R(k_j, pos_j)> / (sqrt(D) * tau) + g_h * s_j
+    over keys j of the same sequence with pos_j <= pos_i (self included);
+    O_i = sum_j softmax_j(l_ij) v_j;  LSE_i = log sum_j exp(l_ij).
+    GQA: q head h reads kv head h // (Hq / Hkv).  g has one value per q head,
+    tau is one scalar.  Every kept key is biased, question keys included.
+
+    q: [M, Hq, D]; k, v: [M, Hkv, D]; s_kept: [M]; gain: [Hq]; pos: [M];
+    cu_kept: [S+1].  rows: optional iterable of kept-row indices to evaluate
+    (others are left NaN).  Returns (O [M, Hq, D] float64, LSE [Hq, M] float64).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    s_kept = np.asarray(s_kept, dtype=np.float64)
+    gain = np.asarray(gain, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    ck = np.asarray(cu_kept, dtype=np.int64)
+    m_tot, hq, d = q.shape
+    hkv = k.shape[1]
+    if hq % hkv != 0:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    if not (tau > 0 and math.isfinite(tau)):
+        raise ValueError("tau must be positive and finite")
+    grp = hq // hkv
+    scale = 1.0 / (math.sqrt(d) * float(tau))
+    out = np.full((m_tot, hq, d), np.nan)
+    lse = np.full((hq, m_tot), np.nan)
+    want = np.zeros(m_tot, dtype=bool)
+    if rows is None:
+        want[:] = True
+    else:
+        want[np.asarray(list(rows), dtype=np.int64)] = True
+    for si in range(len(ck) - 1):
+        a, b = int(ck[si]), int(ck[si + 1])
+        if a == b or not want[a:b].any():
+            continue
+        p = pos[a:b]
+        qr = rope(q[a:b], p, rope_base)
+        kr = rope(k[a:b], p, rope_base)
+        vs = v[a:b]
+        sel = np.nonzero(want[a:b])[0]
+        for h in range(hq):
+            hk = h // grp
+            bias = gain[h] * s_kept[a:b]
+            for r0 in range(0, sel.shape[0], block_rows):
+                ri = sel[r0:r0 + block_rows]
+                logit = (qr[ri, h, :] @ kr[:, hk, :].T) * scale + bias[None, :]
+                mask = p[None, :] > p[ri][:, None]
+                logit[mask] = -np.inf
+                mx = logit.max(axis=1, keepdims=True)
+                e = np.exp(logit - mx)
+                den = e.sum(axis=1, keepdims=True)
+                out[a + ri, h, :] = (e @ vs[:, hk, :]) / den
+                lse[h, a + ri] = (mx + np.log(den))[:, 0]
+    return out, lse
+
+
+# ----------------------------------------------------------------------------
+# The whole gated layer, for end-to-end checks
+# ----------------------------------------------------------------------------
+def gated_layer(x, w1, b1, w2, b2, cu_seqlens, doc_begin, doc_end, k_doc):
+    """Gate -> select -> gather.  Attention inputs are projections of the kept
+    residuals that the host model owns; callers pass them separately.
+    Returns dict with fp64 scores, their float32 rounding (what the selector
+    consumes), kept_idx, cu_kept, x_kept, s_kept, pos_kept."""
+    s64 = gate_score(x, w1, b1, w2, b2)
+    s32 = s64.astype(np.float32)
+    kept, cu_kept = topk_select(s32, cu_seqlens, doc_begin, doc_end, k_doc)
+    xk, sk, pk = gather_kept(x, s32, kept, cu_seqlens, cu_kept)
+    return dict(scores=s64, scores_f32=s32, kept_idx=kept, cu_kept=cu_kept,
+                x_kept=xk, s_kept=sk, pos_kept=pk)

@@ -1,0 +1,355 @@
+"""Pins for the CPU oracle against things other than itself: library routines
+(torch fp64 linear/silu/SDPA), hand-worked fixtures, closed forms, brute force
+and invariants.  No GPU."""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _num(v):
+    return float(v) if not isinstance(v, str) else float(v.replace("nan", "nan"))
+
+
+# ---------------------------------------------------------------- gate ----
+def test_gate_matches_torch_linear_silu():
+    r = np.random.default_rng(11)
+    x = r.standard_normal((37, 24))
+    w1 = r.standard_normal((10, 24)) * 0.3
+    b1 = r.standard_normal(10)
+    w2 = r.standard_normal(10)
+    b2 = 0.37
+    got = oracle.gate_score(x, w1, b1, w2, b2, chunk_rows=8)
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    ref = F.linear(F.silu(F.linear(t(x), t(w1), t(b1))), t(w2)[None, :]).squeeze(1) + b2
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_gate_closed_forms():
+    r = np.random.default_rng(12)
+    w1 = r.standard_normal((6, 5))
+    b1 = np.array([0.0, 1.0, -1.0, 2.0, -3.0, 0.5])
+    w2 = r.standard_normal(6)
+    # x = 0 -> s = w2 . SiLU(b1) + b2, with sigmoid(1) = 0.7310585786300049 (table value)
+    s = oracle.gate_score(np.zeros((3, 5)), w1, b1, w2, -0.25)
+    sig = {0.0: 0.5, 1.0: 0.7310585786300049, -1.0: 0.2689414213699951,
+           2.0: 0.8807970779778823, -3.0: 0.04742587317756678, 0.5: 0.6224593312018546}
+    want = sum(w2[i] * b1[i] * sig[b1[i]] for i in range(6)) - 0.25
+    np.testing.assert_allclose(s, want, rtol=1e-14)
+    # W1 = 0 and b1 = 0 -> SiLU(0) = 0 -> s = b2 exactly
+    s0 = oracle.gate_score(r.standard_normal((4, 5)), np.zeros((6, 5)), None, w2, 1.5)
+    assert np.all(s0 == 1.5)
+
+
+def test_silu_limits():
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    assert abs(oracle.silu(np.array([40.0]))[0] - 40.0) < 1e-12
+    assert abs(oracle.silu(np.array([-40.0]))[0]) < 1e-15
+    assert np.isfinite(oracle.silu(np.array([-1000.0]))).all()
+
+
+def test_gate_workload_shapes():
+    w = workloads.tiny()
+    g = w.gate_inputs()
+    s = oracle.gate_score(g["x_f"], g["w1_f"], g["b1_f"], g["w2_f"], g["b2"])
+    assert s.shape == (512,) and np.isfinite(s).all()
+    assert s.std() > 1e-3
+
+
+# --------------------------------------------------------------- top-K ----
+def _brute_keep(scores, k):
+    """Python sorted() on (nan flag, -score, index): the selection rule read
+    from the pages plus the tie / special-value readings."""
+    n = len(scores)
+    keyf = lambda i: (1, 0.0, i) if math.isnan(scores[i]) else (0, -scores[i], i)
+    return sorted(sorted(range(n), key=keyf)[:min(k, n)])
+
+
+def _beats(a, sa, b, sb):
+    """Pairwise: does token a rank strictly before token b?"""
+    if math.isnan(sa) or math.isnan(sb):
+        if math.isnan(sa) and math.isnan(sb):
+            return a < b
+        return math.isnan(sb)
+    if sa != sb:
+        return sa > sb
+    return a < b
+
+
+def test_topk_golden_hand_example():
+    g = json.load(open(os.path.join(GOLD, "topk_hand.json")))
+    s = np.array([float(v) for v in g["scores"]], dtype=np.float32)
+    for c in g["cases"]:
+        kept, cu = oracle.topk_select(s, [0, 8], [g["doc_begin"]], [g["doc_end"]], [c["k_doc"]])
+        assert kept.tolist() == c["kept"], c
+
+
+def test_topk_exhaustive_tiny():
+    vals = [-math.inf, -1.0, -0.0, 0.0, 1.0, math.nan]
+    for n in range(1, 6):
+        for combo in itertools.product(vals, repeat=n):
+            s = np.array(combo, dtype=np.float32)
+            for k in range(0, n + 2):
+                kept, _ = oracle.topk_select(s, [0, n], [0], [n], [k])
+                assert kept.tolist() == _brute_keep(list(combo), k), (combo, k)
+
+
+def test_topk_random_against_pairwise_dominance():
+    r = np.random.default_rng(3)
+    for trial in range(300):
+        n = int(r.integers(1, 40))
+        q = int(r.integers(0, n + 1))
+        nd = n - q
+        pool = np.array([-2.0, -1.0, 0.0, -0.0, 1.0, 3.0, np.inf, -np.inf, np.nan], dtype=np.float32)
+        s = np.where(r.random(n) < 0.5, r.choice(pool, n), r.standard_normal(n)).astype(np.float32)
+        k = int(r.integers(0, nd + 3))
+        kept, cu = oracle.topk_select(s, [0, n], [0], [nd], [k])
+        kept = kept.tolist()
+        assert kept == sorted(kept)
+        assert len(kept) == min(k, nd) + q == cu[-1]
+        assert set(range(nd, n)) <= set(kept)          # question always kept
+        kd = [i for i in kept if i < nd]
+        pr = [i for i in range(nd) if i not in kept]
+        for a in kd:                                   # every kept doc token beats every pruned one
+            for b in pr:
+                assert _beats(a, float(s[a]), b, float(s[b]))
+        # idempotence: reselecting the kept document tokens with the same budget keeps all
+        sub = s[kd]
+        k2, _ = oracle.topk_select(sub, [0, len(kd)], [0], [len(kd)], [min(k, nd)])
+        assert k2.tolist() == list(range(len(kd)))
+
+
+def test_topk_doc_span_in_middle_and_varlen():
+    r = np.random.default_rng(5)
+    lens, spans, ks = [9, 1, 14, 0, 6], [(2, 7), (0, 1), (3, 10), (0, 0), (0, 6)], [2, 0, 100, 4, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    s = r.standard_normal(cu[-1]).astype(np.float32)
+    kept, ck = oracle.topk_select(s, cu, [a for a, _ in spans], [b for _, b in spans], ks)
+    parts = []
+    for i, n in enumerate(lens):
+        a, b = spans[i]
+        local = _brute_keep([float(v) for v in s[cu[i] + a:cu[i] + b]], ks[i])
+        keep = sorted([a + j for j in local] + list(range(0, a)) + list(range(b, n)))
+        parts += [cu[i] + j for j in keep]
+        assert ck[i + 1] - ck[i] == len(keep)
+    assert kept.tolist() == parts
+
+
+def test_topk_rejects_bad_metadata():
+    with pytest.raises(ValueError):
+        oracle.topk_select(np.zeros(4, np.float32), [0, 4], [0], [5], [1])
+    with pytest.raises(ValueError):
+        oracle.topk_select(np.zeros(4, np.float32), [0, 4], [0], [4], [-1])
+
+
+def test_topk_planted_ties_cut_inside_group():
+    w = workloads.custom([3000, 2000], [100, 50], [240, 160], tie_frac=0.05)
+    s = w.topk_scores()
+    kept, ck = oracle.topk_select(s, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc)
+    for i in range(2):
+        a, nd = int(w.cu_seqlens[i]), int(w.doc_end[i])
+        doc = s[a:a + nd]
+        vals, cnt = np.unique(doc, return_counts=True)
+        t = vals[np.argmax(cnt)]
+        kd = kept[(kept >= a) & (kept < a + nd)] - a
+        tied_kept = np.sort(kd[doc[kd] == t])
+        tied_all = np.nonzero(doc == t)[0]
+        assert 0 < tied_kept.size < tied_all.size          # the cut falls inside the tie group
+        assert (tied_kept == tied_all[:tied_kept.size]).all()  # lowest indices win
+
+
+# -------------------------------------------------------------- gather ----
+def test_gather_definition():
+    r = np.random.default_rng(8)
+    cu = np.array([0, 5, 12])
+    x = r.standard_normal((12, 3))
+    s = r.standard_normal(12).astype(np.float32)
+    kept = np.array([1, 3, 4, 5, 6, 11])
+    ck = np.array([0, 3, 6])
+    xk, sk, pk = oracle.gather_kept(x, s, kept, cu, ck)
+    assert (xk == x[kept]).all() and (sk == s[kept]).all()
+    assert pk.tolist() == [1, 3, 4, 0, 1, 6]
+
+
+# ---------------------------------------------------------------- RoPE ----
+def _rope_complex(x, pos, base):
+    """Independent form: channels (m, m + D/2) as one complex number times e^{i pos w_m}."""
+    d = x.shape[-1]
+    h = d // 2
+    w = np.array([base ** (-(2.0 * m) / d) for m in range(h)])
+    z = x[..., :h] + 1j * x[..., h:]
+    z = z * np.exp(1j * np.asarray(pos, dtype=np.float64)[:, None, None] * w)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def test_rope_golden_and_complex_form():
+    g = json.load(open(os.path.join(GOLD, "rope_hand.json")))
+    got = oracle.rope(np.array(g["x"])[None, None, :], np.array([g["pos"]]), g["base"])[0, 0]
+    np.testing.assert_allclose(got, g["out"], rtol=0, atol=1e-15)
+    r = np.random.default_rng(9)
+    x = r.standard_normal((20, 3, 16))
+    pos = r.integers(0, 200000, 20)
+    np.testing.assert_allclose(oracle.rope(x, pos, 1e6), _rope_complex(x, pos, 1e6), atol=1e-12)
+
+
+def test_rope_invariants():
+    r = np.random.default_rng(10)
+    q = r.standard_normal((1, 1, 64))
+    k = r.standard_normal((1, 1, 64))
+    np.testing.assert_array_equal(oracle.rope(q, [0], 1e6), q)
+    np.testing.assert_allclose(np.linalg.norm(oracle.rope(q, [12345], 1e6)), np.linalg.norm(q), rtol=1e-14)
+    dot = lambda p1, p2: float((oracle.rope(q, [p1], 1e6) * oracle.rope(k, [p2], 1e6)).sum())
+    assert abs(dot(100, 40) - dot(100 + 777, 40 + 777)) < 1e-10
+
+
+# ----------------------------------------------------------- attention ----
+def _sdpa_ref(q, k, v, pos, gain, tau, s, base, keep_mask=None):
+    """torch fp64 SDPA with a float mask: g_h * s_j on kept keys, -inf on pruned
+    keys and on keys at later positions; K/V repeated per q head."""
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    if base:
+        q, k = _rope_complex(q, pos, base), _rope_complex(k, pos, base)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    qt = t(q).permute(1, 0, 2)
+    kt = t(k).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+    vt = t(v).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+    pos = np.asarray(pos)
+    allowed = pos[None, :] <= pos[:, None]
+    if keep_mask is not None:
+        allowed = allowed & keep_mask[None, :]
+    mask = torch.full((hq, n, n), -math.inf, dtype=torch.float64)
+    bias = t(np.asarray(gain, dtype=np.float64)[:, None] * np.asarray(s, dtype=np.float64)[None, :])
+    al = torch.from_numpy(allowed)
+    for h in range(hq):
+        mask[h][al] = bias[h][None, :].expand(n, n)[al]
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=1.0 / (math.sqrt(d) * tau))
+    return o.permute(1, 0, 2).numpy()
+
+
+def test_attention_golden_two_tokens():
+    g = json.load(open(os.path.join(GOLD, "attn_two_tokens.json")))
+    a = lambda key: np.array(g[key], dtype=np.float64)[:, None, :]
+    out, lse = oracle.keybias_attention(a("q"), a("k"), a("v"), np.array(g["s"]), np.array([g["gain"]]),
+                                        g["tau"], np.array([0, 1]), [0, 2], rope_base=0)
+    np.testing.assert_allclose(out[:, 0, :], g["out"], atol=1e-15)
+    np.testing.assert_allclose(lse[0], g["lse"], atol=1e-15)
+
+
+def test_attention_reduces_to_causal_sdpa():
+    """g = 0, tau = 1, nothing pruned: plain causal GQA attention (is_causal SDPA)."""
+    r = np.random.default_rng(21)
+    n, hq, hkv, d = 37, 4, 2, 16
+    q, k, v = (r.standard_normal((n, h, d)) for h in (hq, hkv, hkv))
+    out, _ = oracle.keybias_attention(q, k, v, r.standard_normal(n), np.zeros(hq), 1.0,
+                                      np.arange(n), [0, n], rope_base=0)
+    t = lambda a: torch.from_numpy(a).permute(1, 0, 2)
+    ref = F.scaled_dot_product_attention(t(q), t(k).repeat_interleave(2, 0), t(v).repeat_interleave(2, 0),
+                                         is_causal=True).permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out, ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("base", [0.0, 1e6, 100.0])
+def test_attention_pruning_equals_masking(base):
+    """Key-bias attention on the compacted set == full-length attention with
+    pruned keys masked out, at the kept query rows (pins gather, positions,
+    RoPE on original positions, causality, bias sign, per-head gain, tau)."""
+    r = np.random.default_rng(22)
+    n, hq, hkv, d = 60, 6, 2, 8
+    q, k, v = (r.standard_normal((n, h, d)) for h in (hq, hkv, hkv))
+    s = r.standard_normal(n).astype(np.float32)
+    gain = r.uniform(0.5, 2, hq)
+    tau = 0.83
+    kept, ck = oracle.topk_select(s, [0, n], [0], [48], [17])
+    qk, sk, pk = oracle.gather_kept(q, s, kept, [0, n], ck)
+    kk = k[kept]
+    vk = v[kept]
+    out, _ = oracle.keybias_attention(qk, kk, vk, sk, gain, tau, pk, ck, rope_base=base)
+    keep = np.zeros(n, dtype=bool)
+    keep[kept] = True
+    ref = _sdpa_ref(q, k, v, np.arange(n), gain, tau, s, base, keep_mask=keep)
+    np.testing.assert_allclose(out, ref[kept], atol=1e-11)
+
+
+def test_attention_shift_invariance_and_tau_placement():
+    r = np.random.default_rng(23)
+    n, hq, hkv, d = 30, 2, 1, 8
+    q, k, v = (r.standard_normal((n, h, d)) for h in (hq, hkv, hkv))
+    s = r.standard_normal(n)
+    g = np.array([0.7, 1.9])
+    pos = np.sort(r.choice(1000, n, replace=False))
+    o1, l1 = oracle.keybias_attention(q, k, v, s, g, 0.9, pos, [0, n])
+    o2, l2 = oracle.keybias_attention(q, k, v, s + 3.25, g, 0.9, pos, [0, n])
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    np.testing.assert_allclose(l2 - l1, (g * 3.25)[:, None] * np.ones((1, n)), atol=1e-12)
+    o3, _ = oracle.keybias_attention(q / 0.9, k, v, s, g, 1.0, pos, [0, n])
+    np.testing.assert_allclose(o1, o3, atol=1e-12)
+
+
+def test_attention_gqa_and_varlen():
+    r = np.random.default_rng(24)
+    lens = [5, 1, 13, 8]
+    ck = np.concatenate([[0], np.cumsum(lens)])
+    m, hq, hkv, d = ck[-1], 8, 2, 16
+    q, k, v = (r.standard_normal((m, h, d)) for h in (hq, hkv, hkv))
+    s = r.standard_normal(m)
+    g = r.uniform(0.5, 2, hq)
+    pos = np.concatenate([np.sort(r.choice(50, L, replace=False)) for L in lens])
+    out, lse = oracle.keybias_attention(q, k, v, s, g, 0.95, pos, ck)
+    # GQA == MHA with repeat-interleaved K/V
+    o_mha, _ = oracle.keybias_attention(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), s, g, 0.95, pos, ck)
+    np.testing.assert_allclose(out, o_mha, atol=1e-12)
+    # varlen == concatenation of per-sequence calls
+    for i in range(len(lens)):
+        a, b = ck[i], ck[i + 1]
+        oi, li = oracle.keybias_attention(q[a:b], k[a:b], v[a:b], s[a:b], g, 0.95, pos[a:b], [0, b - a])
+        np.testing.assert_allclose(out[a:b], oi, atol=1e-12)
+        np.testing.assert_allclose(lse[:, a:b], li, atol=1e-12)
+
+
+def test_attention_closed_forms_and_lse():
+    r = np.random.default_rng(25)
+    n, d = 12, 8
+    k = r.standard_normal((n, 1, d))
+    v = r.standard_normal((n, 1, d))
+    q = r.standard_normal((n, 1, d))
+    s = r.standard_normal(n)
+    out, lse = oracle.keybias_attention(q, k, v, s, np.array([1.3]), 0.8, np.arange(n), [0, n])
+    np.testing.assert_allclose(out[0, 0], v[0, 0], atol=1e-14)            # row 0 sees only itself
+    o0, _ = oracle.keybias_attention(np.zeros_like(q), k, v, s, np.array([0.0]), 1.0, np.arange(n), [0, n])
+    means = np.cumsum(v[:, 0], axis=0) / np.arange(1, n + 1)[:, None]
+    np.testing.assert_allclose(o0[:, 0], means, atol=1e-13)              # uniform weights
+    qr, kr = _rope_complex(q, np.arange(n), 1e6), _rope_complex(k, np.arange(n), 1e6)
+    logits = torch.from_numpy((qr[:, 0] @ kr[:, 0].T) / (math.sqrt(d) * 0.8) + 1.3 * s[None, :])
+    logits = logits.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), -math.inf)
+    np.testing.assert_allclose(lse[0], torch.logsumexp(logits, 1).numpy(), atol=1e-12)
+
+
+def test_attention_rows_subset():
+    r = np.random.default_rng(26)
+    n, hq, hkv, d = 40, 2, 1, 8
+    q, k, v = (r.standard_normal((n, h, d)) for h in (hq, hkv, hkv))
+    s = r.standard_normal(n)
+    full, _ = oracle.keybias_attention(q, k, v, s, np.ones(hq), 1.0, np.arange(n), [0, n])
+    part, _ = oracle.keybias_attention(q, k, v, s, np.ones(hq), 1.0, np.arange(n), [0, n], rows=[0, 7, 39])
+    np.testing.assert_array_equal(part[[0, 7, 39]], full[[0, 7, 39]])
+    assert np.isnan(part[1]).all()
+
+
+def test_attention_rejects_bad_params():
+    z = np.zeros((2, 2, 4))
+    with pytest.raises(ValueError):
+        oracle.keybias_attention(z, z[:, :1], z[:, :1], np.zeros(2), np.ones(2), 0.0, [0, 1], [0, 2])
+    with pytest.raises(ValueError):
+        oracle.keybias_attention(np.zeros((2, 3, 4)), z, z, np.zeros(2), np.ones(3), 1.0, [0, 1], [0, 2])
