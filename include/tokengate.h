@@ -1,0 +1,181 @@
+/*
+ * tokengate.h - C ABI of libtokengate, the gfx950 (MI355X) hot path of
+ * TokenGate's pruned prefill: gate score -> top-K select -> compaction ->
+ * token-gated (key-bias) causal GQA attention over the kept tokens.
+ *
+ * Source of the method: the TokenGate news pages, chiefly the spke.com
+ * article "Investigadores de Stanford y UC Berkeley Presentan TokenGate: La
+ * Atencion con Compuertas por Token Hace el Prefill de Contexto Largo Hasta
+ * 11.3x Mas Rapido", sections "Como funciona la poda de tokens aprendida de
+ * TokenGate?" (three-phase forward pass, gate module, pruned forward, question
+ * never pruned), "Que es la atencion con control de acceso por tokens?"
+ * (score as attention-logit bias, per-head gain, temperature) and "Como se
+ * despliega TokenGate?" (document placeholder and keep budget).
+ *
+ * Conventions shared by every call
+ *  - Pointers marked [device] are caller-owned device memory; pointers marked
+ *    [host] are ordinary host memory.  The library never allocates or frees
+ *    memory; scratch space comes from the caller through a workspace
+ *    argument sized by the matching *_workspace_bytes() call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every device call is asynchronous and stream-ordered; none synchronises.
+ *  - Inputs are read-only.  Outputs must not alias inputs and are fully
+ *    overwritten.
+ *  - All scalar arguments and host-visible pointers are validated before any
+ *    HIP call; a failed check returns TG_ERR_INVALID_ARG / TG_ERR_UNSUPPORTED
+ *    / TG_ERR_WORKSPACE and launches nothing.  A failed launch returns
+ *    TG_ERR_HIP.  Device-resident metadata (cu_seqlens, spans, budgets,
+ *    cu_kept, positions) is trusted: inconsistent values are undefined
+ *    behaviour.
+ *  - Calls are reentrant and thread-safe; the library has no global state.
+ */
+#ifndef TOKENGATE_H
+#define TOKENGATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    TG_OK = 0,
+    TG_ERR_INVALID_ARG = 1,  /* bad scalar, NULL required pointer, misaligned pointer */
+    TG_ERR_UNSUPPORTED = 2,  /* a shape or dtype this build has no kernel for */
+    TG_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+    TG_ERR_HIP = 4           /* a HIP launch failed */
+};
+
+enum { TG_F32 = 0, TG_BF16 = 1 };   /* element type of residuals / gate weights */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* tg_status_string(int status);
+
+/*
+ * Kept-token counts, on the host.  Only the document span of each sequence is
+ * prunable and the question (every token outside the span) is always kept
+ * (spke.com article, section on how the pruning works), so the kept count is
+ * known before any score exists:
+ *     M_s = min(k_doc[s], doc_end[s] - doc_begin[s]) + (n_s - n_doc_s).
+ *   n_seqs        number of packed sequences S >= 0
+ *   cu_seqlens_h  [host] S+1 int32 prefix offsets, cu[0] = 0, non-decreasing
+ *   doc_begin_h,
+ *   doc_end_h     [host] S int32, in-sequence document span, 0 <= b <= e <= n_s
+ *   k_doc_h       [host] S int32 document budgets >= 0
+ *   cu_kept_h     [host, out] S+1 int32 prefix offsets of kept tokens
+ * Errors: TG_ERR_INVALID_ARG on NULL pointers, negative sizes, inconsistent
+ * spans or int32 overflow.  Never touches the GPU.
+ */
+int tg_kept_counts(int32_t n_seqs, const int32_t* cu_seqlens_h, const int32_t* doc_begin_h,
+                   const int32_t* doc_end_h, const int32_t* k_doc_h, int32_t* cu_kept_h);
+
+/*
+ * Gate MLP score of every token (spke.com article, gate-module phase: a small
+ * MLP scores each token from its post-attention residual at the gate layer):
+ *     scores[t] = w2 . SiLU(W1 x_t + b1) + b2,   SiLU(a) = a * sigmoid(a).
+ * The hidden layer is kept in fp32 (bf16 MFMA products, fp32 accumulation).
+ *   x             [device] n_tokens rows of d_model elements of x_dtype,
+ *                 consecutive rows x_row_stride elements apart
+ *   x_dtype       TG_BF16 (MFMA path) or TG_F32 (fp32 FMA path)
+ *   w1            [device] d_hid x d_model, row-major (nn.Linear layout), x_dtype
+ *   b1            [device] d_hid fp32, or NULL for no bias
+ *   w2            [device] d_hid fp32
+ *   b2            scalar fp32 output bias
+ *   scores        [device, out] n_tokens fp32
+ * Requirements: d_model % 8 == 0, x_row_stride >= d_model and % 8 == 0,
+ * x and w1 16-byte aligned.  bf16: d_hid in {32, 64, ..., 256} (multiple of
+ * 32); fp32: 1 <= d_hid <= 1024, d_model <= 8192.  n_tokens == 0 is a no-op.
+ */
+int tg_gate_score(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d_model,
+                  int64_t x_row_stride, const void* w1, const float* b1, const float* w2,
+                  float b2, int32_t d_hid, float* scores, void* stream);
+
+/* Workspace bytes tg_topk_select needs (0 for this build; kept for ABI growth). */
+size_t tg_topk_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen);
+
+/*
+ * Top-K selection with the question always kept (spke.com article, gate-module
+ * phase and the rule that only the document is prunable).  Per sequence s:
+ * keep K_eff = min(k_doc[s], n_doc_s) document tokens in the order (score
+ * descending, index ascending), plus every token outside [doc_begin,
+ * doc_end).  Score comparison: -0.0 == +0.0, NaN ranks below -inf (NaNs among
+ * themselves by index), +-inf order normally.  Output is exact and
+ * deterministic.
+ *   scores        [device] n_tokens_total fp32
+ *   cu_seqlens    [device] S+1 int32
+ *   doc_begin, doc_end, k_doc   [device] S int32 each
+ *   cu_kept       [device] S+1 int32, as produced by tg_kept_counts
+ *   kept_idx      [device, out] cu_kept[S] int32 GLOBAL token indices,
+ *                 ascending within each sequence
+ *   max_seqlen    host upper bound of n_s (used for validation only)
+ * Errors: TG_ERR_INVALID_ARG on NULL pointers or negative sizes.
+ */
+int tg_topk_select(const float* scores, int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen,
+                   const int32_t* cu_seqlens, const int32_t* doc_begin, const int32_t* doc_end,
+                   const int32_t* k_doc, const int32_t* cu_kept, int32_t* kept_idx,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Compaction of the kept set (spke.com article, pruned-forward phase: layers
+ * above the gate see only the kept tokens and never create KV for the rest):
+ *     x_kept[m] = x[kept_idx[m]],  scores_kept[m] = scores[kept_idx[m]],
+ *     pos_kept[m] = kept_idx[m] - cu_seqlens[seq(m)]   (original position).
+ *   x             [device] residual rows as in tg_gate_score
+ *   scores        [device] fp32 per token (may be NULL: then scores_kept must be NULL)
+ *   kept_idx      [device] n_kept_total int32 global indices
+ *   cu_seqlens, cu_kept   [device] S+1 int32
+ *   x_kept        [device, out] n_kept_total x d_model, dense rows, x_dtype
+ *   scores_kept   [device, out] n_kept_total fp32 (or NULL)
+ *   pos_kept      [device, out] n_kept_total int32 (or NULL)
+ * Bit-exact copy.  Requirements as tg_gate_score for x.
+ */
+int tg_gather_kept(const void* x, int32_t x_dtype, int32_t d_model, int64_t x_row_stride,
+                   const float* scores, const int32_t* kept_idx, int64_t n_kept_total,
+                   int32_t n_seqs, const int32_t* cu_seqlens, const int32_t* cu_kept,
+                   void* x_kept, float* scores_kept, int32_t* pos_kept, void* stream);
+
+/* Workspace bytes tg_keybias_attn_prefill needs for these sizes. */
+size_t tg_attn_workspace_bytes(int32_t n_seqs, int64_t n_kept_total, int32_t n_kv_heads,
+                               int32_t head_dim);
+
+/*
+ * Token-gated causal GQA attention over the kept tokens (spke.com article,
+ * section on token-gated attention: every kept token's gate score is added as
+ * a bias to the attention logits of the layers above the gate, scaled by a
+ * learnable per-head gain, with a learnable temperature).  Formula used
+ * (the pages do not print one):
+ *     l_ij = <R(q_i,pos_i), R(k_j,pos_j)> / (sqrt(D) * tau) + head_gain[h] * key_score[j]
+ * over keys j of the same sequence with pos_j <= pos_i; O_i = softmax_j(l_ij) V;
+ * lse[h][i] = log sum_j exp(l_ij).  q head h reads kv head h / (Hq / Hkv).
+ * R is rotary embedding on original positions (rotate-half pairing (m, m+D/2),
+ * angle pos * rope_base^(-2m/D), angles reduced in fp64); rope_base <= 0
+ * disables it.  bf16 MFMA with fp32 accumulation and fp32 online softmax.
+ *   q             [device] bf16, token m head h at q + m*q_row_stride + h*D
+ *   k, v          [device] bf16, token m kv head g at k + m*kv_row_stride + g*D
+ *   key_score     [device] n_kept_total fp32 (the kept tokens' gate scores)
+ *   head_gain     [device] n_q_heads fp32
+ *   tau           temperature > 0, finite
+ *   pos           [device] n_kept_total int32 original positions, strictly
+ *                 increasing within each sequence (tg_gather_kept output is)
+ *   cu_kept       [device] S+1 int32 prefix offsets of the kept sequences
+ *   max_kept_seqlen  host upper bound of max_s M_s (sizes the grid)
+ *   out           [device, out] bf16 n_kept_total x n_q_heads x D, dense
+ *   lse           [device, out] fp32 n_q_heads x n_kept_total, or NULL
+ *   workspace     [device] >= tg_attn_workspace_bytes(...) bytes, 256-B aligned
+ * Requirements: head_dim in {64, 128}; n_q_heads % n_kv_heads == 0 and the
+ * group size Hq/Hkv in {1, 2, 4, 8}; q_row_stride >= Hq*D, kv_row_stride >=
+ * Hkv*D, both multiples of 8; q, k, v 16-byte aligned.
+ */
+int tg_keybias_attn_prefill(const void* q, const void* k, const void* v, int64_t q_row_stride,
+                            int64_t kv_row_stride, const float* key_score, const float* head_gain,
+                            float tau, const int32_t* pos, const int32_t* cu_kept, int32_t n_seqs,
+                            int64_t n_kept_total, int32_t max_kept_seqlen, int32_t n_q_heads,
+                            int32_t n_kv_heads, int32_t head_dim, double rope_base, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENGATE_H */

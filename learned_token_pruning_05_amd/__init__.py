@@ -1,0 +1,19 @@
+"""MI355X (gfx950) hot path of TokenGate's pruned prefill.
+
+gate score -> top-K select (question always kept) -> compaction -> token-gated
+causal GQA attention over the kept tokens, as hand-written HIP kernels behind a
+C ABI (include/tokengate.h).  This package is the thin Python binding; the
+library is loaded lazily by _lib.load(), and nothing here runs on the CPU.
+"""
+
+from . import _lib  # noqa: F401
+from ._lib import (  # noqa: F401
+    TokenGateError,
+    load,
+    tg_attn_workspace_bytes,
+    tg_gate_score,
+    tg_gather_kept,
+    tg_kept_counts,
+    tg_keybias_attn_prefill,
+    tg_topk_select,
+)

@@ -1,0 +1,181 @@
+"""ctypes binding of libtokengate: the C-ABI entry points under the same names.
+
+Argument marshalling only: shapes, strides, data pointers and the current
+stream are read from torch tensors and passed through; every step of the path
+runs in the library's HIP kernels.  Output tensors the caller does not pass are
+allocated with torch on the input's device.  A non-zero status raises
+TokenGateError.  There is no fallback: if the library is missing, load() raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtokengate.so")
+
+TG_OK, TG_ERR_INVALID_ARG, TG_ERR_UNSUPPORTED, TG_ERR_WORKSPACE, TG_ERR_HIP = range(5)
+TG_F32, TG_BF16 = 0, 1
+
+# symbol -> (restype, argtypes)
+_P, _I32, _I64, _F, _D, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                               ctypes.c_double, ctypes.c_size_t)
+SIGNATURES = {
+    "tg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "tg_kept_counts": (ctypes.c_int, [_I32, _P, _P, _P, _P, _P]),
+    "tg_gate_score": (ctypes.c_int, [_P, _I32, _I64, _I32, _I64, _P, _P, _P, _F, _I32, _P, _P]),
+    "tg_topk_workspace_bytes": (_SZ, [_I32, _I64, _I32]),
+    "tg_topk_select": (ctypes.c_int, [_P, _I32, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "tg_gather_kept": (ctypes.c_int, [_P, _I32, _I32, _I64, _P, _P, _I64, _I32, _P, _P, _P, _P, _P, _P]),
+    "tg_attn_workspace_bytes": (_SZ, [_I32, _I64, _I32, _I32]),
+    "tg_keybias_attn_prefill": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P, _F, _P, _P, _I32, _I64,
+                                               _I32, _I32, _I32, _I32, _D, _P, _P, _P, _SZ, _P]),
+}
+
+
+class TokenGateError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Load the in-tree libtokengate.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype, f.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().tg_status_string(status).decode()
+
+
+def _check(fn, status):
+    if status != TG_OK:
+        raise TokenGateError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return TG_BF16
+    if t.dtype == torch.float32:
+        return TG_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _rows(t):
+    """(n_rows, row_len, row_stride) of a 2-D tensor with unit inner stride."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with contiguous rows")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _i32_host(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+# ------------------------------------------------------------------ entries --
+def tg_kept_counts(cu_seqlens, doc_begin, doc_end, k_doc) -> np.ndarray:
+    """Host-side kept counts -> cu_kept (int32 numpy, S+1)."""
+    cu, b, e, k = (_i32_host(a) for a in (cu_seqlens, doc_begin, doc_end, k_doc))
+    s = len(cu) - 1
+    out = np.zeros(s + 1, dtype=np.int32)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    _check("tg_kept_counts", load().tg_kept_counts(s, p(cu), p(b), p(e), p(k), p(out)))
+    return out
+
+
+def tg_gate_score(x, w1, b1, w2, b2: float, scores=None):
+    n, d_model, stride = _rows(x)
+    d_hid = w1.shape[0]
+    if scores is None:
+        scores = torch.empty(n, dtype=torch.float32, device=x.device)
+    st = load().tg_gate_score(_ptr(x), _dtype_code(x), n, d_model, stride, _ptr(w1), _ptr(b1), _ptr(w2),
+                              float(b2), d_hid, _ptr(scores), _stream(x))
+    _check("tg_gate_score", st)
+    return scores
+
+
+def tg_topk_select(scores, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, n_kept_total: int,
+                   max_seqlen: int, kept_idx=None):
+    """Device metadata tensors (int32); n_kept_total = cu_kept[-1] known on the host."""
+    n_seqs = cu_seqlens.shape[0] - 1
+    if kept_idx is None:
+        kept_idx = torch.empty(n_kept_total, dtype=torch.int32, device=scores.device)
+    lib = load()
+    ws_bytes = lib.tg_topk_workspace_bytes(n_seqs, scores.shape[0], max_seqlen)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=scores.device) if ws_bytes else None
+    st = lib.tg_topk_select(_ptr(scores), n_seqs, scores.shape[0], max_seqlen, _ptr(cu_seqlens), _ptr(doc_begin),
+                            _ptr(doc_end), _ptr(k_doc), _ptr(cu_kept), _ptr(kept_idx), _ptr(ws), ws_bytes,
+                            _stream(scores))
+    _check("tg_topk_select", st)
+    return kept_idx
+
+
+def tg_gather_kept(x, scores, kept_idx, cu_seqlens, cu_kept, x_kept=None, scores_kept=None,
+                   pos_kept=None):
+    n, d_model, stride = _rows(x)
+    m = kept_idx.shape[0]
+    dev = x.device
+    if x_kept is None:
+        x_kept = torch.empty((m, d_model), dtype=x.dtype, device=dev)
+    if scores_kept is None and scores is not None:
+        scores_kept = torch.empty(m, dtype=torch.float32, device=dev)
+    if pos_kept is None:
+        pos_kept = torch.empty(m, dtype=torch.int32, device=dev)
+    st = load().tg_gather_kept(_ptr(x), _dtype_code(x), d_model, stride, _ptr(scores), _ptr(kept_idx), m,
+                               cu_seqlens.shape[0] - 1, _ptr(cu_seqlens), _ptr(cu_kept), _ptr(x_kept),
+                               _ptr(scores_kept), _ptr(pos_kept), _stream(x))
+    _check("tg_gather_kept", st)
+    return x_kept, scores_kept, pos_kept
+
+
+def tg_attn_workspace_bytes(n_seqs, n_kept_total, n_kv_heads, head_dim) -> int:
+    return load().tg_attn_workspace_bytes(n_seqs, n_kept_total, n_kv_heads, head_dim)
+
+
+def tg_keybias_attn_prefill(q, k, v, key_score, head_gain, tau: float, pos, cu_kept,
+                            max_kept_seqlen: int, rope_base: float = 1e6, out=None, lse=None,
+                            workspace=None, want_lse: bool = True):
+    """q: [M, Hq, D] (token rows may be strided), k/v: [M, Hkv, D] bf16."""
+    m, hq, d = q.shape
+    hkv = k.shape[1]
+    if q.stride(2) != 1 or q.stride(1) != d or k.stride(2) != 1 or k.stride(1) != d or v.stride() != k.stride():
+        raise ValueError("heads must be contiguous within a token row; k and v must share strides")
+    n_seqs = cu_kept.shape[0] - 1
+    dev = q.device
+    if out is None:
+        out = torch.empty((m, hq, d), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((hq, m), dtype=torch.float32, device=dev)
+    need = tg_attn_workspace_bytes(n_seqs, m, hkv, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load().tg_keybias_attn_prefill(_ptr(q), _ptr(k), _ptr(v), q.stride(0), k.stride(0), _ptr(key_score),
+                                        _ptr(head_gain), float(tau), _ptr(pos), _ptr(cu_kept), n_seqs, m,
+                                        int(max_kept_seqlen), hq, hkv, d, float(rope_base), _ptr(out),
+                                        _ptr(lse), _ptr(workspace), workspace.numel(), _stream(q))
+    _check("tg_keybias_attn_prefill", st)
+    return out, lse

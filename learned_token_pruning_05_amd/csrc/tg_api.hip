@@ -1,0 +1,165 @@
+// C ABI of libtokengate: argument validation (before any HIP call) and launch.
+#include <math.h>
+
+#include "tg_common.hpp"
+
+using namespace tg;
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* tg_status_string(int status) {
+    switch (status) {
+        case TG_OK: return "TG_OK";
+        case TG_ERR_INVALID_ARG: return "TG_ERR_INVALID_ARG";
+        case TG_ERR_UNSUPPORTED: return "TG_ERR_UNSUPPORTED";
+        case TG_ERR_WORKSPACE: return "TG_ERR_WORKSPACE";
+        case TG_ERR_HIP: return "TG_ERR_HIP";
+        default: return "TG_ERR_UNKNOWN";
+    }
+}
+
+int tg_kept_counts(int32_t n_seqs, const int32_t* cu_seqlens_h, const int32_t* doc_begin_h,
+                   const int32_t* doc_end_h, const int32_t* k_doc_h, int32_t* cu_kept_h) {
+    if (n_seqs < 0 || !cu_seqlens_h || !cu_kept_h) return TG_ERR_INVALID_ARG;
+    if (n_seqs > 0 && (!doc_begin_h || !doc_end_h || !k_doc_h)) return TG_ERR_INVALID_ARG;
+    if (cu_seqlens_h[0] != 0) return TG_ERR_INVALID_ARG;
+    int64_t acc = 0;
+    cu_kept_h[0] = 0;
+    for (int32_t s = 0; s < n_seqs; ++s) {
+        const int64_t n = (int64_t)cu_seqlens_h[s + 1] - cu_seqlens_h[s];
+        const int32_t b = doc_begin_h[s], e = doc_end_h[s], k = k_doc_h[s];
+        if (n < 0 || b < 0 || b > e || e > n || k < 0) return TG_ERR_INVALID_ARG;
+        const int64_t nd = e - b;
+        acc += (k < nd ? k : nd) + (n - nd);
+        if (acc > INT32_MAX) return TG_ERR_INVALID_ARG;
+        cu_kept_h[s + 1] = (int32_t)acc;
+    }
+    return TG_OK;
+}
+
+int tg_gate_score(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d_model,
+                  int64_t x_row_stride, const void* w1, const float* b1, const float* w2,
+                  float b2, int32_t d_hid, float* scores, void* stream) {
+    if (n_tokens < 0 || d_model <= 0 || d_hid <= 0 || !isfinite(b2)) return TG_ERR_INVALID_ARG;
+    if (x_dtype != TG_F32 && x_dtype != TG_BF16) return TG_ERR_INVALID_ARG;
+    if (d_model % 8 != 0 || x_row_stride < d_model || x_row_stride % 8 != 0) return TG_ERR_INVALID_ARG;
+    if (n_tokens == 0) return TG_OK;
+    if (!x || !w1 || !w2 || !scores || !aligned16(x) || !aligned16(w1)) return TG_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    if (x_dtype == TG_BF16) {
+        if (d_model % 32 != 0) return TG_ERR_UNSUPPORTED;
+        if (d_hid != 64 && d_hid != 128 && d_hid != 192 && d_hid != 256) return TG_ERR_UNSUPPORTED;
+        return launch_gate_bf16((const bf16*)x, n_tokens, d_model, x_row_stride, (const bf16*)w1, b1,
+                                w2, b2, d_hid, scores, st);
+    }
+    if (d_hid > 1024 || d_model > 2048) return TG_ERR_UNSUPPORTED;
+    return launch_gate_f32((const float*)x, n_tokens, d_model, x_row_stride, (const float*)w1, b1, w2,
+                           b2, d_hid, scores, st);
+}
+
+size_t tg_topk_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen) {
+    (void)n_seqs;
+    (void)n_tokens_total;
+    (void)max_seqlen;
+    return 0;
+}
+
+int tg_topk_select(const float* scores, int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen,
+                   const int32_t* cu_seqlens, const int32_t* doc_begin, const int32_t* doc_end,
+                   const int32_t* k_doc, const int32_t* cu_kept, int32_t* kept_idx,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (n_seqs < 0 || n_tokens_total < 0 || n_tokens_total > INT32_MAX || max_seqlen < 0)
+        return TG_ERR_INVALID_ARG;
+    if (n_seqs == 0) return TG_OK;
+    if (!cu_seqlens || !doc_begin || !doc_end || !k_doc || !cu_kept || !kept_idx)
+        return TG_ERR_INVALID_ARG;
+    if (n_tokens_total > 0 && !scores) return TG_ERR_INVALID_ARG;
+    return launch_topk(scores, n_seqs, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, kept_idx,
+                       (hipStream_t)stream);
+}
+
+int tg_gather_kept(const void* x, int32_t x_dtype, int32_t d_model, int64_t x_row_stride,
+                   const float* scores, const int32_t* kept_idx, int64_t n_kept_total,
+                   int32_t n_seqs, const int32_t* cu_seqlens, const int32_t* cu_kept,
+                   void* x_kept, float* scores_kept, int32_t* pos_kept, void* stream) {
+    if (n_kept_total < 0 || n_seqs < 0 || d_model <= 0) return TG_ERR_INVALID_ARG;
+    if (x_dtype != TG_F32 && x_dtype != TG_BF16) return TG_ERR_INVALID_ARG;
+    if (d_model % 8 != 0 || x_row_stride < d_model || x_row_stride % 8 != 0) return TG_ERR_INVALID_ARG;
+    if (n_kept_total == 0) return TG_OK;
+    if (!x || !kept_idx || !x_kept || !aligned16(x) || !aligned16(x_kept)) return TG_ERR_INVALID_ARG;
+    if (scores_kept && !scores) return TG_ERR_INVALID_ARG;
+    if (pos_kept && (n_seqs < 1 || !cu_seqlens || !cu_kept)) return TG_ERR_INVALID_ARG;
+    const int esize = x_dtype == TG_BF16 ? 2 : 4;
+    return launch_gather(x, esize, d_model, x_row_stride, scores, kept_idx, n_kept_total, n_seqs,
+                         cu_seqlens, cu_kept, x_kept, scores_kept, pos_kept, (hipStream_t)stream);
+}
+
+size_t tg_attn_workspace_bytes(int32_t n_seqs, int64_t n_kept_total, int32_t n_kv_heads,
+                               int32_t head_dim) {
+    if (n_seqs < 0 || n_kept_total < 0 || n_kv_heads <= 0 || head_dim <= 0) return 0;
+    return attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, nullptr, nullptr,
+                                 nullptr);
+}
+
+int tg_keybias_attn_prefill(const void* q, const void* k, const void* v, int64_t q_row_stride,
+                            int64_t kv_row_stride, const float* key_score, const float* head_gain,
+                            float tau, const int32_t* pos, const int32_t* cu_kept, int32_t n_seqs,
+                            int64_t n_kept_total, int32_t max_kept_seqlen, int32_t n_q_heads,
+                            int32_t n_kv_heads, int32_t head_dim, double rope_base, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!(tau > 0.0f) || !isfinite(tau) || !isfinite(rope_base)) return TG_ERR_INVALID_ARG;
+    if (n_seqs < 0 || n_kept_total < 0 || n_kept_total > INT32_MAX || max_kept_seqlen < 0)
+        return TG_ERR_INVALID_ARG;
+    if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0) return TG_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return TG_ERR_UNSUPPORTED;
+    const int grp = n_q_heads / n_kv_heads;
+    if (grp != 1 && grp != 2 && grp != 4 && grp != 8) return TG_ERR_UNSUPPORTED;
+    if (q_row_stride < (int64_t)n_q_heads * head_dim || q_row_stride % 8 != 0) return TG_ERR_INVALID_ARG;
+    if (kv_row_stride < (int64_t)n_kv_heads * head_dim || kv_row_stride % 8 != 0) return TG_ERR_INVALID_ARG;
+    if (n_kept_total == 0) return TG_OK;
+    if (n_seqs < 1 || max_kept_seqlen < 1 || max_kept_seqlen > n_kept_total) return TG_ERR_INVALID_ARG;
+    if (!q || !k || !v || !key_score || !head_gain || !pos || !cu_kept || !out) return TG_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return TG_ERR_INVALID_ARG;
+    size_t off_k, off_vt, off_cs;
+    const size_t need = attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, &off_k,
+                                              &off_vt, &off_cs);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+        return TG_ERR_WORKSPACE;
+    AttnArgs a;
+    a.q = (const bf16*)q;
+    a.k = (const bf16*)k;
+    a.v = (const bf16*)v;
+    a.q_stride = q_row_stride;
+    a.kv_stride = kv_row_stride;
+    a.key_score = key_score;
+    a.gain = head_gain;
+    a.qk_scale_log2 = (float)(1.4426950408889634 / (sqrt((double)head_dim) * (double)tau));
+    a.pos = pos;
+    a.cu_kept = cu_kept;
+    a.n_seqs = n_seqs;
+    a.m_tot = n_kept_total;
+    a.max_kept_seqlen = max_kept_seqlen;
+    a.hq = n_q_heads;
+    a.hkv = n_kv_heads;
+    a.d = head_dim;
+    a.rope = rope_base > 0.0;
+    a.rope_log2_base = a.rope ? log2(rope_base) : 0.0;
+    a.out = (bf16*)out;
+    a.lse = lse;
+    char* ws = (char*)workspace;
+    a.ws_k = (bf16*)(ws + off_k);
+    a.ws_vt = (bf16*)(ws + off_vt);
+    a.ws_cs = (float2*)(ws + off_cs);
+    a.mp = attn_padded_rows(n_seqs, n_kept_total);
+    return launch_attn(a, (hipStream_t)stream);
+}
+
+}  // extern "C"

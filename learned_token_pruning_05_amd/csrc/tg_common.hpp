@@ -1,0 +1,81 @@
+// Shared types and helpers of the libtokengate kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tokengate.h"
+
+namespace tg {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Launchers, one per kernel family.  Each returns TG_OK or TG_ERR_HIP.
+int launch_gate_bf16(const bf16* x, int64_t n, int d_model, int64_t x_stride, const bf16* w1,
+                     const float* b1, const float* w2, float b2, int d_hid, float* scores,
+                     hipStream_t st);
+int launch_gate_f32(const float* x, int64_t n, int d_model, int64_t x_stride, const float* w1,
+                    const float* b1, const float* w2, float b2, int d_hid, float* scores,
+                    hipStream_t st);
+int launch_topk(const float* scores, int n_seqs, const int* cu_seqlens, const int* doc_begin,
+                const int* doc_end, const int* k_doc, const int* cu_kept, int* kept_idx,
+                hipStream_t st);
+int launch_gather(const void* x, int esize, int d_model, int64_t x_stride, const float* scores,
+                  const int* kept_idx, int64_t m_tot, int n_seqs, const int* cu_seqlens,
+                  const int* cu_kept, void* x_kept, float* s_kept, int* pos_kept, hipStream_t st);
+
+struct AttnArgs {
+    const bf16* q;
+    const bf16* k;
+    const bf16* v;
+    int64_t q_stride, kv_stride;
+    const float* key_score;
+    const float* gain;
+    float qk_scale_log2;   // log2(e) / (sqrt(D) * tau)
+    const int* pos;
+    const int* cu_kept;
+    int n_seqs;
+    int64_t m_tot;
+    int max_kept_seqlen;
+    int hq, hkv, d;
+    double rope_log2_base;  // log2(rope base); <= -1e300 when rotary embedding is off
+    bool rope;
+    bf16* out;
+    float* lse;
+    // workspace carve-up
+    bf16* ws_k;       // [Hkv][Mp][D]  rotated keys, per-sequence padded rows
+    bf16* ws_vt;      // [Hkv][D][Mp]  values, transposed
+    float2* ws_cs;    // [M][D/2]      (cos, sin) per kept token and frequency
+    int64_t mp;       // padded row count
+};
+int64_t attn_padded_rows(int n_seqs, int64_t m_tot);
+size_t attn_workspace_layout(int n_seqs, int64_t m_tot, int hkv, int d, size_t* off_k,
+                             size_t* off_vt, size_t* off_cs);
+int launch_attn(const AttnArgs& a, hipStream_t st);
+
+// Upper-bound search: the sequence s with cu[s] <= m < cu[s+1] (cu non-decreasing,
+// cu[0] <= m < cu[n]).
+__device__ __forceinline__ int find_seq(const int* __restrict__ cu, int n, int64_t m) {
+    int lo = 0, hi = n;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (cu[mid] <= m) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// First padded workspace row of kept sequence s: a multiple of 8 (16-byte
+// aligned bf16 rows for vector loads), and sequences never overlap.
+__device__ __host__ __forceinline__ int64_t padded_seq_start(int64_t cu_kept_s, int s) {
+    return (cu_kept_s + 8 * (int64_t)s + 7) & ~(int64_t)7;
+}
+
+}  // namespace tg

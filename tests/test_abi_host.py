@@ -1,0 +1,144 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call.  No GPU."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tokengate.h")
+
+
+def _declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tg_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_hot_path_calls():
+    syms = _declared_symbols()
+    for s in ("tg_gate_score", "tg_topk_select", "tg_gather_kept", "tg_keybias_attn_prefill"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from learned_token_pruning_05_amd import _lib
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for s in _declared_symbols():
+        assert hasattr(raw, s), s
+        assert s in _lib.SIGNATURES, s
+
+
+def test_status_strings(lib):
+    from learned_token_pruning_05_amd import _lib
+    assert _lib.status_string(0) == "TG_OK"
+    assert _lib.status_string(3) == "TG_ERR_WORKSPACE"
+    assert _lib.status_string(99) == "TG_ERR_UNKNOWN"
+
+
+def test_kept_counts_matches_definition(lib):
+    from learned_token_pruning_05_amd import _lib
+    for w in workloads.all_configs() + [workloads.custom([5, 1, 9, 0], [2, 1, 0, 0], [1, 7, 3, 0])]:
+        got = _lib.tg_kept_counts(w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+        want = oracle.kept_counts(w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+        assert got.tolist() == want.tolist(), w.name
+
+
+@pytest.mark.parametrize("bad", [
+    dict(doc_end=[6]),          # span beyond the sequence
+    dict(doc_begin=[3], doc_end=[2]),
+    dict(k_doc=[-1]),
+    dict(cu=[1, 6]),            # cu_seqlens[0] != 0
+])
+def test_kept_counts_rejects(lib, bad):
+    from learned_token_pruning_05_amd import _lib
+    args = dict(cu=[0, 5], doc_begin=[0], doc_end=[3], k_doc=[1])
+    args.update(bad)
+    with pytest.raises(_lib.TokenGateError):
+        _lib.tg_kept_counts(args["cu"], args["doc_begin"], args["doc_end"], args["k_doc"])
+
+
+# Raw calls with NULL / fake pointers: every one must fail validation and
+# return before any HIP call, so no device memory is touched.
+FAKE = ctypes.c_void_p(0x1000)     # 16-B aligned, never dereferenced
+MIS = ctypes.c_void_p(0x1004)      # misaligned
+
+
+def test_gate_validation(lib):
+    L = lib
+    E, U = 1, 2
+    g = lambda **kw: L.tg_gate_score(*[kw.get(k, v) for k, v in [
+        ("x", FAKE), ("dt", 1), ("n", 10), ("d", 2048), ("stride", 2048), ("w1", FAKE), ("b1", None),
+        ("w2", FAKE), ("b2", 0.0), ("dh", 256), ("out", FAKE), ("st", None)]])
+    assert g(n=-1) == E
+    assert g(dt=7) == E
+    assert g(d=2047) == E
+    assert g(stride=1024) == E
+    assert g(b2=float("nan")) == E
+    assert g(x=None) == E
+    assert g(x=MIS) == E
+    assert g(w2=None) == E
+    assert g(dh=100) == U
+    assert g(d=2056, stride=2056) == U           # bf16 path needs d_model % 32 == 0
+    assert g(dt=0, d=4096, stride=4096) == U     # fp32 path limit
+    assert g(n=0) == 0                          # empty: no launch
+
+
+def test_topk_validation(lib):
+    L = lib
+    t = lambda **kw: L.tg_topk_select(*[kw.get(k, v) for k, v in [
+        ("s", FAKE), ("ns", 1), ("n", 10), ("mx", 10), ("cu", FAKE), ("b", FAKE), ("e", FAKE), ("k", FAKE),
+        ("ck", FAKE), ("out", FAKE), ("ws", None), ("wsb", 0), ("st", None)]])
+    assert t(ns=-1) == 1
+    assert t(n=-5) == 1
+    assert t(n=2 ** 31) == 1
+    assert t(cu=None) == 1
+    assert t(out=None) == 1
+    assert t(s=None) == 1
+    assert t(ns=0) == 0
+
+
+def test_gather_validation(lib):
+    L = lib
+    t = lambda **kw: L.tg_gather_kept(*[kw.get(k, v) for k, v in [
+        ("x", FAKE), ("dt", 1), ("d", 2048), ("stride", 2048), ("s", FAKE), ("ki", FAKE), ("m", 10),
+        ("ns", 1), ("cu", FAKE), ("ck", FAKE), ("xk", FAKE), ("sk", FAKE), ("pk", FAKE), ("st", None)]])
+    assert t(m=-1) == 1
+    assert t(d=12, stride=12) == 1
+    assert t(x=MIS) == 1
+    assert t(xk=None) == 1
+    assert t(s=None) == 1          # scores_kept requested without scores
+    assert t(cu=None) == 1         # positions requested without metadata
+    assert t(m=0) == 0
+
+
+def test_attn_validation(lib):
+    L = lib
+    need = L.tg_attn_workspace_bytes(1, 100, 8, 128)
+    assert need > 100 * 8 * 128 * 2 * 2
+    a = lambda **kw: L.tg_keybias_attn_prefill(*[kw.get(k, v) for k, v in [
+        ("q", FAKE), ("k", FAKE), ("v", FAKE), ("qs", 2048), ("kvs", 1024), ("ks", FAKE), ("g", FAKE),
+        ("tau", 0.9), ("pos", FAKE), ("ck", FAKE), ("ns", 1), ("m", 100), ("mx", 100), ("hq", 16),
+        ("hkv", 8), ("d", 128), ("rb", 1e6), ("out", FAKE), ("lse", None), ("ws", FAKE), ("wsb", need),
+        ("st", None)]])
+    assert a(tau=0.0) == 1
+    assert a(tau=-1.0) == 1
+    assert a(tau=float("inf")) == 1
+    assert a(rb=float("nan")) == 1
+    assert a(hq=12) == 1               # not a multiple of Hkv
+    assert a(d=96) == 2                # unsupported head_dim
+    assert a(hq=24, qs=3072) == 2      # group size 3
+    assert a(qs=1000) == 1             # stride too small
+    assert a(kvs=1028) == 1            # stride not a multiple of 8
+    assert a(mx=101) == 1              # longer than the total
+    assert a(q=None) == 1
+    assert a(v=MIS) == 1
+    assert a(wsb=need - 1) == 3        # workspace too small
+    assert a(ws=ctypes.c_void_p(0x1010)) == 3   # workspace not 256-B aligned
+    assert a(m=0) == 0
