@@ -1,0 +1,269 @@
+"""Benchmark of one gated layer of TokenGate's pruned prefill on one MI355X.
+
+One step = tg_gate_score -> tg_topk_select -> tg_gather_kept ->
+tg_keybias_attn_prefill on one batch of seeded synthetic input, all resident in
+HBM before the timed region.  Q/K/V are synthetic stand-ins for the host
+model's projections of the kept residuals (sized by the kept count); the
+projections themselves are outside the gated layer.
+
+Prints one JSON line: ms per gated layer at 128k (headline), per-stage times
+from HIP events recorded on the launch stream, the attention roofline against
+the bf16 MFMA peak, top-K + gather bandwidth against HBM, the 32k budget sweep,
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+from learned_token_pruning_05_amd import _lib as tg  # noqa: E402
+
+METRIC = "ms/gated layer + key-bias attn TFLOP/s (frac bf16 peak) at 32k/128k, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PROFILE_PMC = os.path.join(ROOT, "profiles", "attn_fwd_128k_pmc.md")
+
+
+def attn_flops(cu_kept, hq, d):
+    m = np.diff(np.asarray(cu_kept, dtype=np.int64))
+    return float(2 * d * hq * np.sum(m * (m + 1)))
+
+
+class Layer:
+    """Device-resident inputs, outputs and workspace of one gated layer."""
+
+    def __init__(self, w: workloads.Workload):
+        dev = torch.device("cuda:0")
+        self.w = w
+        g = w.gate_inputs()
+        self.x = g["x"].to(dev)
+        self.w1 = g["w1"].to(dev)
+        self.w2 = g["w2"].to(dev)
+        self.b2 = g["b2"]
+        i32 = lambda a: torch.from_numpy(np.asarray(a, dtype=np.int32)).to(dev)
+        self.cu = i32(w.cu_seqlens)
+        self.db, self.de, self.kd = i32(w.doc_begin), i32(w.doc_end), i32(w.k_doc_arr)
+        self.ck_h = tg.tg_kept_counts(w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+        self.ck = i32(self.ck_h)
+        self.m = int(self.ck_h[-1])
+        self.max_seq = int(max(w.seqlens))
+        self.max_kept = int(np.diff(self.ck_h).max())
+        q, k, v = w.qkv(self.m)
+        self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
+        gain, self.tau = w.attn_params()
+        self.gain = torch.from_numpy(gain).to(dev)
+        n = w.n_tokens
+        self.scores = torch.empty(n, dtype=torch.float32, device=dev)
+        self.kept = torch.empty(self.m, dtype=torch.int32, device=dev)
+        self.xk = torch.empty((self.m, w.d_model), dtype=self.x.dtype, device=dev)
+        self.sk = torch.empty(self.m, dtype=torch.float32, device=dev)
+        self.pk = torch.empty(self.m, dtype=torch.int32, device=dev)
+        self.out = torch.empty((self.m, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((w.n_q_heads, self.m), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(tg.tg_attn_workspace_bytes(w.n_seqs, self.m, w.n_kv_heads, w.head_dim),
+                              dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, ev=None):
+        """One gated layer; ev = 5 events recorded between the stages, or None."""
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        tg.tg_gate_score(self.x, self.w1, None, self.w2, self.b2, scores=self.scores)
+        rec(1)
+        tg.tg_topk_select(self.scores, self.cu, self.db, self.de, self.kd, self.ck, self.m, self.max_seq,
+                          kept_idx=self.kept)
+        rec(2)
+        tg.tg_gather_kept(self.x, self.scores, self.kept, self.cu, self.ck, x_kept=self.xk,
+                          scores_kept=self.sk, pos_kept=self.pk)
+        rec(3)
+        tg.tg_keybias_attn_prefill(self.q, self.k, self.v, self.sk, self.gain, self.tau, self.pk, self.ck,
+                                   self.max_kept, rope_base=self.w.rope_base, out=self.out, lse=self.lse,
+                                   workspace=self.ws)
+        rec(4)
+
+    def measure(self, steps, warmup):
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(evs[i])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps * 1e3
+        st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])   # ms
+        layer = np.array([e[0].elapsed_time(e[4]) for e in evs])
+        return dict(wall_ms=wall, stage_ms=st.mean(axis=0), layer_ms=float(layer.mean()),
+                    layer_ms_p10=float(np.percentile(layer, 10)), layer_ms_p90=float(np.percentile(layer, 90)))
+
+    # algorithmic work per launch
+    def gate_work(self):
+        w = self.w
+        n, d, dh = w.n_tokens, w.d_model, w.d_hid
+        e = self.x.element_size()
+        return 2.0 * n * d * dh, float(n * d * e + dh * d * e + 4 * n)
+
+    def topk_gather_bytes(self):
+        n, m, d = self.w.n_tokens, self.m, self.w.d_model
+        e = self.x.element_size()
+        return float(4 * n + 4 * m + m * (2 * d * e + 12) + 4 * m)
+
+    def attn_work(self):
+        return attn_flops(self.ck_h, self.w.n_q_heads, self.w.head_dim)
+
+
+def pmc_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source (else None)."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    import hashlib
+    src = os.path.join(ROOT, "learned_token_pruning_05_amd", "csrc", "tg_attn.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    vals = {}
+    for line in open(PROFILE_PMC):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().split()[0]
+    if vals.get("kernel_source_sha256_16") != sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w: workloads.Workload):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload,
+    scaled to one full gated layer."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    g = w.gate_inputs()
+    n = w.n_tokens
+    gate_rows = min(n, 8192)
+    t = time.perf_counter()
+    oracle.gate_score(g["x_f"][:gate_rows], g["w1_f"], g["b1_f"], g["w2_f"], g["b2"])
+    gate_ms = (time.perf_counter() - t) * 1e3 * n / gate_rows
+    s32 = w.topk_scores()                   # seeded selector input of this workload's shape
+    t = time.perf_counter()
+    kept, ck = oracle.topk_select(s32, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+    topk_ms = (time.perf_counter() - t) * 1e3
+    t = time.perf_counter()
+    _, sk, pk = oracle.gather_kept(g["x_f"], s32, kept, w.cu_seqlens, ck)
+    gather_ms = (time.perf_counter() - t) * 1e3
+    m = int(ck[-1])
+    q, k, v = (t_.float().numpy() for t_ in w.qkv(m))
+    gain, tau = w.attn_params()
+    rows = np.linspace(0, m - 1, 256).astype(np.int64)
+    t = time.perf_counter()
+    oracle.keybias_attention(q, k, v, sk, gain, tau, pk, ck, rope_base=w.rope_base, rows=rows)
+    attn_ms = (time.perf_counter() - t) * 1e3 * m / len(rows)   # the oracle's cost per row is flat in i
+    total = gate_ms + topk_ms + gather_ms + attn_ms
+    return {"value": round(total, 3), "unit": "ms/gated layer", "cores": int(threads), "kind": "oracle",
+            "sample": f"{w.name}: gate on {gate_rows} of {n} rows (scaled x{n / gate_rows:.1f}), full top-K and "
+                      f"gather, attention on 256 of {m} query rows, all heads (scaled x{m / 256:.1f}); "
+                      f"per stage ms: gate {gate_ms:.0f}, topk {topk_ms:.0f}, gather {gather_ms:.0f}, "
+                      f"attn {attn_ms:.0f}"}
+
+
+def summarize(layer: Layer, r):
+    gate_s, topk_s, gather_s, attn_s = (x * 1e-3 for x in r["stage_ms"])
+    gf, gb = layer.gate_work()
+    tb = layer.topk_gather_bytes()
+    af = layer.attn_work()
+    return {
+        "ms_per_gated_layer": round(r["layer_ms"], 4),
+        "stage_us": {"gate": round(gate_s * 1e6, 2), "topk": round(topk_s * 1e6, 2),
+                     "gather": round(gather_s * 1e6, 2), "attn": round(attn_s * 1e6, 2)},
+        "attn_tflops": round(af / attn_s / 1e12, 2), "attn_frac_bf16_peak": round(af / attn_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "topk_gather_gbs": round(tb / (topk_s + gather_s) / 1e9, 1),
+        "topk_gather_frac_hbm": round(tb / (topk_s + gather_s) / 1e9 / PEAK_HBM_GBS, 4),
+        "gate_tflops": round(gf / gate_s / 1e12, 2), "gate_gbs": round(gb / gate_s / 1e9, 1),
+        "kept": layer.m,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 32k budget sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              f"(the multi-GPU sharding is a design, not an implementation).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    tg.load()
+
+    w = workloads.long128k()
+    layer = Layer(w)
+    r = layer.measure(args.steps, args.warmup)
+    head = summarize(layer, r)
+    af = layer.attn_work()
+    attn_s = r["stage_ms"][3] * 1e-3
+    achieved = af / attn_s / 1e12
+
+    sweep = {}
+    if not args.no_sweep:
+        for pct in workloads.BUDGET_PCTS:
+            ws = workloads.sweep32k(pct)
+            ls = Layer(ws)
+            rs = ls.measure(max(5, args.steps // 2), 2)
+            sweep[ws.name] = summarize(ls, rs)
+            del ls
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w)
+
+    line = {
+        "metric": METRIC,
+        "value": round(r["layer_ms"], 4),
+        "unit": "ms/gated layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["wall_ms"], 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; Qwen3-1.7B-shaped gated layer, stands in for the pages' NIAH/QA workloads)",
+        "config": {"workload": "128k: 1 sequence, N=131072 (130816 document + 256 question), keep 8192 "
+                               "document tokens (M=8448), d_model 2048 bf16, gate 2048->256->1, 16 q / 8 kv "
+                               "heads, head_dim 128, RoPE 1e6, causal key-bias attention over kept tokens",
+                   "global_batch": 1, "seq_len": w.n_tokens, "kept": layer.m, "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "tg_keybias_attn_prefill (rotary/transposition pre-pass + attn_fwd_kernel)",
+                     "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": pmc_traffic()},
+        "gated_layer_128k": head,
+        "sweep_32k": sweep,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
