@@ -71,6 +71,8 @@ class Layer:
         self.pk = torch.empty(self.m, dtype=torch.int32, device=dev)
         self.out = torch.empty((self.m, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((w.n_q_heads, self.m), dtype=torch.float32, device=dev)
+        self.ws_topk = torch.empty(tg.tg_topk_workspace_bytes(w.n_seqs, n, self.max_seq), dtype=torch.uint8,
+                                   device=dev)
         self.ws = torch.empty(tg.tg_attn_workspace_bytes(w.n_seqs, self.m, w.n_kv_heads, w.head_dim),
                               dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
@@ -82,7 +84,7 @@ class Layer:
         tg.tg_gate_score(self.x, self.w1, None, self.w2, self.b2, scores=self.scores)
         rec(1)
         tg.tg_topk_select(self.scores, self.cu, self.db, self.de, self.kd, self.ck, self.m, self.max_seq,
-                          kept_idx=self.kept)
+                          kept_idx=self.kept, workspace=self.ws_topk)
         rec(2)
         tg.tg_gather_kept(self.x, self.scores, self.kept, self.cu, self.ck, x_kept=self.xk,
                           scores_kept=self.sk, pos_kept=self.pk)

@@ -84,14 +84,16 @@ int tg_kept_counts(int32_t n_seqs, const int32_t* cu_seqlens_h, const int32_t* d
  *   b2            scalar fp32 output bias
  *   scores        [device, out] n_tokens fp32
  * Requirements: d_model % 8 == 0, x_row_stride >= d_model and % 8 == 0,
- * x and w1 16-byte aligned.  bf16: d_hid in {32, 64, ..., 256} (multiple of
- * 32); fp32: 1 <= d_hid <= 1024, d_model <= 8192.  n_tokens == 0 is a no-op.
+ * x and w1 16-byte aligned.  bf16: d_model % 32 == 0 and d_hid in {64, 128,
+ * 192, 256}; fp32: 1 <= d_hid <= 1024 and d_model <= 2048 (TG_ERR_UNSUPPORTED
+ * otherwise).  n_tokens == 0 is a no-op.
  */
 int tg_gate_score(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d_model,
                   int64_t x_row_stride, const void* w1, const float* b1, const float* w2,
                   float b2, int32_t d_hid, float* scores, void* stream);
 
-/* Workspace bytes tg_topk_select needs (0 for this build; kept for ABI growth). */
+/* Workspace bytes tg_topk_select needs: per-sequence state and histogram,
+ * per-chunk counts, and 8 bytes per token for threshold candidates. */
 size_t tg_topk_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen);
 
 /*
@@ -108,8 +110,14 @@ size_t tg_topk_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32_t m
  *   cu_kept       [device] S+1 int32, as produced by tg_kept_counts
  *   kept_idx      [device, out] cu_kept[S] int32 GLOBAL token indices,
  *                 ascending within each sequence
- *   max_seqlen    host upper bound of n_s (used for validation only)
- * Errors: TG_ERR_INVALID_ARG on NULL pointers or negative sizes.
+ *   max_seqlen    host upper bound of every n_s (sizes the grid); at most 4 Mi
+ *                 tokens and at most n_tokens_total
+ *   workspace     [device] >= tg_topk_workspace_bytes(...) bytes, 256-byte
+ *                 aligned, contents need not be initialised
+ * Errors: TG_ERR_INVALID_ARG on NULL pointers or bad sizes, TG_ERR_UNSUPPORTED
+ * for max_seqlen above 4 Mi, TG_ERR_WORKSPACE for a missing or short workspace.
+ * n_s > max_seqlen is undefined behaviour (outputs incomplete, never out of
+ * bounds).
  */
 int tg_topk_select(const float* scores, int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen,
                    const int32_t* cu_seqlens, const int32_t* doc_begin, const int32_t* doc_end,

@@ -16,4 +16,5 @@ from ._lib import (  # noqa: F401
     tg_kept_counts,
     tg_keybias_attn_prefill,
     tg_topk_select,
+    tg_topk_workspace_bytes,
 )

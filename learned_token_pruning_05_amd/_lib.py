@@ -118,18 +118,23 @@ def tg_gate_score(x, w1, b1, w2, b2: float, scores=None):
     return scores
 
 
+def tg_topk_workspace_bytes(n_seqs, n_tokens_total, max_seqlen) -> int:
+    return load().tg_topk_workspace_bytes(n_seqs, n_tokens_total, max_seqlen)
+
+
 def tg_topk_select(scores, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, n_kept_total: int,
-                   max_seqlen: int, kept_idx=None):
+                   max_seqlen: int, kept_idx=None, workspace=None):
     """Device metadata tensors (int32); n_kept_total = cu_kept[-1] known on the host."""
     n_seqs = cu_seqlens.shape[0] - 1
     if kept_idx is None:
         kept_idx = torch.empty(n_kept_total, dtype=torch.int32, device=scores.device)
     lib = load()
-    ws_bytes = lib.tg_topk_workspace_bytes(n_seqs, scores.shape[0], max_seqlen)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=scores.device) if ws_bytes else None
+    if workspace is None:
+        need = lib.tg_topk_workspace_bytes(n_seqs, scores.shape[0], max_seqlen)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=scores.device)
     st = lib.tg_topk_select(_ptr(scores), n_seqs, scores.shape[0], max_seqlen, _ptr(cu_seqlens), _ptr(doc_begin),
-                            _ptr(doc_end), _ptr(k_doc), _ptr(cu_kept), _ptr(kept_idx), _ptr(ws), ws_bytes,
-                            _stream(scores))
+                            _ptr(doc_end), _ptr(k_doc), _ptr(cu_kept), _ptr(kept_idx), _ptr(workspace),
+                            workspace.numel(), _stream(scores))
     _check("tg_topk_select", st)
     return kept_idx
 

@@ -8,23 +8,33 @@
 // causal on original positions, R = rotary embedding on original positions.
 //
 // Work split.
-//  1. attn_prep_k_kernel: per kept token, rotary angles in fp64 (reduced mod 2pi)
-//     -> fp32 (cos, sin) table; keys rotated in fp32, rounded to bf16 and stored
-//     head-major [Hkv][row][D] so a 64-key tile is one contiguous 16 KiB block.
-//  2. attn_prep_v_kernel: values transposed to [Hkv][D][row] so the P.V MFMA
-//     operand (8 keys per lane at fixed d) is two 8-byte LDS reads.
-//     Rows are padded per sequence (16-byte aligned starts).
-//  3. attn_fwd_kernel: FlashAttention-style online softmax in the log2 domain.
-//     S^T = K.Q^T on 32x32x16 bf16 MFMA puts one query per lane (lane & 31), so
-//     row statistics are per-lane scalars combined across the two 32-lane
-//     halves with one permlane32 swap; P^T feeds O^T = V^T.P^T directly from
-//     the S^T accumulator registers (8 consecutive accumulators are exactly
-//     one 16-key MFMA step, with the V^T operand read in the matching key
-//     order).  Scale and bias fold into one FMA per logit:
-//         t = qk * log2(e)/(sqrt(D) tau) + g_h log2(e) s_j,  p = exp2(t - m).
+//  1. attn_prep_kernel (one workgroup per 64 kept tokens):
+//     - rotary angles pos * base^(-2f/D) in fp64, reduced mod 2pi, then fp32
+//       (cos, sin), kept as a per-token table for the queries;
+//     - keys rotated in fp32 and rounded to bf16 into K' rows [Hkv][row][D+16]
+//       whose 16 extra columns carry the key score split in two bf16 halves
+//       (s_hi, s_lo, s_hi, 0...), so the bias rides inside the QK MFMA;
+//     - values transposed through LDS to V^T [Hkv][D][row] (coalesced stores),
+//       the layout the P.V MFMA operand wants.
+//     Rows are padded per sequence so every sequence starts 16-byte aligned.
+//  2. attn_fwd_kernel: FlashAttention-style online softmax in the log2 domain.
+//     Queries are rotated, scaled by log2(e)/(sqrt(D) tau) and rounded to bf16
+//     once per workgroup; their 16 extra columns hold (g_hi, g_hi, g_lo, 0...)
+//     with g = g_h log2(e), so one extra MFMA k-step adds
+//     g_hi s_hi + g_hi s_lo + g_lo s_hi = g s (to ~2^-16 relative) and the MFMA
+//     output is already the log2-domain logit.  S^T = K'.Q'^T on 32x32x16 bf16
+//     MFMA puts one query per lane (lane & 31): row statistics are per-lane
+//     scalars combined across the two 32-lane halves with one permlane32 swap;
+//     P^T feeds O^T = V^T.P^T straight from the S^T accumulators (8 consecutive
+//     accumulators are one 16-key MFMA step, V^T read in the matching order).
+//     The running max is refreshed only when a tile raises it by more than 8
+//     (p <= 2^8 otherwise; the result is exact either way), so the O rescale is
+//     rare; row sums use v_dot2 on the bf16 P that the P.V MFMA consumes.
 //     All q heads of a KV group that fit in the workgroup share each K/V tile.
 //     Causality uses the kept order (positions increase within a sequence, so
-//     pos_j <= pos_i  <=>  j <= i).
+//     pos_j <= pos_i  <=>  j <= i).  Blocks are ordered head-fastest so that,
+//     with workgroups dealt round-robin to the 8 XCDs, each KV head keeps to
+//     one XCD's L2.
 #include <math.h>
 
 #include "tg_common.hpp"
@@ -40,7 +50,7 @@ static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 size_t attn_workspace_layout(int n_seqs, int64_t m_tot, int hkv, int d, size_t* off_k,
                              size_t* off_vt, size_t* off_cs) {
     const int64_t mp = attn_padded_rows(n_seqs, m_tot);
-    const size_t kb = align256((size_t)hkv * mp * d * 2);
+    const size_t kb = align256((size_t)hkv * mp * (d + 16) * 2);
     const size_t vb = align256((size_t)hkv * mp * d * 2);
     const size_t cb = align256((size_t)(m_tot > 0 ? m_tot : 1) * (d / 2) * sizeof(float2));
     if (off_k) *off_k = 0;
@@ -51,91 +61,127 @@ size_t attn_workspace_layout(int n_seqs, int64_t m_tot, int hkv, int d, size_t* 
 
 namespace {
 
-constexpr int kBN = 64;   // keys per tile
+constexpr int kBN = 64;     // keys per tile
+constexpr int kExtra = 16;  // extra K'/Q' columns carrying the key bias
+
+struct RopeFreqs {
+    double inv_freq[64];   // base^(-2f/D), f < D/2
+};
+
+__device__ __forceinline__ void split_bf16(float x, bf16* hi, bf16* lo) {
+    const bf16 h = (bf16)x;
+    *hi = h;
+    *lo = (bf16)(x - (float)h);
+}
 
 // ---------------------------------------------------------------- pre-pass --
-// One thread per (kept token, chunk of 8 frequency pairs).
 template <int D>
-__global__ __launch_bounds__(256) void attn_prep_k_kernel(
-    const bf16* __restrict__ k, int64_t kv_stride, const int* __restrict__ pos,
-    const int* __restrict__ cu_kept, int n_seqs, int64_t m_tot, int hkv, int64_t mp,
-    double log2_base, int rope, bf16* __restrict__ ws_k, float2* __restrict__ ws_cs) {
-    constexpr int HALF = D / 2, NCH = HALF / 8;
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t m = gid / NCH;
-    const int c = (int)(gid % NCH);
-    if (m >= m_tot) return;
-    const int s = find_seq(cu_kept, n_seqs, m);
-    const int64_t prow = padded_seq_start(cu_kept[s], s) + (m - cu_kept[s]);
-    float cs_c[8], cs_s[8];
-    if (rope) {
+__global__ __launch_bounds__(256) void attn_prep_kernel(
+    const bf16* __restrict__ k, const bf16* __restrict__ v, int64_t kv_stride,
+    const float* __restrict__ key_score, const int* __restrict__ pos, const int* __restrict__ cu_kept,
+    int n_seqs, int64_t m_tot, int hkv, int64_t mp, RopeFreqs fr, int rope, bf16* __restrict__ ws_k,
+    bf16* __restrict__ ws_vt, float2* __restrict__ ws_cs) {
+    constexpr int HALF = D / 2, KD = D + kExtra, FPW = HALF / 4, VLD = D + 2;
+    __shared__ __attribute__((aligned(16))) bf16 vs[64 * VLD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t m0 = (int64_t)blockIdx.x * 64;
+    const int64_t m = m0 + lane;
+    const bool valid = m < m_tot;
+    int64_t prow = 0;
+    if (valid) {
+        const int s = find_seq(cu_kept, n_seqs, m);
+        prow = padded_seq_start(cu_kept[s], s) + (m - cu_kept[s]);
+    }
+    const int f0 = wave * FPW;
+    float cn[FPW], sn[FPW];
+    if (rope && valid) {
         const double p = (double)pos[m];
         const double two_pi = 6.283185307179586;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int f = c * 8 + e;
-            const double inv_freq = exp2(-(2.0 * f / D) * log2_base);
-            const double ang = p * inv_freq;
-            const double red = ang - two_pi * rint(ang / two_pi);
-            float sn, cn;
-            sincosf((float)red, &sn, &cn);
-            cs_c[e] = cn;
-            cs_s[e] = sn;
+        for (int e = 0; e < FPW; ++e) {
+            const double ang = p * fr.inv_freq[f0 + e];
+            const double red = ang - two_pi * rint(ang * (1.0 / two_pi));
+            sincosf((float)red, &sn[e], &cn[e]);
         }
-        float4* dst = (float4*)(ws_cs + m * HALF + c * 8);
+        float4* dst = (float4*)(ws_cs + m * HALF + f0);
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) dst[e / 2] = make_float4(cs_c[e], cs_s[e], cs_c[e + 1], cs_s[e + 1]);
+        for (int e = 0; e < FPW; e += 2) dst[e / 2] = make_float4(cn[e], sn[e], cn[e + 1], sn[e + 1]);
     }
-    for (int h = 0; h < hkv; ++h) {
-        const bf16* src = k + m * kv_stride + (int64_t)h * D;
-        bf16x8 x1 = *(const bf16x8*)(src + c * 8);
-        bf16x8 x2 = *(const bf16x8*)(src + HALF + c * 8);
-        if (rope) {
-            bf16x8 y1, y2;
+    // K' rows: rotated keys + bias columns
+    if (valid) {
+        bf16x8 extra[2] = {bf16x8{}, bf16x8{}};
+        if (wave == 0) {
+            bf16 sh, sl;
+            split_bf16(key_score[m], &sh, &sl);
+            extra[0][0] = sh;
+            extra[0][1] = sl;
+            extra[0][2] = sh;
+        }
+        for (int h = 0; h < hkv; ++h) {
+            const bf16* src = k + m * kv_stride + (int64_t)h * D;
+            bf16* dst = ws_k + ((int64_t)h * mp + prow) * KD;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float a = (float)x1[e], b = (float)x2[e];
-                y1[e] = (bf16)(a * cs_c[e] - b * cs_s[e]);
-                y2[e] = (bf16)(b * cs_c[e] + a * cs_s[e]);
+            for (int c = 0; c < FPW / 8; ++c) {
+                bf16x8 x1 = *(const bf16x8*)(src + f0 + c * 8);
+                bf16x8 x2 = *(const bf16x8*)(src + HALF + f0 + c * 8);
+                if (rope) {
+                    bf16x8 y1, y2;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float a = (float)x1[e], b = (float)x2[e];
+                        const float cc = cn[c * 8 + e], ss = sn[c * 8 + e];
+                        y1[e] = (bf16)(a * cc - b * ss);
+                        y2[e] = (bf16)(b * cc + a * ss);
+                    }
+                    x1 = y1;
+                    x2 = y2;
+                }
+                *(bf16x8*)(dst + f0 + c * 8) = x1;
+                *(bf16x8*)(dst + HALF + f0 + c * 8) = x2;
             }
-            x1 = y1;
-            x2 = y2;
+            if (wave == 0) {
+                *(bf16x8*)(dst + D) = extra[0];
+                *(bf16x8*)(dst + D + 8) = extra[1];
+            }
         }
-        bf16* dst = ws_k + ((int64_t)h * mp + prow) * D;
-        *(bf16x8*)(dst + c * 8) = x1;
-        *(bf16x8*)(dst + HALF + c * 8) = x2;
     }
-}
-
-// One thread per (kept token, kv head, chunk of 8 channels); tokens fastest so
-// the transposed 2-byte stores of a wave are contiguous.
-template <int D>
-__global__ __launch_bounds__(256) void attn_prep_v_kernel(
-    const bf16* __restrict__ v, int64_t kv_stride, const int* __restrict__ cu_kept, int n_seqs,
-    int64_t m_tot, int hkv, int64_t mp, bf16* __restrict__ ws_vt) {
-    constexpr int NCH = D / 8;
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t m = gid % m_tot;
-    const int64_t rest = gid / m_tot;
-    const int c = (int)(rest % NCH);
-    const int h = (int)(rest / NCH);
-    if (h >= hkv) return;
-    const int s = find_seq(cu_kept, n_seqs, m);
-    const int64_t prow = padded_seq_start(cu_kept[s], s) + (m - cu_kept[s]);
-    const bf16x8 x = *(const bf16x8*)(v + m * kv_stride + (int64_t)h * D + c * 8);
-    bf16* dst = ws_vt + ((int64_t)h * D + c * 8) * mp + prow;
+    // V^T through LDS: coalesced row loads, then per channel d the 64 lanes
+    // store 64 consecutive kept rows.
+    constexpr int VCH = 64 * (D / 8) / 256;
+    for (int h = 0; h < hkv; ++h) {
+        __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dst[(int64_t)e * mp] = x[e];
+        for (int i = 0; i < VCH; ++i) {
+            const int ch = tid + 256 * i;
+            const int r = ch / (D / 8), c8 = ch % (D / 8);
+            bf16x8 x = bf16x8{};
+            if (m0 + r < m_tot) x = *(const bf16x8*)(v + (m0 + r) * kv_stride + (int64_t)h * D + c8 * 8);
+            uint32_t* dst = (uint32_t*)(vs + r * VLD + c8 * 8);   // VLD rows are 4-byte aligned
+            const uint32_t* xs = (const uint32_t*)&x;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dst[u] = xs[u];
+        }
+        __syncthreads();
+        if (valid) {
+            bf16* dst = ws_vt + ((int64_t)h * D) * mp + prow;
+#pragma unroll 8
+            for (int dd = 0; dd < D / 4; ++dd) {
+                const int d = wave * (D / 4) + dd;
+                dst[(int64_t)d * mp] = vs[lane * VLD + d];
+            }
+        }
+    }
 }
 
 // ------------------------------------------------------------- main kernel --
 template <int D>
 struct AttnLds {
-    static constexpr int KLD = D + 8;      // K tile row (elements): 16-B reads conflict-free
+    static constexpr int KD = D + kExtra;
+    static constexpr int KLD = KD + 8;     // K' tile row (elements): 16-B reads conflict-free
     static constexpr int VLD = kBN + 4;    // V^T tile row: 8-B reads conflict-free
     static constexpr int K_ELEMS = kBN * KLD;
     static constexpr int V_ELEMS = D * VLD;
-    static constexpr int BUF_BYTES = (K_ELEMS + V_ELEMS) * 2 + 4 * kBN * 4;
+    static constexpr int BUF_BYTES = (K_ELEMS + V_ELEMS) * 2;
 };
 
 // HW q heads per workgroup (1, 2 or 4); each of the 4 waves owns 32 query tokens
@@ -144,34 +190,36 @@ template <int D, int HW>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const bf16* __restrict__ q, int64_t q_stride, const bf16* __restrict__ ws_k,
     const bf16* __restrict__ ws_vt, const float2* __restrict__ ws_cs, int rope,
-    const float* __restrict__ key_score, const float* __restrict__ gain, float qk_scale_log2,
-    const int* __restrict__ cu_kept, int n_seqs, int64_t m_tot, int64_t mp, int hq, int grp,
-    int n_qtiles, bf16* __restrict__ out, float* __restrict__ lse) {
+    const float* __restrict__ gain, float qk_scale_log2, const int* __restrict__ cu_kept, int n_seqs,
+    int64_t m_tot, int64_t mp, int hq, int grp, int n_qtiles, int n_hblk, bf16* __restrict__ out,
+    float* __restrict__ lse) {
     using L = AttnLds<D>;
     constexpr int WB = 4 / HW;
     constexpr int BMT = 32 * WB;
-    constexpr int KS = D / 16;      // MFMA k-steps over head_dim
+    constexpr int KS = D / 16;      // MFMA k-steps over head_dim (+1 for the bias columns)
+    constexpr int KD = L::KD;
     constexpr int DB = D / 32;      // 32-row blocks of O^T
-    constexpr int KCH = kBN * D / 8 / 256;   // 16-B chunks of the K tile per thread
-    constexpr int VCH = D * kBN / 8 / 256;   // ... of the V^T tile
+    constexpr int KCH = kBN * KD / 8 / 256 + ((kBN * KD / 8) % 256 ? 1 : 0);   // 16-B chunks of K' per thread
+    constexpr int VCH = D * kBN / 8 / 256;                                      // ... of V^T
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int il = lane & 31, half = lane >> 5;
 
-    // largest query tiles first (causal work grows with the tile index)
-    const int tile_rev = blockIdx.x / n_seqs;
-    const int s = blockIdx.x % n_seqs;
-    const int qt = n_qtiles - 1 - tile_rev;
+    // head-fastest block order; largest query tiles first
+    const int b = blockIdx.x;
+    const int hidx = b % n_hblk;
+    const int rest = b / n_hblk;
+    const int s = rest % n_seqs;
+    const int qt = n_qtiles - 1 - rest / n_seqs;
     const int cs0 = cu_kept[s];
     const int ms = cu_kept[s + 1] - cs0;
     const int q0 = qt * BMT;
     if (q0 >= ms) return;
 
     const int nsub = grp / HW;
-    const int hk = blockIdx.y / nsub;
-    const int hbase = hk * grp + (blockIdx.y % nsub) * HW;
-    const int h = hbase + wave / WB;
+    const int hk = hidx / nsub;
+    const int h = hk * grp + (hidx % nsub) * HW + wave / WB;
     const int qb = q0 + (wave % WB) * 32;    // first query (sequence-local) of this wave
     const int qi = qb + il;                  // this lane's query
     const bool qvalid = qi < ms;
@@ -179,20 +227,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const int kend = min(ms, q0 + BMT);
     const int n_kt = (kend + kBN - 1) / kBN;
 
-    // ---- Q fragment (B operand of S^T = K Q^T), rotary applied in fp32
-    bf16x8 qf[KS];
+    // ---- Q' fragment (B operand of S^T = K' Q'^T): rotated, scaled, + gain columns
+    bf16x8 qf[KS + 1];
     {
         const bf16* qrow = q + (int64_t)(cs0 + (qvalid ? qi : 0)) * q_stride + (int64_t)h * D;
+        float xf[KS][8];
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
-            qf[t] = qvalid ? *(const bf16x8*)(qrow + t * 16 + half * 8) : bf16x8{};
+            const bf16x8 raw = qvalid ? *(const bf16x8*)(qrow + t * 16 + half * 8) : bf16x8{};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xf[t][e] = (float)raw[e];
         }
         if (rope && qvalid) {
             const float2* csr = ws_cs + (int64_t)(cs0 + qi) * (D / 2);
 #pragma unroll
             for (int t = 0; t < KS / 2; ++t) {
                 const float4* c4 = (const float4*)(csr + t * 16 + half * 8);
-                bf16x8 y1, y2;
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
                     const float4 cc = c4[e2];
@@ -200,22 +250,30 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
                     for (int u = 0; u < 2; ++u) {
                         const int e = e2 * 2 + u;
                         const float cn = u ? cc.z : cc.x, sn = u ? cc.w : cc.y;
-                        const float a = (float)qf[t][e], b = (float)qf[t + KS / 2][e];
-                        y1[e] = (bf16)(a * cn - b * sn);
-                        y2[e] = (bf16)(b * cn + a * sn);
+                        const float a = xf[t][e], bb = xf[t + KS / 2][e];
+                        xf[t][e] = a * cn - bb * sn;
+                        xf[t + KS / 2][e] = bb * cn + a * sn;
                     }
                 }
-                qf[t] = y1;
-                qf[t + KS / 2] = y2;
             }
         }
+#pragma unroll
+        for (int t = 0; t < KS; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[t][e] = (bf16)(xf[t][e] * qk_scale_log2);
+        qf[KS] = bf16x8{};
+        if (half == 0) {
+            bf16 gh, glo;
+            split_bf16(gain[h] * kLog2e, &gh, &glo);
+            qf[KS][0] = gh;
+            qf[KS][1] = gh;
+            qf[KS][2] = glo;
+        }
     }
-    const float gl = gain[h] * kLog2e;
 
     // ---- tile staging
     u32x4 kreg[KCH], vreg[VCH];
-    float breg = 0.0f;
-    const bf16* kbase = ws_k + ((int64_t)hk * mp + prow0) * D;
+    const bf16* kbase = ws_k + ((int64_t)hk * mp + prow0) * KD;
     const bf16* vbase = ws_vt + (int64_t)hk * D * mp + prow0;
     auto load_tile = [&](int kt) {
         const int j0 = kt * kBN;
@@ -223,9 +281,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
             const int ch = tid + 256 * c;
-            const int r = ch / (D / 8), cc = ch % (D / 8);
-            kreg[c] = (!tail || j0 + r < kend) ? *(const u32x4*)(kbase + (int64_t)(j0 + r) * D + cc * 8)
-                                               : u32x4{0u, 0u, 0u, 0u};
+            const int r = ch / (KD / 8), cc = ch % (KD / 8);
+            const bool ok = ch < kBN * KD / 8 && (!tail || j0 + r < kend);
+            kreg[c] = ok ? *(const u32x4*)(kbase + (int64_t)(j0 + r) * KD + cc * 8) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int c = 0; c < VCH; ++c) {
@@ -242,38 +300,31 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
                 vreg[c] = *(u32x4*)&t8;
             }
         }
-        if (tid < HW * kBN) {
-            const int jj = tid % kBN, hh = tid / kBN;
-            breg = (j0 + jj < kend) ? gain[hbase + hh] * kLog2e * key_score[cs0 + j0 + jj] : 0.0f;
-        }
     };
     auto store_tile = [&](int buf) {
-        char* base = smem + buf * L::BUF_BYTES;
-        bf16* ks = (bf16*)base;
+        bf16* ks = (bf16*)(smem + buf * L::BUF_BYTES);
         bf16* vs = ks + L::K_ELEMS;
-        float* bs = (float*)(vs + L::V_ELEMS);
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
             const int ch = tid + 256 * c;
-            *(u32x4*)(ks + (ch / (D / 8)) * L::KLD + (ch % (D / 8)) * 8) = kreg[c];
+            if (ch < kBN * KD / 8) *(u32x4*)(ks + (ch / (KD / 8)) * L::KLD + (ch % (KD / 8)) * 8) = kreg[c];
         }
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
         for (int c = 0; c < VCH; ++c) {
             const int ch = tid + 256 * c;
             bf16* dst = vs + (ch / (kBN / 8)) * L::VLD + (ch % (kBN / 8)) * 8;
-            // VLD rows are 8-byte aligned: two 8-byte stores
-            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
             ((u32x2*)dst)[0] = u32x2{vreg[c][0], vreg[c][1]};
             ((u32x2*)dst)[1] = u32x2{vreg[c][2], vreg[c][3]};
         }
-        if (tid < HW * kBN) bs[tid] = breg;
     };
 
     f32x16 o[DB];
 #pragma unroll
-    for (int b = 0; b < DB; ++b) o[b] = f32x16{};
+    for (int bb = 0; bb < DB; ++bb) o[bb] = f32x16{};
     float m_run = -INFINITY, l_run = 0.0f;
-    (void)gl;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
     load_tile(0);
     store_tile(0);
@@ -283,73 +334,70 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         if (kt + 1 < n_kt) load_tile(kt + 1);
         const int j0 = kt * kBN;
         if (j0 <= qb + 31) {   // some key of this tile is visible to this wave
-            const char* base = smem + buf * L::BUF_BYTES;
-            const bf16* ks = (const bf16*)base;
+            const bf16* ks = (const bf16*)(smem + buf * L::BUF_BYTES);
             const bf16* vs = ks + L::K_ELEMS;
-            const float* bs = (const float*)(vs + L::V_ELEMS) + (wave / WB) * kBN;
 
             f32x16 st[2];
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
                 st[blk] = f32x16{};
 #pragma unroll
-                for (int t = 0; t < KS; ++t) {
+                for (int t = 0; t <= KS; ++t) {
                     const bf16x8 a = *(const bf16x8*)(ks + (blk * 32 + il) * L::KLD + t * 16 + half * 8);
                     st[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], st[blk], 0, 0, 0);
                 }
             }
-            // st[blk][r] <-> key j0 + blk*32 + (r/4)*8 + half*4 + r%4, query qi
-            const bool need_mask = j0 + kBN - 1 > qb;
-            float mx = -INFINITY;
+            // st[blk][r] <-> key j0 + blk*32 + (r/4)*8 + half*4 + r%4, query qi (log2 units)
+            if (j0 + kBN - 1 > qb) {
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
+                for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int jl = blk * 32 + g * 8 + half * 4;
-                    const float4 b4 = *(const float4*)(bs + jl);
-                    const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float t = fmaf(st[blk][g * 4 + e], qk_scale_log2, bb[e]);
-                        if (need_mask && j0 + jl + e > qi) t = -INFINITY;
-                        st[blk][g * 4 + e] = t;
-                        mx = fmaxf(mx, t);
-                    }
-                }
+                    for (int r = 0; r < 16; ++r)
+                        if (j0 + blk * 32 + (r >> 2) * 8 + half * 4 + (r & 3) > qi) st[blk][r] = -INFINITY;
             }
+            float mx = st[0][0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[0][r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[1][r]);
             {
                 auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
                 mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
             }
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            float lsum = 0.0f;
+            // refresh the running max only if this tile raises it by more than 8
+            if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f)) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int bb = 0; bb < DB; ++bb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[bb][r] *= alpha;
+            }
             bf16x8 pb[4];
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
+            for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(st[blk][r] - m_new);
-                    lsum += p;
-                    pb[blk * 2 + (r >> 3)][r & 7] = (bf16)p;
+                for (int r = 0; r < 16; ++r)
+                    pb[blk * 2 + (r >> 3)][r & 7] = (bf16)__builtin_amdgcn_exp2f(st[blk][r] - m_run);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const bf16x2 pr = {pb[u][e], pb[u][e + 1]};
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
                 }
-            }
-            l_run = l_run * alpha + lsum;
-#pragma unroll
-            for (int b = 0; b < DB; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
             // O^T += V^T P^T, 16 keys per step
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
 #pragma unroll
-                for (int b = 0; b < DB; ++b) {
-                    const bf16* vr = vs + (b * 32 + il) * L::VLD + u * 16 + half * 4;
+                for (int bb = 0; bb < DB; ++bb) {
+                    const bf16* vr = vs + (bb * 32 + il) * L::VLD + u * 16 + half * 4;
                     const bf16x4 lo = *(const bf16x4*)vr;
                     const bf16x4 hi = *(const bf16x4*)(vr + 8);
                     const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], o[b], 0, 0, 0);
+                    o[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], o[bb], 0, 0, 0);
                 }
             }
         }
@@ -367,13 +415,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const float inv = 1.0f / l_tot;
     bf16* orow = out + ((int64_t)(cs0 + qi) * hq + h) * D;
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
+    for (int bb = 0; bb < DB; ++bb) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             bf16x4 v4;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v4[e] = (bf16)(o[b][g * 4 + e] * inv);
-            *(bf16x4*)(orow + b * 32 + g * 8 + half * 4) = v4;
+            for (int e = 0; e < 4; ++e) v4[e] = (bf16)(o[bb][g * 4 + e] * inv);
+            *(bf16x4*)(orow + bb * 32 + g * 8 + half * 4) = v4;
         }
     }
     if (lse && half == 0) lse[(int64_t)h * m_tot + cs0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
@@ -384,7 +432,9 @@ int launch_fwd(const AttnArgs& a, hipStream_t st) {
     constexpr int BMT = 32 * (4 / HW);
     const int grp = a.hq / a.hkv;
     const int n_qtiles = (a.max_kept_seqlen + BMT - 1) / BMT;
-    const dim3 grid((unsigned)(n_qtiles * a.n_seqs), (unsigned)(a.hkv * (grp / HW)));
+    const int n_hblk = a.hkv * (grp / HW);
+    const int64_t nblk = (int64_t)n_qtiles * a.n_seqs * n_hblk;
+    if (nblk > 0x7fffffff) return TG_ERR_UNSUPPORTED;
     const size_t shm = 2 * (size_t)AttnLds<D>::BUF_BYTES;
     static bool attr_set = false;   // idempotent; racing first calls set the same value
     if (!attr_set) {
@@ -393,27 +443,20 @@ int launch_fwd(const AttnArgs& a, hipStream_t st) {
             return TG_ERR_HIP;
         attr_set = true;
     }
-    hipLaunchKernelGGL((attn_fwd_kernel<D, HW>), grid, dim3(256), shm, st, a.q, a.q_stride, a.ws_k,
-                       a.ws_vt, a.ws_cs, (int)a.rope, a.key_score, a.gain, a.qk_scale_log2,
-                       a.cu_kept, a.n_seqs, a.m_tot, a.mp, a.hq, grp, n_qtiles, a.out, a.lse);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, HW>), dim3((unsigned)nblk), dim3(256), shm, st, a.q,
+                       a.q_stride, a.ws_k, a.ws_vt, a.ws_cs, (int)a.rope, a.gain, a.qk_scale_log2,
+                       a.cu_kept, a.n_seqs, a.m_tot, a.mp, a.hq, grp, n_qtiles, n_hblk, a.out, a.lse);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 
 template <int D>
 int launch_all(const AttnArgs& a, hipStream_t st) {
-    {
-        const int64_t threads = a.m_tot * (D / 16);
-        hipLaunchKernelGGL(attn_prep_k_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                           st, a.k, a.kv_stride, a.pos, a.cu_kept, a.n_seqs, a.m_tot, a.hkv, a.mp,
-                           a.rope_log2_base, (int)a.rope, a.ws_k, a.ws_cs);
-        if (hipGetLastError() != hipSuccess) return TG_ERR_HIP;
-    }
-    {
-        const int64_t threads = a.m_tot * a.hkv * (D / 8);
-        hipLaunchKernelGGL(attn_prep_v_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                           st, a.v, a.kv_stride, a.cu_kept, a.n_seqs, a.m_tot, a.hkv, a.mp, a.ws_vt);
-        if (hipGetLastError() != hipSuccess) return TG_ERR_HIP;
-    }
+    RopeFreqs fr;
+    for (int f = 0; f < 64; ++f) fr.inv_freq[f] = f < D / 2 ? exp2(-(2.0 * f / D) * a.rope_log2_base) : 0.0;
+    hipLaunchKernelGGL(attn_prep_kernel<D>, dim3((unsigned)((a.m_tot + 63) / 64)), dim3(256), 0, st, a.k,
+                       a.v, a.kv_stride, a.key_score, a.pos, a.cu_kept, a.n_seqs, a.m_tot, a.hkv, a.mp, fr,
+                       (int)a.rope, a.ws_k, a.ws_vt, a.ws_cs);
+    if (hipGetLastError() != hipSuccess) return TG_ERR_HIP;
     const int grp = a.hq / a.hkv;
     switch (grp) {
         case 1: return launch_fwd<D, 1>(a, st);

@@ -25,9 +25,11 @@ int launch_gate_bf16(const bf16* x, int64_t n, int d_model, int64_t x_stride, co
 int launch_gate_f32(const float* x, int64_t n, int d_model, int64_t x_stride, const float* w1,
                     const float* b1, const float* w2, float b2, int d_hid, float* scores,
                     hipStream_t st);
-int launch_topk(const float* scores, int n_seqs, const int* cu_seqlens, const int* doc_begin,
-                const int* doc_end, const int* k_doc, const int* cu_kept, int* kept_idx,
-                hipStream_t st);
+size_t topk_workspace_bytes(int n_seqs, int64_t n_tokens, int max_seqlen);
+int topk_max_seqlen();
+int launch_topk(const float* scores, int n_seqs, int64_t n_tokens, int max_seqlen,
+                const int* cu_seqlens, const int* doc_begin, const int* doc_end, const int* k_doc,
+                const int* cu_kept, int* kept_idx, void* ws, hipStream_t st);
 int launch_gather(const void* x, int esize, int d_model, int64_t x_stride, const float* scores,
                   const int* kept_idx, int64_t m_tot, int n_seqs, const int* cu_seqlens,
                   const int* cu_kept, void* x_kept, float* s_kept, int* pos_kept, hipStream_t st);

@@ -101,6 +101,13 @@ def test_topk_validation(lib):
     assert t(cu=None) == 1
     assert t(out=None) == 1
     assert t(s=None) == 1
+    assert t(mx=11) == 1                         # longer than the whole batch
+    assert t(n=2 ** 23, mx=2 ** 23) == 2          # beyond the 4 Mi grid limit
+    need = L.tg_topk_workspace_bytes(1, 10, 10)
+    assert need > 0
+    assert t(ws=None, wsb=need) == 3
+    assert t(ws=FAKE, wsb=need - 1) == 3
+    assert t(ws=ctypes.c_void_p(0x1010), wsb=need) == 3   # not 256-byte aligned
     assert t(ns=0) == 0
 
 
