@@ -27,9 +27,14 @@
 //     scalars combined across the two 32-lane halves with one permlane32 swap;
 //     P^T feeds O^T = V^T.P^T straight from the S^T accumulators (8 consecutive
 //     accumulators are one 16-key MFMA step, V^T read in the matching order).
-//     The running max is refreshed only when a tile raises it by more than 8
-//     (p <= 2^8 otherwise; the result is exact either way), so the O rescale is
-//     rare; row sums use v_dot2 on the bf16 P that the P.V MFMA consumes.
+//     A running offset m (set from the first tile's exact row max, kept
+//     bf16-exact) rides in Q' column 3 against 1.0 in K' column 3, so the MFMA
+//     emits u = t - m and p = exp2(u) needs no max or subtraction.  Row sums
+//     use v_dot2 on the bf16 P that the P.V MFMA consumes; a block whose sum
+//     exceeds 2^62 (some p very large) takes a rare path that raises m to the
+//     block max and rescales O and l (the result is exact either way).  Each
+//     64-key tile is two 32-key blocks, so block 0's exponentials can overlap
+//     block 1's QK MFMAs and block 1's can overlap block 0's P.V MFMAs.
 //     All q heads of a KV group that fit in the workgroup share each K/V tile.
 //     Causality uses the kept order (positions increase within a sequence, so
 //     pos_j <= pos_i  <=>  j <= i).  Blocks are ordered head-fastest so that,
@@ -41,8 +46,10 @@
 
 namespace tg {
 
+// Rows of the padded K'/V^T layout: sequence s starts at padded_seq_start();
+// the last sequence's final tile may reach 63 rows past its end.
 int64_t attn_padded_rows(int n_seqs, int64_t m_tot) {
-    return ((m_tot + 8 * (int64_t)n_seqs + 8) + 63) & ~(int64_t)63;
+    return (((m_tot + 8 * (int64_t)n_seqs + 8) + 63) & ~(int64_t)63) + 64;
 }
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -72,6 +79,13 @@ __device__ __forceinline__ void split_bf16(float x, bf16* hi, bf16* lo) {
     const bf16 h = (bf16)x;
     *hi = h;
     *lo = (bf16)(x - (float)h);
+}
+
+// Smallest bf16-representable value >= x (x finite).
+__device__ __forceinline__ float bf16_ceil(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const float t = __uint_as_float(u & 0xffff0000u);   // truncation toward zero
+    return t >= x ? t : __uint_as_float((u & 0xffff0000u) + 0x10000u);
 }
 
 // ---------------------------------------------------------------- pre-pass --
@@ -116,6 +130,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
             extra[0][0] = sh;
             extra[0][1] = sl;
             extra[0][2] = sh;
+            extra[0][3] = (bf16)1.0f;
         }
         for (int h = 0; h < hkv; ++h) {
             const bf16* src = k + m * kv_stride + (int64_t)h * D;
@@ -171,21 +186,61 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
             }
         }
     }
+    // Zero the padding rows between sequences (and after the last one), so that
+    // key tiles can be loaded whole: rows past a sequence's end are then either
+    // zeros or other sequences' finite data, and their probabilities are 0.
+    // Grid-stride over (padded row, kv head); a row is padding iff it lies past
+    // the end of the sequence whose padded start precedes it.
+    const int64_t nthreads = (int64_t)gridDim.x * 256;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + tid; idx < mp * hkv; idx += nthreads) {
+        const int64_t r = idx / hkv;
+        const int h = (int)(idx % hkv);
+        int lo = 0, hi = n_seqs;   // last sequence whose padded start is <= r (or 0)
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (padded_seq_start(cu_kept[mid], mid) <= r) lo = mid; else hi = mid;
+        }
+        const int64_t p0 = padded_seq_start(cu_kept[lo], lo);
+        if (r >= p0 && r < p0 + (cu_kept[lo + 1] - cu_kept[lo])) continue;   // a token row
+        bf16* kr = ws_k + ((int64_t)h * mp + r) * KD;
+#pragma unroll
+        for (int c = 0; c < KD; c += 8) *(bf16x8*)(kr + c) = bf16x8{};
+        bf16* vr = ws_vt + (int64_t)h * D * mp + r;
+        for (int d = 0; d < D; ++d) vr[(int64_t)d * mp] = (bf16)0.0f;
+    }
 }
 
 // ------------------------------------------------------------- main kernel --
 template <int D>
 struct AttnLds {
+    // K' tiles arrive by global_load_lds_dwordx4: every load instruction copies
+    // 64 lanes x 16 B into 1 KiB of consecutive LDS, so rows are padded by one
+    // 16-B chunk (pad slots hold a duplicate, never read) to keep the MFMA
+    // operand reads free of bank conflicts.  V^T tiles go through registers:
+    // their conflict-free row pitch (136 B) is not a multiple of 16 B.
     static constexpr int KD = D + kExtra;
-    static constexpr int KLD = KD + 8;     // K' tile row (elements): 16-B reads conflict-free
-    static constexpr int VLD = kBN + 4;    // V^T tile row: 8-B reads conflict-free
-    static constexpr int K_ELEMS = kBN * KLD;
-    static constexpr int V_ELEMS = D * VLD;
-    static constexpr int BUF_BYTES = (K_ELEMS + V_ELEMS) * 2;
+    static constexpr int KCHUNK = KD / 8;          // 16-B chunks per K' row (18 / 10)
+    static constexpr int KROW = KCHUNK + 1;        // padded row, in chunks
+    static constexpr int KLD = KROW * 8;           // ... in elements (152 / 88)
+    static constexpr int VLD = kBN + 4;            // V^T row (elements): 136 B, conflict-free 8-B reads
+    static constexpr int VCH = D * kBN / 8 / 256;  // 16-B chunks of a V^T tile per thread (staged in registers)
+    static constexpr int K_INSTR = kBN * KROW / 64;    // load instructions per K' tile (19 / 11)
+    static_assert(kBN * KROW % 64 == 0, "K' tiles must be whole load instructions");
+    static constexpr int KPW = (K_INSTR + 3) / 4;      // per wave
+    static constexpr int K_BYTES = kBN * KLD * 2;
+    static constexpr int V_BYTES = D * VLD * 2;
+    static constexpr int SMEM = 2 * K_BYTES + 2 * V_BYTES;   // two K' and two V^T buffers
 };
 
 // HW q heads per workgroup (1, 2 or 4); each of the 4 waves owns 32 query tokens
 // of one head; WB = 4 / HW waves per head; BMT = 32 * WB tokens per workgroup.
+//
+// Software pipeline per wave, iteration j (K' runs one tile ahead of V^T):
+//   R1  QK MFMAs of tile j+1, interleaved with the exponentials of tile j;
+//       (rare) offset refresh if tile j produced a huge probability;
+//   R2  P.V MFMAs of tile j;
+//       mask tile j+1 if it reaches this wave's diagonal;
+//   K'(j+2) goes straight to LDS and V^T(j+1) through registers meanwhile.
 template <int D, int HW>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const bf16* __restrict__ q, int64_t q_stride, const bf16* __restrict__ ws_k,
@@ -196,11 +251,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     using L = AttnLds<D>;
     constexpr int WB = 4 / HW;
     constexpr int BMT = 32 * WB;
-    constexpr int KS = D / 16;      // MFMA k-steps over head_dim (+1 for the bias columns)
+    constexpr int KS = D / 16;      // MFMA k-steps over head_dim (+1 for the extra columns)
     constexpr int KD = L::KD;
     constexpr int DB = D / 32;      // 32-row blocks of O^T
-    constexpr int KCH = kBN * KD / 8 / 256 + ((kBN * KD / 8) % 256 ? 1 : 0);   // 16-B chunks of K' per thread
-    constexpr int VCH = D * kBN / 8 / 256;                                      // ... of V^T
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -227,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const int kend = min(ms, q0 + BMT);
     const int n_kt = (kend + kBN - 1) / kBN;
 
-    // ---- Q' fragment (B operand of S^T = K' Q'^T): rotated, scaled, + gain columns
+    // ---- Q' fragment (B operand of S^T = K' Q'^T): rotated, scaled, + extra columns
     bf16x8 qf[KS + 1];
     {
         const bf16* qrow = q + (int64_t)(cs0 + (qvalid ? qi : 0)) * q_stride + (int64_t)h * D;
@@ -271,47 +324,41 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         }
     }
 
-    // ---- tile staging
-    u32x4 kreg[KCH], vreg[VCH];
+    // ---- LDS-direct tile loads.  Load instruction g of a K' (V^T) tile is
+    // issued by wave g % 4 and copies one 16-B chunk per lane; the per-lane
+    // source offsets are fixed for the whole kernel.
+    int koff[L::KPW];
+#pragma unroll
+    for (int i = 0; i < L::KPW; ++i) {
+        const int slot = (wave + 4 * i) * 64 + lane;
+        const int r = slot / L::KROW, c = slot % L::KROW;
+        koff[i] = r * KD + (c < L::KCHUNK ? c : 0) * 8;
+    }
     const bf16* kbase = ws_k + ((int64_t)hk * mp + prow0) * KD;
     const bf16* vbase = ws_vt + (int64_t)hk * D * mp + prow0;
-    auto load_tile = [&](int kt) {
-        const int j0 = kt * kBN;
-        const bool tail = j0 + kBN > kend;
+    char* const kbufs = smem;
+    char* const vbufs = smem + 2 * L::K_BYTES;
+    auto load_k = [&](int t, int buf) {
+        const bf16* src = kbase + (int64_t)t * kBN * KD;
+        char* dst = kbufs + buf * L::K_BYTES;
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            const int ch = tid + 256 * c;
-            const int r = ch / (KD / 8), cc = ch % (KD / 8);
-            const bool ok = ch < kBN * KD / 8 && (!tail || j0 + r < kend);
-            kreg[c] = ok ? *(const u32x4*)(kbase + (int64_t)(j0 + r) * KD + cc * 8) : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int i = 0; i < L::KPW; ++i)
+            if (wave + 4 * i < L::K_INSTR) lds_load16(src + koff[i], dst + (wave + 4 * i) * 1024);
+    };
+    u32x4 vreg[L::VCH];
+    auto load_v = [&](int t) {
 #pragma unroll
-        for (int c = 0; c < VCH; ++c) {
+        for (int c = 0; c < L::VCH; ++c) {
             const int ch = tid + 256 * c;
             const int dr = ch / (kBN / 8), cc = ch % (kBN / 8);
-            const int j = j0 + cc * 8;
-            if (!tail || j + 8 <= kend) {
-                vreg[c] = *(const u32x4*)(vbase + (int64_t)dr * mp + j);
-            } else {
-                const bf16* p = vbase + (int64_t)dr * mp + j;
-                bf16x8 t8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) t8[e] = (j + e < kend) ? p[e] : (bf16)0.0f;
-                vreg[c] = *(u32x4*)&t8;
-            }
+            vreg[c] = *(const u32x4*)(vbase + (int64_t)dr * mp + t * kBN + cc * 8);
         }
     };
-    auto store_tile = [&](int buf) {
-        bf16* ks = (bf16*)(smem + buf * L::BUF_BYTES);
-        bf16* vs = ks + L::K_ELEMS;
-#pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            const int ch = tid + 256 * c;
-            if (ch < kBN * KD / 8) *(u32x4*)(ks + (ch / (KD / 8)) * L::KLD + (ch % (KD / 8)) * 8) = kreg[c];
-        }
+    auto store_v = [&](int buf) {
+        bf16* vs = (bf16*)(vbufs + buf * L::V_BYTES);
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-        for (int c = 0; c < VCH; ++c) {
+        for (int c = 0; c < L::VCH; ++c) {
             const int ch = tid + 256 * c;
             bf16* dst = vs + (ch / (kBN / 8)) * L::VLD + (ch % (kBN / 8)) * 8;
             ((u32x2*)dst)[0] = u32x2{vreg[c][0], vreg[c][1]};
@@ -322,86 +369,159 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     f32x16 o[DB];
 #pragma unroll
     for (int bb = 0; bb < DB; ++bb) o[bb] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.0f;
+    // Running offset m (log2 units), bf16-exact because Q' carries -m in its
+    // extra column 3 against a 1.0 in K', so the MFMA emits u = t - m directly.
+    float m_run = 0.0f, l_run = 0.0f;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+    // A tile whose row sum exceeds this had some p > ~2^57: refresh the offset.
+    constexpr float kSumLimit = 0x1p62f;
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < n_kt) load_tile(kt + 1);
-        const int j0 = kt * kBN;
-        if (j0 <= qb + 31) {   // some key of this tile is visible to this wave
-            const bf16* ks = (const bf16*)(smem + buf * L::BUF_BYTES);
-            const bf16* vs = ks + L::K_ELEMS;
-
-            f32x16 st[2];
+    auto set_offset = [&](float m) {
+        m_run = m;
+        if (half == 0) qf[KS][3] = (bf16)(-m);
+    };
+    auto qk = [&](const bf16* ks, int blk, f32x16& acc) {
+        acc = f32x16{};
+        const bf16* kr = ks + (blk * 32 + il) * L::KLD + half * 8;
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                st[blk] = f32x16{};
+        for (int t = 0; t <= KS; ++t) {
+            const bf16x8 ka = *(const bf16x8*)(kr + t * 16);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[t], acc, 0, 0, 0);
+        }
+    };
+    // acc[r] <-> key j0 + blk*32 + (r/4)*8 + half*4 + r%4, query qi
+    auto mask = [&](f32x16& acc, int j0, int blk) {
 #pragma unroll
-                for (int t = 0; t <= KS; ++t) {
-                    const bf16x8 a = *(const bf16x8*)(ks + (blk * 32 + il) * L::KLD + t * 16 + half * 8);
-                    st[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], st[blk], 0, 0, 0);
-                }
+        for (int r = 0; r < 16; ++r)
+            if (j0 + blk * 32 + (r >> 2) * 8 + half * 4 + (r & 3) > qi) acc[r] = -INFINITY;
+    };
+    auto expo = [&](const f32x16& acc, bf16x8* pb) {
+        float l = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(acc[r]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const bf16x2 pr = {pb[u][e], pb[u][e + 1]};
+                l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
             }
-            // st[blk][r] <-> key j0 + blk*32 + (r/4)*8 + half*4 + r%4, query qi (log2 units)
-            if (j0 + kBN - 1 > qb) {
+        return l;
+    };
+    auto pv = [&](const bf16* vs, int blk, const bf16x8* pb) {
 #pragma unroll
-                for (int blk = 0; blk < 2; ++blk)
+        for (int uu = 0; uu < 2; ++uu) {
+            const int u = blk * 2 + uu;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (j0 + blk * 32 + (r >> 2) * 8 + half * 4 + (r & 3) > qi) st[blk][r] = -INFINITY;
-            }
-            float mx = st[0][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[0][r]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[1][r]);
-            {
-                auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-                mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            }
-            // refresh the running max only if this tile raises it by more than 8
-            if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f)) {
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                m_run = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int bb = 0; bb < DB; ++bb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[bb][r] *= alpha;
-            }
-            bf16x8 pb[4];
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    pb[blk * 2 + (r >> 3)][r & 7] = (bf16)__builtin_amdgcn_exp2f(st[blk][r] - m_run);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const bf16x2 pr = {pb[u][e], pb[u][e + 1]};
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
-                }
-            // O^T += V^T P^T, 16 keys per step
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-#pragma unroll
-                for (int bb = 0; bb < DB; ++bb) {
-                    const bf16* vr = vs + (bb * 32 + il) * L::VLD + u * 16 + half * 4;
-                    const bf16x4 lo = *(const bf16x4*)vr;
-                    const bf16x4 hi = *(const bf16x4*)(vr + 8);
-                    const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    o[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], o[bb], 0, 0, 0);
-                }
+            for (int bb = 0; bb < DB; ++bb) {
+                const bf16* vr = vs + (bb * 32 + il) * L::VLD + u * 16 + half * 4;
+                const bf16x4 lo = *(const bf16x4*)vr;
+                const bf16x4 hi = *(const bf16x4*)(vr + 8);
+                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                o[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[uu], o[bb], 0, 0, 0);
             }
         }
-        if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    };
+    auto row_max = [&](float mx) {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    };
+    auto tile_max = [&](const f32x16& a0, const f32x16& a1) {
+        float mx = a0[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, a0[r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, a1[r]);
+        return row_max(mx);
+    };
+
+    // ---- prologue: K'(0), K'(1), V^T(0); tile 0's logits set the offset
+    load_k(0, 0);
+    if (n_kt > 1) load_k(1, 1);
+    load_v(0);
+    store_v(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 s0, s1;
+    qk((const bf16*)kbufs, 0, s0);
+    qk((const bf16*)kbufs, 1, s1);
+    if (kBN - 1 > qb) {
+        mask(s0, 0, 0);
+        mask(s1, 0, 1);
+    }
+    {
+        const float m0 = bf16_ceil(tile_max(s0, s1));   // key 0 is always visible
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s0[r] -= m0;
+            s1[r] -= m0;
+        }
+        set_offset(m0);
+    }
+    __syncthreads();   // K' buffer 0 is reloaded in iteration 0
+
+    for (int j = 0; j < n_kt; ++j) {
+        if (j + 2 < n_kt) load_k(j + 2, j & 1);
+        if (j + 1 < n_kt) load_v(j + 1);
+        const bf16* ksn = (const bf16*)(kbufs + ((j + 1) & 1) * L::K_BYTES);   // K'(j+1); stale past the end
+        const bf16* vs = (const bf16*)(vbufs + (j & 1) * L::V_BYTES);
+
+        // R1: QK(j+1) || exponentials of tile j
+        f32x16 n0, n1;
+        bf16x8 pb0[2], pb1[2];
+        qk(ksn, 0, n0);
+        qk(ksn, 1, n1);
+        float l0 = expo(s0, pb0);
+        float l1 = expo(s1, pb1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * (KS + 1); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+        if (__builtin_amdgcn_ballot_w64(!(l0 + l1 <= kSumLimit))) {
+            // rare: raise the offset to tile j's row max, rescale, shift pending logits
+            const float target = bf16_ceil(m_run + fmaxf(tile_max(s0, s1), 0.0f));
+            const float delta = target - m_run;
+            const float alpha = __builtin_amdgcn_exp2f(-delta);
+            l_run *= alpha;
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[bb][r] *= alpha;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s0[r] -= delta;
+                s1[r] -= delta;
+                n0[r] -= delta;
+                n1[r] -= delta;
+            }
+            set_offset(target);
+            l0 = expo(s0, pb0);
+            l1 = expo(s1, pb1);
+        }
+        l_run += l0 + l1;
+
+        // R2: P.V of tile j
+        pv(vs, 0, pb0);
+        pv(vs, 1, pb1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+        for (int i = 0; i < 4 * DB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+        s0 = n0;
+        s1 = n1;
+        if (j + 1 < n_kt && (j + 1) * kBN + kBN - 1 > qb) {
+            mask(s0, (j + 1) * kBN, 0);
+            mask(s1, (j + 1) * kBN, 1);
+        }
+        if (j + 1 < n_kt) store_v((j + 1) & 1);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's K' loads have landed in LDS
         __syncthreads();
     }
 
@@ -434,8 +554,8 @@ int launch_fwd(const AttnArgs& a, hipStream_t st) {
     const int n_qtiles = (a.max_kept_seqlen + BMT - 1) / BMT;
     const int n_hblk = a.hkv * (grp / HW);
     const int64_t nblk = (int64_t)n_qtiles * a.n_seqs * n_hblk;
-    if (nblk > 0x7fffffff) return TG_ERR_UNSUPPORTED;
-    const size_t shm = 2 * (size_t)AttnLds<D>::BUF_BYTES;
+    if (nblk > 0x7fffffff || (int64_t)D * a.mp >= ((int64_t)1 << 31)) return TG_ERR_UNSUPPORTED;
+    const size_t shm = (size_t)AttnLds<D>::SMEM;
     static bool attr_set = false;   // idempotent; racing first calls set the same value
     if (!attr_set) {
         if (hipFuncSetAttribute((const void*)attn_fwd_kernel<D, HW>,

@@ -63,6 +63,13 @@ size_t attn_workspace_layout(int n_seqs, int64_t m_tot, int hkv, int d, size_t* 
                              size_t* off_vt, size_t* off_cs);
 int launch_attn(const AttnArgs& a, hipStream_t st);
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l writes LDS bytes [ldst + 16 l, ldst + 16 l + 16); ldst must be the
+// same for the whole wave.
+__device__ __forceinline__ void lds_load16(const void* gsrc, void* ldst) {
+    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)ldst, 16, 0, 0);
+}
+
 // Upper-bound search: the sequence s with cu[s] <= m < cu[s+1] (cu non-decreasing,
 // cu[0] <= m < cu[n]).
 __device__ __forceinline__ int find_seq(const int* __restrict__ cu, int n, int64_t m) {

@@ -149,3 +149,13 @@ def test_attn_validation(lib):
     assert a(wsb=need - 1) == 3        # workspace too small
     assert a(ws=ctypes.c_void_p(0x1010)) == 3   # workspace not 256-B aligned
     assert a(m=0) == 0
+
+
+def test_library_has_no_undefined_internal_symbols(lib):
+    """Every kernel stub must be defined: an undefined tg:: symbol only shows
+    up when the library is loaded for real."""
+    import subprocess
+    from learned_token_pruning_05_amd import _lib
+    out = subprocess.run(["nm", "-D", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    undefined = [l for l in out.splitlines() if " U " in l and "_ZN2tg" in l]
+    assert not undefined, undefined[:3]

@@ -312,7 +312,9 @@ def test_attention_bias_shift_invariance_gpu():
     c2 = dict(c, sk=(c["sk"] + np.float32(0.75)).astype(np.float32))
     o2, l2 = _run_attn(c2, 1e6)
     assert np.abs(o1 - o2).max() <= 1e-2
-    np.testing.assert_allclose(l2 - l1, (c["gain"] * 0.75)[:, None] * np.ones_like(l1), atol=2e-3)
+    # LSE comes from the row sum of the bf16-rounded probabilities (the ones the
+    # P.V product uses): <= ln(1 + 2^-9) ~ 0.002 per run, so 0.004 for a difference.
+    np.testing.assert_allclose(l2 - l1, (c["gain"] * 0.75)[:, None] * np.ones_like(l1), atol=4e-3)
 
 
 # --------------------------------------------------------------- end to end ----
