@@ -436,6 +436,58 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         return row_max(mx);
     };
 
+    // QK of one tile into two 32-key blocks; block 0's K' fragments are all
+    // read before its MFMAs, block 1's are read while block 0 multiplies.
+    auto qk_tile = [&](const bf16* ks, f32x16& a0, f32x16& a1) {
+        const bf16* kr0 = ks + il * L::KLD + half * 8;
+        const bf16* kr1 = kr0 + 32 * L::KLD;
+        bf16x8 f0[KS + 1], f1[KS + 1];
+#pragma unroll
+        for (int t = 0; t <= KS; ++t) f0[t] = *(const bf16x8*)(kr0 + t * 16);
+#pragma unroll
+        for (int t = 0; t <= KS; ++t) f1[t] = *(const bf16x8*)(kr1 + t * 16);
+        a0 = f32x16{};
+        a1 = f32x16{};
+#pragma unroll
+        for (int t = 0; t <= KS; ++t) a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[t], qf[t], a0, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t <= KS; ++t) a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[t], qf[t], a1, 0, 0, 0);
+        // order: 9 reads, then (MFMA, read) x 9, then 9 MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, KS + 1, 2);
+#pragma unroll
+        for (int t = 0; t <= KS; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, KS + 1, 2);
+    };
+    auto mask_tile = [&](f32x16& a0, f32x16& a1, int j0) {
+        mask(a0, j0, 0);
+        mask(a1, j0, 1);
+    };
+    // Rare: tile t's probabilities were huge.  Raise the offset to the tile's
+    // row max, rescale what is accumulated, recompute the tile's logits.
+    auto refresh = [&](const bf16* ks, int t, bf16x8* pb0, bf16x8* pb1, float& lt) {
+        f32x16 a0, a1;
+        qk_tile(ks, a0, a1);
+        if (t * kBN + kBN - 1 > qb) mask_tile(a0, a1, t * kBN);
+        const float target = bf16_ceil(m_run + fmaxf(tile_max(a0, a1), 0.0f));
+        const float delta = target - m_run;
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        l_run *= alpha;
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[bb][r] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            a0[r] -= delta;
+            a1[r] -= delta;
+        }
+        set_offset(target);
+        lt = expo(a0, pb0) + expo(a1, pb1);
+    };
+
     // ---- prologue: K'(0), K'(1), V^T(0); tile 0's logits set the offset
     load_k(0, 0);
     if (n_kt > 1) load_k(1, 1);
@@ -443,14 +495,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     store_v(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    f32x16 s0, s1;
-    qk((const bf16*)kbufs, 0, s0);
-    qk((const bf16*)kbufs, 1, s1);
-    if (kBN - 1 > qb) {
-        mask(s0, 0, 0);
-        mask(s1, 0, 1);
-    }
+    bf16x8 pb0[2], pb1[2];   // bf16 probabilities of the tile whose P.V is next
     {
+        f32x16 s0, s1;
+        qk_tile((const bf16*)kbufs, s0, s1);
+        if (kBN - 1 > qb) mask_tile(s0, s1, 0);
         const float m0 = bf16_ceil(tile_max(s0, s1));   // key 0 is always visible
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -458,6 +507,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
             s1[r] -= m0;
         }
         set_offset(m0);
+        l_run = expo(s0, pb0) + expo(s1, pb1);
     }
     __syncthreads();   // K' buffer 0 is reloaded in iteration 0
 
@@ -466,61 +516,35 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         if (j + 1 < n_kt) load_v(j + 1);
         const bf16* ksn = (const bf16*)(kbufs + ((j + 1) & 1) * L::K_BYTES);   // K'(j+1); stale past the end
         const bf16* vs = (const bf16*)(vbufs + (j & 1) * L::V_BYTES);
+        const bool more = j + 1 < n_kt;
 
-        // R1: QK(j+1) || exponentials of tile j
+        // R1: QK of tile j+1
         f32x16 n0, n1;
-        bf16x8 pb0[2], pb1[2];
-        qk(ksn, 0, n0);
-        qk(ksn, 1, n1);
-        float l0 = expo(s0, pb0);
-        float l1 = expo(s1, pb1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * (KS + 1); ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        }
-        if (__builtin_amdgcn_ballot_w64(!(l0 + l1 <= kSumLimit))) {
-            // rare: raise the offset to tile j's row max, rescale, shift pending logits
-            const float target = bf16_ceil(m_run + fmaxf(tile_max(s0, s1), 0.0f));
-            const float delta = target - m_run;
-            const float alpha = __builtin_amdgcn_exp2f(-delta);
-            l_run *= alpha;
-#pragma unroll
-            for (int bb = 0; bb < DB; ++bb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[bb][r] *= alpha;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s0[r] -= delta;
-                s1[r] -= delta;
-                n0[r] -= delta;
-                n1[r] -= delta;
-            }
-            set_offset(target);
-            l0 = expo(s0, pb0);
-            l1 = expo(s1, pb1);
-        }
-        l_run += l0 + l1;
+        qk_tile(ksn, n0, n1);
+        if (more && (j + 1) * kBN + kBN - 1 > qb) mask_tile(n0, n1, (j + 1) * kBN);
 
-        // R2: P.V of tile j
+        // R2: P.V of tile j || exponentials of tile j+1
+        bf16x8 nb0[2], nb1[2];
         pv(vs, 0, pb0);
         pv(vs, 1, pb1);
+        float ln = expo(n0, nb0) + expo(n1, nb1);
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
         for (int i = 0; i < 4 * DB; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            __builtin_amdgcn_sched_group_barrier(0x400, 2, 1);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
         }
-        s0 = n0;
-        s1 = n1;
-        if (j + 1 < n_kt && (j + 1) * kBN + kBN - 1 > qb) {
-            mask(s0, (j + 1) * kBN, 0);
-            mask(s1, (j + 1) * kBN, 1);
+        // unconditional uses keep the exponentials in R2 (past the end they are unused)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            pb0[u] = nb0[u];
+            pb1[u] = nb1[u];
         }
-        if (j + 1 < n_kt) store_v((j + 1) & 1);
+        if (more && __builtin_amdgcn_ballot_w64(!(ln <= kSumLimit))) refresh(ksn, j + 1, pb0, pb1, ln);
+        l_run = more ? l_run + ln : l_run;
+        if (more) store_v((j + 1) & 1);
         __builtin_amdgcn_s_waitcnt(0);   // this wave's K' loads have landed in LDS
         __syncthreads();
     }
