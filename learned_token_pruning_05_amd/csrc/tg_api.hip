@@ -53,8 +53,9 @@ int tg_gate_score(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d_mo
     if (!x || !w1 || !w2 || !scores || !aligned16(x) || !aligned16(w1)) return TG_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;
     if (x_dtype == TG_BF16) {
-        if (d_model % 32 != 0) return TG_ERR_UNSUPPORTED;
+        if (d_model % 64 != 0) return TG_ERR_UNSUPPORTED;
         if (d_hid != 64 && d_hid != 128 && d_hid != 192 && d_hid != 256) return TG_ERR_UNSUPPORTED;
+        if (x_row_stride >= (1 << 23)) return TG_ERR_UNSUPPORTED;   // per-workgroup offsets are 32-bit
         return launch_gate_bf16((const bf16*)x, n_tokens, d_model, x_row_stride, (const bf16*)w1, b1,
                                 w2, b2, d_hid, scores, st);
     }

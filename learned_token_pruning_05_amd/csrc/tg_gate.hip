@@ -4,11 +4,14 @@
 // token from its post-attention residual at the gate layer.  Computed here as
 //     s_t = w2 . SiLU(W1 x_t + b1) + b2.
 //
-// bf16 path: one workgroup owns 128 tokens and the whole hidden layer, so the
+// bf16 path: one workgroup owns 256 tokens and the whole hidden layer, so the
 // hidden activations never leave registers: X.W1^T on 32x32x16 bf16 MFMA with
 // fp32 accumulation, then b1 + SiLU + w2-dot in fp32 in the epilogue, reduced
-// to one score per token.  Both operands are K-contiguous and staged through
-// double-buffered LDS in 32-column slabs.
+// to one score per token.  Both operands are K-contiguous; 64-column slabs (a
+// whole 128-B line of every row) go straight from memory into double-buffered
+// LDS.  With
+// enough tokens, 256 tokens per workgroup keeps the W1 re-reads (all of W1 per
+// workgroup, from L2) equal to the X stream; small inputs use 128.
 //
 // fp32 path: plain FMA (no rounding of the residual), for fp32 residuals.
 #include "tg_common.hpp"
@@ -16,66 +19,101 @@
 namespace tg {
 namespace {
 
-constexpr int kBM = 128;   // tokens per workgroup
-constexpr int kBK = 32;    // reduction slab
-constexpr int kLdk = kBK + 8;  // padded LDS row (elements): 80 B, conflict-free 16-B reads
+// Slab geometry: BK reduction columns per slab; rows padded by one 16-B chunk.
+template <int BK>
+struct Slab {
+    static constexpr int ROW_CHUNKS = BK / 8 + 1;   // 16-B chunks per padded LDS row
+    static constexpr int LDK = ROW_CHUNKS * 8;      // padded row (elements): 80 B / 144 B
+};
+constexpr int kBK = 64;      // reduction slab (a full 128-B line of every X row)
+constexpr int kStages = 2;   // slabs in LDS: one in use, one in flight
+constexpr int kRowChunks = Slab<kBK>::ROW_CHUNKS;
+constexpr int kLdk = Slab<kBK>::LDK;
 
 __device__ __forceinline__ float silu_f32(float a) {
     // a * sigmoid(a); exp2 of a finite argument, saturating correctly at +-inf.
     return a / (1.0f + __builtin_amdgcn_exp2f(-a * kLog2e));
 }
 
-// CB = hidden units per wave / 32; d_hid = 64 * CB; waves arranged 2 (rows) x 2 (cols).
-template <int CB>
-__global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (LDS / export counters left unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (7 << 4) | (0xf << 8); }
+
+// Wait until at most n (wave-uniform, 0..12) vector-memory operations remain.
+__device__ __forceinline__ void wait_vm_le(int n) {
+    switch (n) {
+        case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2)); break;
+        case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3)); break;
+        case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); break;
+        case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5)); break;
+        case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6)); break;
+        case 7: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7)); break;
+        case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
+        case 9: __builtin_amdgcn_s_waitcnt(vmcnt_imm(9)); break;
+        case 10: __builtin_amdgcn_s_waitcnt(vmcnt_imm(10)); break;
+        case 11: __builtin_amdgcn_s_waitcnt(vmcnt_imm(11)); break;
+        case 12: __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); break;
+        default: __builtin_amdgcn_s_waitcnt(0); break;
+    }
+}
+
+// BM tokens per workgroup (BM / 64 row groups of waves x 2 hidden-column
+// groups); CB = 32-wide hidden blocks per wave, d_hid = 64 * CB.  Both operands
+// are K-contiguous and arrive by global_load_lds_dwordx4 (1 KiB of consecutive
+// LDS per instruction; rows padded by one 16-B chunk whose slot reloads chunk
+// 0).  Three slab buffers keep two slabs of loads in flight per workgroup.
+template <int CB, int BM>
+__global__ __launch_bounds__(BM * 2, 1) void gate_bf16_kernel(
     const bf16* __restrict__ x, int64_t n, int d_model, int64_t x_stride,
     const bf16* __restrict__ w1, const float* __restrict__ b1, const float* __restrict__ w2,
     float b2, float* __restrict__ scores) {
+    constexpr int NT = BM * 2;                         // threads
+    constexpr int NW = NT / 64;                        // waves
     constexpr int NH = 64 * CB;
-    constexpr int XCH = kBM * kBK / 8 / 256;   // 16-B chunks of the X slab per thread (2)
-    constexpr int WCH = NH * kBK / 8 / 256;    // ... of the W1 slab (CB)
-    constexpr int SLAB = (kBM + NH) * kLdk;            // elements per slab buffer
-    constexpr int RED_BYTES = kBM * 65 * 4;            // epilogue partial sums
-    constexpr int LDS_BYTES = 2 * SLAB * 2 > RED_BYTES ? 2 * SLAB * 2 : RED_BYTES;
-    __shared__ __attribute__((aligned(16))) char lds_raw[LDS_BYTES];
+    constexpr int XI = BM * kRowChunks / 64;           // load instructions per X slab
+    constexpr int WI = NH * kRowChunks / 64;           // ... per W1 slab
+    constexpr int NI = XI + WI;
+    constexpr int IPW = (NI + NW - 1) / NW;            // per wave (upper bound)
+    constexpr int SLAB = (BM + NH) * kLdk;             // elements per slab buffer
+    constexpr int RED_BYTES = BM * 65 * 4;             // epilogue partial sums
+    constexpr int LDS_BYTES = kStages * SLAB * 2 > RED_BYTES ? kStages * SLAB * 2 : RED_BYTES;
+    static_assert(BM * kRowChunks % 64 == 0 && NH * kRowChunks % 64 == 0, "whole load instructions");
+    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
     bf16* const lds0 = (bf16*)lds_raw;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
     const int il = lane & 31, half = lane >> 5;
-    const int64_t row0 = (int64_t)blockIdx.x * kBM;
+    const int64_t row0 = (int64_t)blockIdx.x * BM;
+    const bf16* const xblk = x + row0 * x_stride;
+    // this wave's load instructions: g = wave + NW * i for g < NI
+    const int my_ni = (NI - wave + NW - 1) / NW;
 
-    // global -> register staging of one slab
-    u32x4 xr[XCH], wreg[WCH];
-    auto load_slab = [&](int kb) {
+    int off[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int g = wave + NW * i;
+        off[i] = 0;
+        if (g < XI) {
+            const int slot = g * 64 + lane;
+            const int r = slot / kRowChunks, c = slot % kRowChunks;
+            const int rr = row0 + r < n ? r : (int)(n - 1 - row0);   // clamp rows past the end
+            off[i] = rr * (int)x_stride + (c < kBK / 8 ? c : 0) * 8;
+        } else if (g < NI) {
+            const int slot = (g - XI) * 64 + lane;
+            const int r = slot / kRowChunks, c = slot % kRowChunks;
+            off[i] = r * d_model + (c < kBK / 8 ? c : 0) * 8;
+        }
+    }
+    auto issue = [&](int kb, int buf) {
         const int k0 = kb * kBK;
+        char* dst = (char*)(lds0 + buf * SLAB);
 #pragma unroll
-        for (int c = 0; c < XCH; ++c) {
-            const int ch = tid + 256 * c;
-            const int r = ch >> 2, cc = ch & 3;
-            int64_t gr = row0 + r;
-            gr = gr < n ? gr : n - 1;
-            xr[c] = *(const u32x4*)(x + gr * x_stride + k0 + cc * 8);
-        }
-#pragma unroll
-        for (int c = 0; c < WCH; ++c) {
-            const int ch = tid + 256 * c;
-            const int r = ch >> 2, cc = ch & 3;
-            wreg[c] = *(const u32x4*)(w1 + (int64_t)r * d_model + k0 + cc * 8);
-        }
-    };
-    auto store_slab = [&](int buf) {
-        bf16* xs = lds0 + buf * SLAB;
-        bf16* ws = xs + kBM * kLdk;
-#pragma unroll
-        for (int c = 0; c < XCH; ++c) {
-            const int ch = tid + 256 * c;
-            *(u32x4*)(xs + (ch >> 2) * kLdk + (ch & 3) * 8) = xr[c];
-        }
-#pragma unroll
-        for (int c = 0; c < WCH; ++c) {
-            const int ch = tid + 256 * c;
-            *(u32x4*)(ws + (ch >> 2) * kLdk + (ch & 3) * 8) = wreg[c];
+        for (int i = 0; i < IPW; ++i) {
+            const int g = wave + NW * i;
+            if (g < XI) lds_load16(xblk + k0 + off[i], dst + g * 1024);
+            else if (g < NI) lds_load16(w1 + k0 + off[i], dst + BM * kLdk * 2 + (g - XI) * 1024);
         }
     };
 
@@ -86,14 +124,20 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
         for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x16{};
 
     const int nk = d_model / kBK;
-    load_slab(0);
-    store_slab(0);
+    constexpr int AHEAD = kStages - 1;   // slabs in flight while one is consumed
+#pragma unroll
+    for (int p = 0; p < AHEAD; ++p)
+        if (p < nk) issue(p, p);
+    // slab 0 must land; slabs 1 .. AHEAD-1 may still be in flight
+    if (AHEAD > 1 && nk > 1) wait_vm_le(my_ni * (AHEAD - 1));
+    else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kb = 0; kb < nk; ++kb) {
-        const int buf = kb & 1;
-        if (kb + 1 < nk) load_slab(kb + 1);
+        const int buf = kb % kStages;
+        const bool more = kb + AHEAD < nk;
+        if (more) issue(kb + AHEAD, (kb + AHEAD) % kStages);
         const bf16* xs = lds0 + buf * SLAB;
-        const bf16* ws = xs + kBM * kLdk;
+        const bf16* ws = xs + BM * kLdk;
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
             bf16x8 a[2], b[CB];
@@ -109,7 +153,9 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
                 for (int cb = 0; cb < CB; ++cb)
                     acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
         }
-        if (kb + 1 < nk) store_slab(buf ^ 1);
+        // slab kb+1 must have landed; later slabs may stay in flight
+        if (more && AHEAD > 1) wait_vm_le(my_ni * (AHEAD - 1));
+        else __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
@@ -123,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
         bias1[cb] = b1 ? b1[nidx] : 0.0f;
         wout[cb] = w2[nidx];
     }
-    float* red = (float*)lds_raw;   // [kBM][65] partial sums, aliases the slab buffers
+    float* red = (float*)lds_raw;   // [BM][65] partial sums, aliases the slab buffers
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
@@ -145,6 +191,35 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
         sum += __shfl_xor(sum, 1, 64);
         if (part == 0 && row0 + tok < n) scores[row0 + tok] = sum + b2;
     }
+}
+
+template <int CB, int BM>
+int launch_gate_tile(const bf16* x, int64_t n, int d_model, int64_t x_stride, const bf16* w1,
+                     const float* b1, const float* w2, float b2, float* scores, hipStream_t st) {
+    constexpr int NH = 64 * CB;
+    constexpr size_t slab = (size_t)(BM + NH) * kLdk * 2;
+    constexpr size_t red = (size_t)BM * 65 * 4;
+    constexpr size_t shm = kStages * slab > red ? kStages * slab : red;
+    static bool attr_set = false;   // idempotent; racing first calls set the same value
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void*)gate_bf16_kernel<CB, BM>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) != hipSuccess)
+            return TG_ERR_HIP;
+        attr_set = true;
+    }
+    const dim3 grid((unsigned)((n + BM - 1) / BM));
+    hipLaunchKernelGGL((gate_bf16_kernel<CB, BM>), grid, dim3(BM * 2), shm, st, x, n, d_model, x_stride, w1,
+                       b1, w2, b2, scores);
+    return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
+template <int CB>
+int launch_gate_cb(const bf16* x, int64_t n, int d_model, int64_t x_stride, const bf16* w1,
+                   const float* b1, const float* w2, float b2, float* scores, hipStream_t st) {
+    // 256-token tiles once there are at least two per CU (256 CUs), else 128
+    if (n >= (int64_t)256 * 256 * 2)
+        return launch_gate_tile<CB, 256>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
+    return launch_gate_tile<CB, 128>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
 }
 
 // fp32 residuals: 4 tokens per workgroup staged in LDS, threads stride over
@@ -201,15 +276,13 @@ int launch_gate_bf16(const bf16* x, int64_t n, int d_model, int64_t x_stride, co
                      const float* b1, const float* w2, float b2, int d_hid, float* scores,
                      hipStream_t st) {
     if (n == 0) return TG_OK;
-    const dim3 grid((unsigned)((n + kBM - 1) / kBM));
     switch (d_hid) {
-        case 64:  hipLaunchKernelGGL(gate_bf16_kernel<1>, grid, dim3(256), 0, st, x, n, d_model, x_stride, w1, b1, w2, b2, scores); break;
-        case 128: hipLaunchKernelGGL(gate_bf16_kernel<2>, grid, dim3(256), 0, st, x, n, d_model, x_stride, w1, b1, w2, b2, scores); break;
-        case 192: hipLaunchKernelGGL(gate_bf16_kernel<3>, grid, dim3(256), 0, st, x, n, d_model, x_stride, w1, b1, w2, b2, scores); break;
-        case 256: hipLaunchKernelGGL(gate_bf16_kernel<4>, grid, dim3(256), 0, st, x, n, d_model, x_stride, w1, b1, w2, b2, scores); break;
+        case 64: return launch_gate_cb<1>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
+        case 128: return launch_gate_cb<2>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
+        case 192: return launch_gate_cb<3>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
+        case 256: return launch_gate_cb<4>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
         default: return TG_ERR_UNSUPPORTED;
     }
-    return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 
 int launch_gate_f32(const float* x, int64_t n, int d_model, int64_t x_stride, const float* w1,
