@@ -8,7 +8,7 @@
 // causal on original positions, R = rotary embedding on original positions.
 //
 // Work split.
-//  1. attn_prep_kernel (one workgroup per 64 kept tokens):
+//  1. attn_prep_kernel (one workgroup per 64 kept tokens and kv head):
 //     - rotary angles pos * base^(-2f/D) in fp64, reduced mod 2pi, then fp32
 //       (cos, sin), kept as a per-token table for the queries;
 //     - keys rotated in fp32 and rounded to bf16 into K' rows [Hkv][row][D+16]
@@ -89,6 +89,9 @@ __device__ __forceinline__ float bf16_ceil(float x) {
 }
 
 // ---------------------------------------------------------------- pre-pass --
+// One workgroup per (64 kept tokens, kv head); lane = token.  Head-0 groups
+// also store the (cos, sin) table the queries use.  A last group row zero-fills
+// the padding rows (below).
 template <int D>
 __global__ __launch_bounds__(256) void attn_prep_kernel(
     const bf16* __restrict__ k, const bf16* __restrict__ v, int64_t kv_stride,
@@ -98,6 +101,32 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
     constexpr int HALF = D / 2, KD = D + kExtra, FPW = HALF / 4, VLD = D + 2;
     __shared__ __attribute__((aligned(16))) bf16 vs[64 * VLD];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = blockIdx.y;
+    if (h == hkv) {
+        // Zero the padding rows between sequences (and after the last one), so
+        // that key tiles can be loaded whole: rows past a sequence's end are then
+        // either zeros or other sequences' finite data, and their probabilities
+        // are 0.  Grid-stride over (padded row, kv head); a row is padding iff it
+        // lies past the end of the sequence whose padded start precedes it.
+        const int64_t nthreads = (int64_t)gridDim.x * 256;
+        for (int64_t idx = (int64_t)blockIdx.x * 256 + tid; idx < mp * hkv; idx += nthreads) {
+            const int64_t r = idx / hkv;
+            const int hh = (int)(idx % hkv);
+            int lo = 0, hi = n_seqs;   // last sequence whose padded start is <= r (or 0)
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (padded_seq_start(cu_kept[mid], mid) <= r) lo = mid; else hi = mid;
+            }
+            const int64_t p0 = padded_seq_start(cu_kept[lo], lo);
+            if (r >= p0 && r < p0 + (cu_kept[lo + 1] - cu_kept[lo])) continue;   // a token row
+            bf16* kr = ws_k + ((int64_t)hh * mp + r) * KD;
+#pragma unroll
+            for (int c = 0; c < KD; c += 8) *(bf16x8*)(kr + c) = bf16x8{};
+            bf16* vr = ws_vt + (int64_t)hh * D * mp + r;
+            for (int d = 0; d < D; ++d) vr[(int64_t)d * mp] = (bf16)0.0f;
+        }
+        return;
+    }
     const int64_t m0 = (int64_t)blockIdx.x * 64;
     const int64_t m = m0 + lane;
     const bool valid = m < m_tot;
@@ -106,111 +135,88 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
         const int s = find_seq(cu_kept, n_seqs, m);
         prow = padded_seq_start(cu_kept[s], s) + (m - cu_kept[s]);
     }
-    const int f0 = wave * FPW;
-    float cn[FPW], sn[FPW];
-    if (rope && valid) {
-        const double p = (double)pos[m];
-        const double two_pi = 6.283185307179586;
+    // V^T through LDS: coalesced row loads first (their latency overlaps the
+    // rotary work), then per channel d the 64 lanes store 64 consecutive rows.
+    constexpr int VCH = 64 * (D / 8) / 256;
+    bf16x8 vx[VCH];
 #pragma unroll
-        for (int e = 0; e < FPW; ++e) {
-            const double ang = p * fr.inv_freq[f0 + e];
-            const double red = ang - two_pi * rint(ang * (1.0 / two_pi));
-            sincosf((float)red, &sn[e], &cn[e]);
-        }
-        float4* dst = (float4*)(ws_cs + m * HALF + f0);
-#pragma unroll
-        for (int e = 0; e < FPW; e += 2) dst[e / 2] = make_float4(cn[e], sn[e], cn[e + 1], sn[e + 1]);
+    for (int i = 0; i < VCH; ++i) {
+        const int ch = tid + 256 * i;
+        const int r = ch / (D / 8), c8 = ch % (D / 8);
+        vx[i] = (m0 + r < m_tot) ? *(const bf16x8*)(v + (m0 + r) * kv_stride + (int64_t)h * D + c8 * 8) : bf16x8{};
     }
-    // K' rows: rotated keys + bias columns
+    // K' row: rotated key + bias columns
+    const int f0 = wave * FPW;
     if (valid) {
-        bf16x8 extra[2] = {bf16x8{}, bf16x8{}};
+        float cn[FPW], sn[FPW];
+        if (rope) {
+            const double p = (double)pos[m];
+            const double two_pi = 6.283185307179586;
+#pragma unroll
+            for (int e = 0; e < FPW; ++e) {
+                const double ang = p * fr.inv_freq[f0 + e];
+                const double red = ang - two_pi * rint(ang * (1.0 / two_pi));
+                sincosf((float)red, &sn[e], &cn[e]);
+            }
+            if (h == 0) {
+                float4* dst = (float4*)(ws_cs + m * HALF + f0);
+#pragma unroll
+                for (int e = 0; e < FPW; e += 2) dst[e / 2] = make_float4(cn[e], sn[e], cn[e + 1], sn[e + 1]);
+            }
+        }
+        const bf16* src = k + m * kv_stride + (int64_t)h * D;
+        bf16* dst = ws_k + ((int64_t)h * mp + prow) * KD;
+#pragma unroll
+        for (int c = 0; c < FPW / 8; ++c) {
+            bf16x8 x1 = *(const bf16x8*)(src + f0 + c * 8);
+            bf16x8 x2 = *(const bf16x8*)(src + HALF + f0 + c * 8);
+            if (rope) {
+                bf16x8 y1, y2;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float a = (float)x1[e], b = (float)x2[e];
+                    const float cc = cn[c * 8 + e], ss = sn[c * 8 + e];
+                    y1[e] = (bf16)(a * cc - b * ss);
+                    y2[e] = (bf16)(b * cc + a * ss);
+                }
+                x1 = y1;
+                x2 = y2;
+            }
+            *(bf16x8*)(dst + f0 + c * 8) = x1;
+            *(bf16x8*)(dst + HALF + f0 + c * 8) = x2;
+        }
         if (wave == 0) {
+            bf16x8 extra[2] = {bf16x8{}, bf16x8{}};
             bf16 sh, sl;
             split_bf16(key_score[m], &sh, &sl);
             extra[0][0] = sh;
             extra[0][1] = sl;
             extra[0][2] = sh;
             extra[0][3] = (bf16)1.0f;
-        }
-        for (int h = 0; h < hkv; ++h) {
-            const bf16* src = k + m * kv_stride + (int64_t)h * D;
-            bf16* dst = ws_k + ((int64_t)h * mp + prow) * KD;
-#pragma unroll
-            for (int c = 0; c < FPW / 8; ++c) {
-                bf16x8 x1 = *(const bf16x8*)(src + f0 + c * 8);
-                bf16x8 x2 = *(const bf16x8*)(src + HALF + f0 + c * 8);
-                if (rope) {
-                    bf16x8 y1, y2;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float a = (float)x1[e], b = (float)x2[e];
-                        const float cc = cn[c * 8 + e], ss = sn[c * 8 + e];
-                        y1[e] = (bf16)(a * cc - b * ss);
-                        y2[e] = (bf16)(b * cc + a * ss);
-                    }
-                    x1 = y1;
-                    x2 = y2;
-                }
-                *(bf16x8*)(dst + f0 + c * 8) = x1;
-                *(bf16x8*)(dst + HALF + f0 + c * 8) = x2;
-            }
-            if (wave == 0) {
-                *(bf16x8*)(dst + D) = extra[0];
-                *(bf16x8*)(dst + D + 8) = extra[1];
-            }
+            *(bf16x8*)(dst + D) = extra[0];
+            *(bf16x8*)(dst + D + 8) = extra[1];
         }
     }
-    // V^T through LDS: coalesced row loads, then per channel d the 64 lanes
-    // store 64 consecutive kept rows.
-    constexpr int VCH = 64 * (D / 8) / 256;
-    for (int h = 0; h < hkv; ++h) {
-        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-            const int ch = tid + 256 * i;
-            const int r = ch / (D / 8), c8 = ch % (D / 8);
-            bf16x8 x = bf16x8{};
-            if (m0 + r < m_tot) x = *(const bf16x8*)(v + (m0 + r) * kv_stride + (int64_t)h * D + c8 * 8);
-            uint32_t* dst = (uint32_t*)(vs + r * VLD + c8 * 8);   // VLD rows are 4-byte aligned
-            const uint32_t* xs = (const uint32_t*)&x;
+    for (int i = 0; i < VCH; ++i) {
+        const int ch = tid + 256 * i;
+        const int r = ch / (D / 8), c8 = ch % (D / 8);
+        uint32_t* d32 = (uint32_t*)(vs + r * VLD + c8 * 8);   // VLD rows are 4-byte aligned
+        const uint32_t* xs = (const uint32_t*)&vx[i];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) dst[u] = xs[u];
-        }
-        __syncthreads();
-        if (valid) {
-            bf16* dst = ws_vt + ((int64_t)h * D) * mp + prow;
+        for (int u = 0; u < 4; ++u) d32[u] = xs[u];
+    }
+    __syncthreads();
+    if (valid) {
+        bf16* dst = ws_vt + ((int64_t)h * D) * mp + prow;
 #pragma unroll 8
-            for (int dd = 0; dd < D / 4; ++dd) {
-                const int d = wave * (D / 4) + dd;
-                dst[(int64_t)d * mp] = vs[lane * VLD + d];
-            }
+        for (int dd = 0; dd < D / 4; ++dd) {
+            const int d = wave * (D / 4) + dd;
+            dst[(int64_t)d * mp] = vs[lane * VLD + d];
         }
-    }
-    // Zero the padding rows between sequences (and after the last one), so that
-    // key tiles can be loaded whole: rows past a sequence's end are then either
-    // zeros or other sequences' finite data, and their probabilities are 0.
-    // Grid-stride over (padded row, kv head); a row is padding iff it lies past
-    // the end of the sequence whose padded start precedes it.
-    const int64_t nthreads = (int64_t)gridDim.x * 256;
-    for (int64_t idx = (int64_t)blockIdx.x * 256 + tid; idx < mp * hkv; idx += nthreads) {
-        const int64_t r = idx / hkv;
-        const int h = (int)(idx % hkv);
-        int lo = 0, hi = n_seqs;   // last sequence whose padded start is <= r (or 0)
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (padded_seq_start(cu_kept[mid], mid) <= r) lo = mid; else hi = mid;
-        }
-        const int64_t p0 = padded_seq_start(cu_kept[lo], lo);
-        if (r >= p0 && r < p0 + (cu_kept[lo + 1] - cu_kept[lo])) continue;   // a token row
-        bf16* kr = ws_k + ((int64_t)h * mp + r) * KD;
-#pragma unroll
-        for (int c = 0; c < KD; c += 8) *(bf16x8*)(kr + c) = bf16x8{};
-        bf16* vr = ws_vt + (int64_t)h * D * mp + r;
-        for (int d = 0; d < D; ++d) vr[(int64_t)d * mp] = (bf16)0.0f;
     }
 }
 
-// ------------------------------------------------------------- main kernel --
 template <int D>
 struct AttnLds {
     // K' tiles arrive by global_load_lds_dwordx4: every load instruction copies
@@ -597,7 +603,8 @@ template <int D>
 int launch_all(const AttnArgs& a, hipStream_t st) {
     RopeFreqs fr;
     for (int f = 0; f < 64; ++f) fr.inv_freq[f] = f < D / 2 ? exp2(-(2.0 * f / D) * a.rope_log2_base) : 0.0;
-    hipLaunchKernelGGL(attn_prep_kernel<D>, dim3((unsigned)((a.m_tot + 63) / 64)), dim3(256), 0, st, a.k,
+    // grid.y = kv heads, plus one extra row of groups for the padding fill
+    hipLaunchKernelGGL(attn_prep_kernel<D>, dim3((unsigned)((a.m_tot + 63) / 64), a.hkv + 1), dim3(256), 0, st, a.k,
                        a.v, a.kv_stride, a.key_score, a.pos, a.cu_kept, a.n_seqs, a.m_tot, a.hkv, a.mp, fr,
                        (int)a.rope, a.ws_k, a.ws_vt, a.ws_cs);
     if (hipGetLastError() != hipSuccess) return TG_ERR_HIP;
