@@ -143,7 +143,8 @@ int tg_gather_kept(const void* x, int32_t x_dtype, int32_t d_model, int64_t x_ro
                    int32_t n_seqs, const int32_t* cu_seqlens, const int32_t* cu_kept,
                    void* x_kept, float* scores_kept, int32_t* pos_kept, void* stream);
 
-/* Workspace bytes tg_keybias_attn_prefill needs for these sizes. */
+/* Workspace bytes tg_keybias_attn_prefill (and tg_attn_prepare / tg_attn_forward)
+ * need for these sizes. */
 size_t tg_attn_workspace_bytes(int32_t n_seqs, int64_t n_kept_total, int32_t n_kv_heads,
                                int32_t head_dim);
 
@@ -181,6 +182,42 @@ int tg_keybias_attn_prefill(const void* q, const void* k, const void* v, int64_t
                             int64_t n_kept_total, int32_t max_kept_seqlen, int32_t n_q_heads,
                             int32_t n_kv_heads, int32_t head_dim, double rope_base, void* out,
                             float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two halves of tg_keybias_attn_prefill, for callers that keep the kept
+ * tokens' keys and values for several query passes, or time the attention
+ * kernel alone.  Calling tg_attn_prepare then tg_attn_forward on one stream
+ * gives bit-identical results to tg_keybias_attn_prefill (same kernels).
+ *
+ * tg_attn_prepare writes the kept-only key/value cache into `workspace`
+ * (spke.com article, pruned-forward phase: layers above the gate hold keys
+ * and values for the kept tokens only, and the token-gated attention section:
+ * the key's gate score is its bias).  Per kv head it stores the keys rotated
+ * on their original positions with the gate score folded into extra columns,
+ * the values transposed, and per kept token the rotary cos/sin table that the
+ * forward pass applies to the queries.  Arguments and requirements as for
+ * tg_keybias_attn_prefill (k, v, kv_row_stride, key_score, pos, cu_kept,
+ * n_seqs, n_kept_total, n_kv_heads, head_dim, rope_base, workspace).
+ */
+int tg_attn_prepare(const void* k, const void* v, int64_t kv_row_stride, const float* key_score,
+                    const int32_t* pos, const int32_t* cu_kept, int32_t n_seqs, int64_t n_kept_total,
+                    int32_t n_kv_heads, int32_t head_dim, double rope_base, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * tg_attn_forward runs the token-gated attention of tg_keybias_attn_prefill
+ * over a workspace filled by tg_attn_prepare (q, q_row_stride, head_gain, tau,
+ * max_kept_seqlen, n_q_heads, out, lse as there).  cu_kept, n_seqs,
+ * n_kept_total, n_kv_heads, head_dim and rope_base must equal those of the
+ * tg_attn_prepare call that filled the workspace, and that call must precede
+ * this one in stream order; otherwise the results are undefined.  The
+ * workspace is only read.
+ */
+int tg_attn_forward(const void* q, int64_t q_row_stride, const float* head_gain, float tau,
+                    const int32_t* cu_kept, int32_t n_seqs, int64_t n_kept_total,
+                    int32_t max_kept_seqlen, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                    double rope_base, void* out, float* lse, const void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -34,6 +34,9 @@ SIGNATURES = {
     "tg_attn_workspace_bytes": (_SZ, [_I32, _I64, _I32, _I32]),
     "tg_keybias_attn_prefill": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P, _F, _P, _P, _I32, _I64,
                                                _I32, _I32, _I32, _I32, _D, _P, _P, _P, _SZ, _P]),
+    "tg_attn_prepare": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _D, _P, _SZ, _P]),
+    "tg_attn_forward": (ctypes.c_int, [_P, _I64, _P, _F, _P, _I32, _I64, _I32, _I32, _I32, _I32, _D, _P, _P,
+                                       _P, _SZ, _P]),
 }
 
 
@@ -161,14 +164,56 @@ def tg_attn_workspace_bytes(n_seqs, n_kept_total, n_kv_heads, head_dim) -> int:
     return load().tg_attn_workspace_bytes(n_seqs, n_kept_total, n_kv_heads, head_dim)
 
 
+def _check_kv(k, v):
+    if k.stride(2) != 1 or k.stride(1) != k.shape[2] or v.stride() != k.stride():
+        raise ValueError("heads must be contiguous within a token row; k and v must share strides")
+
+
+def _check_q(q):
+    if q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+        raise ValueError("heads must be contiguous within a token row")
+
+
+def tg_attn_prepare(k, v, key_score, pos, cu_kept, rope_base: float = 1e6, workspace=None):
+    """Kept-only key/value cache for tg_attn_forward; returns the workspace."""
+    _check_kv(k, v)
+    m, hkv, d = k.shape
+    n_seqs = cu_kept.shape[0] - 1
+    need = tg_attn_workspace_bytes(n_seqs, m, hkv, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+    st = load().tg_attn_prepare(_ptr(k), _ptr(v), k.stride(0), _ptr(key_score), _ptr(pos), _ptr(cu_kept), n_seqs, m,
+                                hkv, d, float(rope_base), _ptr(workspace), workspace.numel(), _stream(k))
+    _check("tg_attn_prepare", st)
+    return workspace
+
+
+def tg_attn_forward(q, head_gain, tau: float, cu_kept, max_kept_seqlen: int, n_kv_heads: int, workspace,
+                    rope_base: float = 1e6, out=None, lse=None, want_lse: bool = True):
+    """q: [M, Hq, D] bf16 over a workspace filled by tg_attn_prepare with the same metadata."""
+    _check_q(q)
+    m, hq, d = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((m, hq, d), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((hq, m), dtype=torch.float32, device=dev)
+    st = load().tg_attn_forward(_ptr(q), q.stride(0), _ptr(head_gain), float(tau), _ptr(cu_kept),
+                                cu_kept.shape[0] - 1, m, int(max_kept_seqlen), hq, int(n_kv_heads), d,
+                                float(rope_base), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                _stream(q))
+    _check("tg_attn_forward", st)
+    return out, lse
+
+
 def tg_keybias_attn_prefill(q, k, v, key_score, head_gain, tau: float, pos, cu_kept,
                             max_kept_seqlen: int, rope_base: float = 1e6, out=None, lse=None,
                             workspace=None, want_lse: bool = True):
     """q: [M, Hq, D] (token rows may be strided), k/v: [M, Hkv, D] bf16."""
+    _check_q(q)
+    _check_kv(k, v)
     m, hq, d = q.shape
     hkv = k.shape[1]
-    if q.stride(2) != 1 or q.stride(1) != d or k.stride(2) != 1 or k.stride(1) != d or v.stride() != k.stride():
-        raise ValueError("heads must be contiguous within a token row; k and v must share strides")
     n_seqs = cu_kept.shape[0] - 1
     dev = q.device
     if out is None:

@@ -110,57 +110,129 @@ size_t tg_attn_workspace_bytes(int32_t n_seqs, int64_t n_kept_total, int32_t n_k
                                  nullptr);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the attention entry points; q-side checks only when q_side.
+int attn_check(bool q_side, const void* q, int64_t q_row_stride, int32_t max_kept_seqlen,
+               int32_t n_q_heads, float tau, const void* out, int64_t kv_row_stride,
+               int32_t n_seqs, int64_t n_kept_total, int32_t n_kv_heads, int32_t head_dim,
+               double rope_base, const void* workspace, size_t workspace_bytes) {
+    if (!isfinite(rope_base)) return TG_ERR_INVALID_ARG;
+    if (n_seqs < 0 || n_kept_total < 0 || n_kept_total > INT32_MAX) return TG_ERR_INVALID_ARG;
+    if (n_kv_heads <= 0) return TG_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return TG_ERR_UNSUPPORTED;
+    if (q_side) {
+        if (!(tau > 0.0f) || !isfinite(tau) || max_kept_seqlen < 0) return TG_ERR_INVALID_ARG;
+        if (n_q_heads <= 0 || n_q_heads % n_kv_heads != 0) return TG_ERR_INVALID_ARG;
+        const int grp = n_q_heads / n_kv_heads;
+        if (grp != 1 && grp != 2 && grp != 4 && grp != 8) return TG_ERR_UNSUPPORTED;
+        if (q_row_stride < (int64_t)n_q_heads * head_dim || q_row_stride % 8 != 0) return TG_ERR_INVALID_ARG;
+    } else {
+        if (kv_row_stride < (int64_t)n_kv_heads * head_dim || kv_row_stride % 8 != 0)
+            return TG_ERR_INVALID_ARG;
+    }
+    if (n_kept_total == 0) return -1;   // valid, nothing to do
+    if (n_seqs < 1) return TG_ERR_INVALID_ARG;
+    if (q_side) {
+        if (max_kept_seqlen < 1 || max_kept_seqlen > n_kept_total) return TG_ERR_INVALID_ARG;
+        if (!q || !out || !aligned16(q) || !aligned16(out)) return TG_ERR_INVALID_ARG;
+    }
+    const size_t need = attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, nullptr,
+                                              nullptr, nullptr);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+        return TG_ERR_WORKSPACE;
+    return TG_OK;
+}
+
+void attn_fill(AttnArgs& a, int32_t n_seqs, int64_t n_kept_total, int32_t n_kv_heads,
+               int32_t head_dim, double rope_base, const void* workspace) {
+    size_t off_k, off_vt, off_cs;
+    attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, &off_k, &off_vt, &off_cs);
+    a.n_seqs = n_seqs;
+    a.m_tot = n_kept_total;
+    a.hkv = n_kv_heads;
+    a.d = head_dim;
+    a.rope = rope_base > 0.0;
+    a.rope_log2_base = a.rope ? log2(rope_base) : 0.0;
+    char* ws = (char*)workspace;
+    a.ws_k = (bf16*)(ws + off_k);
+    a.ws_vt = (bf16*)(ws + off_vt);
+    a.ws_cs = (float2*)(ws + off_cs);
+    a.mp = attn_padded_rows(n_seqs, n_kept_total);
+}
+
+}  // namespace
+
+extern "C" {
+
+int tg_attn_prepare(const void* k, const void* v, int64_t kv_row_stride, const float* key_score,
+                    const int32_t* pos, const int32_t* cu_kept, int32_t n_seqs, int64_t n_kept_total,
+                    int32_t n_kv_heads, int32_t head_dim, double rope_base, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    const int st = attn_check(false, nullptr, 0, 0, 0, 1.0f, nullptr, kv_row_stride, n_seqs,
+                              n_kept_total, n_kv_heads, head_dim, rope_base, workspace, workspace_bytes);
+    if (st == -1) return TG_OK;
+    if (st != TG_OK) return st;
+    if (!k || !v || !key_score || !pos || !cu_kept || !aligned16(k) || !aligned16(v)) return TG_ERR_INVALID_ARG;
+    AttnArgs a{};
+    attn_fill(a, n_seqs, n_kept_total, n_kv_heads, head_dim, rope_base, workspace);
+    a.k = (const bf16*)k;
+    a.v = (const bf16*)v;
+    a.kv_stride = kv_row_stride;
+    a.key_score = key_score;
+    a.pos = pos;
+    a.cu_kept = cu_kept;
+    return launch_attn_prep(a, (hipStream_t)stream);
+}
+
+int tg_attn_forward(const void* q, int64_t q_row_stride, const float* head_gain, float tau,
+                    const int32_t* cu_kept, int32_t n_seqs, int64_t n_kept_total,
+                    int32_t max_kept_seqlen, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                    double rope_base, void* out, float* lse, const void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    const int st = attn_check(true, q, q_row_stride, max_kept_seqlen, n_q_heads, tau, out, 0, n_seqs,
+                              n_kept_total, n_kv_heads, head_dim, rope_base, workspace, workspace_bytes);
+    if (st == -1) return TG_OK;
+    if (st != TG_OK) return st;
+    if (!head_gain || !cu_kept) return TG_ERR_INVALID_ARG;
+    AttnArgs a{};
+    attn_fill(a, n_seqs, n_kept_total, n_kv_heads, head_dim, rope_base, workspace);
+    a.q = (const bf16*)q;
+    a.q_stride = q_row_stride;
+    a.gain = head_gain;
+    a.qk_scale_log2 = (float)(1.4426950408889634 / (sqrt((double)head_dim) * (double)tau));
+    a.cu_kept = cu_kept;
+    a.max_kept_seqlen = max_kept_seqlen;
+    a.hq = n_q_heads;
+    a.out = (bf16*)out;
+    a.lse = lse;
+    return launch_attn_fwd(a, (hipStream_t)stream);
+}
+
 int tg_keybias_attn_prefill(const void* q, const void* k, const void* v, int64_t q_row_stride,
                             int64_t kv_row_stride, const float* key_score, const float* head_gain,
                             float tau, const int32_t* pos, const int32_t* cu_kept, int32_t n_seqs,
                             int64_t n_kept_total, int32_t max_kept_seqlen, int32_t n_q_heads,
                             int32_t n_kv_heads, int32_t head_dim, double rope_base, void* out,
                             float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-    if (!(tau > 0.0f) || !isfinite(tau) || !isfinite(rope_base)) return TG_ERR_INVALID_ARG;
-    if (n_seqs < 0 || n_kept_total < 0 || n_kept_total > INT32_MAX || max_kept_seqlen < 0)
+    // validate both halves before launching either
+    int st = attn_check(false, nullptr, 0, 0, 0, 1.0f, nullptr, kv_row_stride, n_seqs, n_kept_total,
+                        n_kv_heads, head_dim, rope_base, workspace, workspace_bytes);
+    if (st == TG_OK || st == -1)
+        st = attn_check(true, q, q_row_stride, max_kept_seqlen, n_q_heads, tau, out, 0, n_seqs,
+                        n_kept_total, n_kv_heads, head_dim, rope_base, workspace, workspace_bytes);
+    if (st == -1) return TG_OK;
+    if (st != TG_OK) return st;
+    if (!k || !v || !key_score || !pos || !cu_kept || !head_gain || !aligned16(k) || !aligned16(v))
         return TG_ERR_INVALID_ARG;
-    if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0) return TG_ERR_INVALID_ARG;
-    if (head_dim != 64 && head_dim != 128) return TG_ERR_UNSUPPORTED;
-    const int grp = n_q_heads / n_kv_heads;
-    if (grp != 1 && grp != 2 && grp != 4 && grp != 8) return TG_ERR_UNSUPPORTED;
-    if (q_row_stride < (int64_t)n_q_heads * head_dim || q_row_stride % 8 != 0) return TG_ERR_INVALID_ARG;
-    if (kv_row_stride < (int64_t)n_kv_heads * head_dim || kv_row_stride % 8 != 0) return TG_ERR_INVALID_ARG;
-    if (n_kept_total == 0) return TG_OK;
-    if (n_seqs < 1 || max_kept_seqlen < 1 || max_kept_seqlen > n_kept_total) return TG_ERR_INVALID_ARG;
-    if (!q || !k || !v || !key_score || !head_gain || !pos || !cu_kept || !out) return TG_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return TG_ERR_INVALID_ARG;
-    size_t off_k, off_vt, off_cs;
-    const size_t need = attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, &off_k,
-                                              &off_vt, &off_cs);
-    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
-        return TG_ERR_WORKSPACE;
-    AttnArgs a;
-    a.q = (const bf16*)q;
-    a.k = (const bf16*)k;
-    a.v = (const bf16*)v;
-    a.q_stride = q_row_stride;
-    a.kv_stride = kv_row_stride;
-    a.key_score = key_score;
-    a.gain = head_gain;
-    a.qk_scale_log2 = (float)(1.4426950408889634 / (sqrt((double)head_dim) * (double)tau));
-    a.pos = pos;
-    a.cu_kept = cu_kept;
-    a.n_seqs = n_seqs;
-    a.m_tot = n_kept_total;
-    a.max_kept_seqlen = max_kept_seqlen;
-    a.hq = n_q_heads;
-    a.hkv = n_kv_heads;
-    a.d = head_dim;
-    a.rope = rope_base > 0.0;
-    a.rope_log2_base = a.rope ? log2(rope_base) : 0.0;
-    a.out = (bf16*)out;
-    a.lse = lse;
-    char* ws = (char*)workspace;
-    a.ws_k = (bf16*)(ws + off_k);
-    a.ws_vt = (bf16*)(ws + off_vt);
-    a.ws_cs = (float2*)(ws + off_cs);
-    a.mp = attn_padded_rows(n_seqs, n_kept_total);
-    return launch_attn(a, (hipStream_t)stream);
+    st = tg_attn_prepare(k, v, kv_row_stride, key_score, pos, cu_kept, n_seqs, n_kept_total, n_kv_heads,
+                         head_dim, rope_base, workspace, workspace_bytes, stream);
+    if (st != TG_OK) return st;
+    return tg_attn_forward(q, q_row_stride, head_gain, tau, cu_kept, n_seqs, n_kept_total,
+                           max_kept_seqlen, n_q_heads, n_kv_heads, head_dim, rope_base, out, lse,
+                           workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

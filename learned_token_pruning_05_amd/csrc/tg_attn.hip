@@ -15,8 +15,10 @@
 //       whose 16 extra columns carry the key score split in two bf16 halves
 //       (s_hi, s_lo, s_hi, 0...), so the bias rides inside the QK MFMA;
 //     - values transposed through LDS to V^T [Hkv][D][row] (coalesced stores),
-//       the layout the P.V MFMA operand wants.
-//     Rows are padded per sequence so every sequence starts 16-byte aligned.
+//       the layout the P.V MFMA operand wants, with the middle two quads of
+//       every 16-key group swapped (vt_col) to match the P^T operand's order.
+//     Rows are padded per sequence so every sequence starts on a 16-row
+//     boundary.
 //  2. attn_fwd_kernel: FlashAttention-style online softmax in the log2 domain.
 //     Queries are rotated, scaled by log2(e)/(sqrt(D) tau) and rounded to bf16
 //     once per workgroup; their 16 extra columns hold (g_hi, g_hi, g_lo, 0...)
@@ -33,8 +35,8 @@
 //     use v_dot2 on the bf16 P that the P.V MFMA consumes; a block whose sum
 //     exceeds 2^62 (some p very large) takes a rare path that raises m to the
 //     block max and rescales O and l (the result is exact either way).  Each
-//     64-key tile is two 32-key blocks, so block 0's exponentials can overlap
-//     block 1's QK MFMAs and block 1's can overlap block 0's P.V MFMAs.
+//     64-key tile is two 32-key blocks: block 0's exponentials overlap block
+//     1's QK MFMAs, and block 1's overlap the previous tile's P.V MFMAs.
 //     All q heads of a KV group that fit in the workgroup share each K/V tile.
 //     Causality uses the kept order (positions increase within a sequence, so
 //     pos_j <= pos_i  <=>  j <= i).  Blocks are ordered head-fastest so that,
@@ -49,7 +51,7 @@ namespace tg {
 // Rows of the padded K'/V^T layout: sequence s starts at padded_seq_start();
 // the last sequence's final tile may reach 63 rows past its end.
 int64_t attn_padded_rows(int n_seqs, int64_t m_tot) {
-    return (((m_tot + 8 * (int64_t)n_seqs + 8) + 63) & ~(int64_t)63) + 64;
+    return (((m_tot + 16 * (int64_t)n_seqs + 16) + 63) & ~(int64_t)63) + 64;
 }
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
             bf16* kr = ws_k + ((int64_t)hh * mp + r) * KD;
 #pragma unroll
             for (int c = 0; c < KD; c += 8) *(bf16x8*)(kr + c) = bf16x8{};
-            bf16* vr = ws_vt + (int64_t)hh * D * mp + r;
+            bf16* vr = ws_vt + (int64_t)hh * D * mp + vt_col(r);
             for (int d = 0; d < D; ++d) vr[(int64_t)d * mp] = (bf16)0.0f;
         }
         return;
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
     }
     __syncthreads();
     if (valid) {
-        bf16* dst = ws_vt + ((int64_t)h * D) * mp + prow;
+        bf16* dst = ws_vt + ((int64_t)h * D) * mp + vt_col(prow);
 #pragma unroll 8
         for (int dd = 0; dd < D / 4; ++dd) {
             const int d = wave * (D / 4) + dd;
@@ -219,36 +221,44 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
 
 template <int D>
 struct AttnLds {
-    // K' tiles arrive by global_load_lds_dwordx4: every load instruction copies
-    // 64 lanes x 16 B into 1 KiB of consecutive LDS, so rows are padded by one
-    // 16-B chunk (pad slots hold a duplicate, never read) to keep the MFMA
-    // operand reads free of bank conflicts.  V^T tiles go through registers:
-    // their conflict-free row pitch (136 B) is not a multiple of 16 B.
+    // K' and V^T tiles arrive by global_load_lds_dwordx4: every load
+    // instruction copies 64 lanes x 16 B into 1 KiB of consecutive LDS, so rows
+    // are padded by one 16-B chunk (pad slots hold a duplicate, never read).
+    // The odd row pitch (19 / 9 chunks) keeps the 16-B MFMA operand reads of
+    // 8 consecutive lanes on 8 distinct 4-bank groups.
     static constexpr int KD = D + kExtra;
     static constexpr int KCHUNK = KD / 8;          // 16-B chunks per K' row (18 / 10)
     static constexpr int KROW = KCHUNK + 1;        // padded row, in chunks
     static constexpr int KLD = KROW * 8;           // ... in elements (152 / 88)
-    static constexpr int VLD = kBN + 4;            // V^T row (elements): 136 B, conflict-free 8-B reads
-    static constexpr int VCH = D * kBN / 8 / 256;  // 16-B chunks of a V^T tile per thread (staged in registers)
+    static constexpr int VCHUNK = kBN / 8;         // 16-B chunks per V^T row (8)
+    static constexpr int VROW = VCHUNK + 1;
+    static constexpr int VLD = VROW * 8;           // V^T row pitch in elements (72: 144 B)
     static constexpr int K_INSTR = kBN * KROW / 64;    // load instructions per K' tile (19 / 11)
-    static_assert(kBN * KROW % 64 == 0, "K' tiles must be whole load instructions");
+    static constexpr int V_INSTR = D * VROW / 64;      // ... per V^T tile (18 / 9)
+    static_assert(kBN * KROW % 64 == 0 && D * VROW % 64 == 0, "tiles must be whole load instructions");
     static constexpr int KPW = (K_INSTR + 3) / 4;      // per wave
+    static constexpr int VPW = (V_INSTR + 3) / 4;
     static constexpr int K_BYTES = kBN * KLD * 2;
     static constexpr int V_BYTES = D * VLD * 2;
     static constexpr int SMEM = 2 * K_BYTES + 2 * V_BYTES;   // two K' and two V^T buffers
 };
 
-// HW q heads per workgroup (1, 2 or 4); each of the 4 waves owns 32 query tokens
-// of one head; WB = 4 / HW waves per head; BMT = 32 * WB tokens per workgroup.
+// HW q heads per workgroup (1, 2 or 4); each of the 4 waves owns QW = 32 QB
+// query tokens of one head (QB blocks of 32); WB = 4 / HW waves per head;
+// BMT = QW WB tokens per workgroup.  Every K'/V^T fragment read from LDS feeds
+// QB MFMAs, so LDS traffic per flop falls as 1/QB; QB = 2 needs one wave per
+// SIMD (about 400 registers).
 //
 // Software pipeline per wave, iteration j (K' runs one tile ahead of V^T):
-//   R1  QK MFMAs of tile j+1, interleaved with the exponentials of tile j;
-//       (rare) offset refresh if tile j produced a huge probability;
-//   R2  P.V MFMAs of tile j;
-//       mask tile j+1 if it reaches this wave's diagonal;
+//   R1  QK MFMAs of tile j+1, key block 0 (K' fragments of block 1 read);
+//   R2  QK MFMAs of tile j+1, key block 1  ||  exponentials of key block 0;
+//   R3  P.V MFMAs of tile j                ||  exponentials of key block 1;
+//       (rare) offset refresh if tile j+1 produced a huge probability;
 //   K'(j+2) goes straight to LDS and V^T(j+1) through registers meanwhile.
-template <int D, int HW>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+// Masks are applied between the regions on the (at most two) tiles that reach
+// a wave's diagonal; tiles wholly past it are masked to zero probability.
+template <int D, int HW, int QB>
+__global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_fwd_kernel(
     const bf16* __restrict__ q, int64_t q_stride, const bf16* __restrict__ ws_k,
     const bf16* __restrict__ ws_vt, const float2* __restrict__ ws_cs, int rope,
     const float* __restrict__ gain, float qk_scale_log2, const int* __restrict__ cu_kept, int n_seqs,
@@ -256,7 +266,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     float* __restrict__ lse) {
     using L = AttnLds<D>;
     constexpr int WB = 4 / HW;
-    constexpr int BMT = 32 * WB;
+    constexpr int QW = 32 * QB;
+    constexpr int BMT = QW * WB;
     constexpr int KS = D / 16;      // MFMA k-steps over head_dim (+1 for the extra columns)
     constexpr int KD = L::KD;
     constexpr int DB = D / 32;      // 32-row blocks of O^T
@@ -279,17 +290,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const int nsub = grp / HW;
     const int hk = hidx / nsub;
     const int h = hk * grp + (hidx % nsub) * HW + wave / WB;
-    const int qb = q0 + (wave % WB) * 32;    // first query (sequence-local) of this wave
-    const int qi = qb + il;                  // this lane's query
-    const bool qvalid = qi < ms;
+    const int qb = q0 + (wave % WB) * QW;    // first query (sequence-local) of this wave
+    int qi[QB];                              // this lane's query in block c
+#pragma unroll
+    for (int c = 0; c < QB; ++c) qi[c] = qb + 32 * c + il;
     const int64_t prow0 = padded_seq_start(cs0, s);
     const int kend = min(ms, q0 + BMT);
     const int n_kt = (kend + kBN - 1) / kBN;
 
-    // ---- Q' fragment (B operand of S^T = K' Q'^T): rotated, scaled, + extra columns
-    bf16x8 qf[KS + 1];
-    {
-        const bf16* qrow = q + (int64_t)(cs0 + (qvalid ? qi : 0)) * q_stride + (int64_t)h * D;
+    // ---- Q' fragments (B operand of S^T = K' Q'^T): rotated, scaled, + extra columns
+    bf16x8 qf[QB][KS + 1];
+#pragma unroll
+    for (int c = 0; c < QB; ++c) {
+        const bool qvalid = qi[c] < ms;
+        const bf16* qrow = q + (int64_t)(cs0 + (qvalid ? qi[c] : 0)) * q_stride + (int64_t)h * D;
         float xf[KS][8];
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
@@ -298,7 +312,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
             for (int e = 0; e < 8; ++e) xf[t][e] = (float)raw[e];
         }
         if (rope && qvalid) {
-            const float2* csr = ws_cs + (int64_t)(cs0 + qi) * (D / 2);
+            const float2* csr = ws_cs + (int64_t)(cs0 + qi[c]) * (D / 2);
 #pragma unroll
             for (int t = 0; t < KS / 2; ++t) {
                 const float4* c4 = (const float4*)(csr + t * 16 + half * 8);
@@ -319,26 +333,32 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
         for (int t = 0; t < KS; ++t)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qf[t][e] = (bf16)(xf[t][e] * qk_scale_log2);
-        qf[KS] = bf16x8{};
+            for (int e = 0; e < 8; ++e) qf[c][t][e] = (bf16)(xf[t][e] * qk_scale_log2);
+        qf[c][KS] = bf16x8{};
         if (half == 0) {
             bf16 gh, glo;
             split_bf16(gain[h] * kLog2e, &gh, &glo);
-            qf[KS][0] = gh;
-            qf[KS][1] = gh;
-            qf[KS][2] = glo;
+            qf[c][KS][0] = gh;
+            qf[c][KS][1] = gh;
+            qf[c][KS][2] = glo;
         }
     }
 
-    // ---- LDS-direct tile loads.  Load instruction g of a K' (V^T) tile is
-    // issued by wave g % 4 and copies one 16-B chunk per lane; the per-lane
-    // source offsets are fixed for the whole kernel.
-    int koff[L::KPW];
+    // ---- LDS-direct tile loads.  Load instruction g of a tile is issued by
+    // wave g % 4 and copies one 16-B chunk per lane; the per-lane source
+    // offsets are fixed for the whole kernel.
+    int koff[L::KPW], voff[L::VPW];
 #pragma unroll
     for (int i = 0; i < L::KPW; ++i) {
         const int slot = (wave + 4 * i) * 64 + lane;
         const int r = slot / L::KROW, c = slot % L::KROW;
         koff[i] = r * KD + (c < L::KCHUNK ? c : 0) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < L::VPW; ++i) {
+        const int slot = (wave + 4 * i) * 64 + lane;
+        const int r = slot / L::VROW, c = slot % L::VROW;
+        voff[i] = r * (int)mp + (c < L::VCHUNK ? c : 0) * 8;   // D * mp < 2^31 (checked at launch)
     }
     const bf16* kbase = ws_k + ((int64_t)hk * mp + prow0) * KD;
     const bf16* vbase = ws_vt + (int64_t)hk * D * mp + prow0;
@@ -351,83 +371,52 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         for (int i = 0; i < L::KPW; ++i)
             if (wave + 4 * i < L::K_INSTR) lds_load16(src + koff[i], dst + (wave + 4 * i) * 1024);
     };
-    u32x4 vreg[L::VCH];
-    auto load_v = [&](int t) {
+    auto load_v = [&](int t, int buf) {
+        const bf16* src = vbase + t * kBN;
+        char* dst = vbufs + buf * L::V_BYTES;
 #pragma unroll
-        for (int c = 0; c < L::VCH; ++c) {
-            const int ch = tid + 256 * c;
-            const int dr = ch / (kBN / 8), cc = ch % (kBN / 8);
-            vreg[c] = *(const u32x4*)(vbase + (int64_t)dr * mp + t * kBN + cc * 8);
-        }
-    };
-    auto store_v = [&](int buf) {
-        bf16* vs = (bf16*)(vbufs + buf * L::V_BYTES);
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-        for (int c = 0; c < L::VCH; ++c) {
-            const int ch = tid + 256 * c;
-            bf16* dst = vs + (ch / (kBN / 8)) * L::VLD + (ch % (kBN / 8)) * 8;
-            ((u32x2*)dst)[0] = u32x2{vreg[c][0], vreg[c][1]};
-            ((u32x2*)dst)[1] = u32x2{vreg[c][2], vreg[c][3]};
-        }
+        for (int i = 0; i < L::VPW; ++i)
+            if (wave + 4 * i < L::V_INSTR) lds_load16(src + voff[i], dst + (wave + 4 * i) * 1024);
     };
 
-    f32x16 o[DB];
+    f32x16 o[QB][DB];
 #pragma unroll
-    for (int bb = 0; bb < DB; ++bb) o[bb] = f32x16{};
-    // Running offset m (log2 units), bf16-exact because Q' carries -m in its
-    // extra column 3 against a 1.0 in K', so the MFMA emits u = t - m directly.
-    float m_run = 0.0f, l_run = 0.0f;
+    for (int c = 0; c < QB; ++c)
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) o[c][bb] = f32x16{};
+    // Running offset m per query block (log2 units), bf16-exact because Q'
+    // carries -m in its extra column 3 against a 1.0 in K', so the MFMA emits
+    // u = t - m directly.
+    float m_run[QB], l_run[QB];
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
     // A tile whose row sum exceeds this had some p > ~2^57: refresh the offset.
     constexpr float kSumLimit = 0x1p62f;
 
-    auto set_offset = [&](float m) {
-        m_run = m;
-        if (half == 0) qf[KS][3] = (bf16)(-m);
+    auto set_offset = [&](int c, float m) {
+        m_run[c] = m;
+        if (half == 0) qf[c][KS][3] = (bf16)(-m);
     };
-    auto qk = [&](const bf16* ks, int blk, f32x16& acc) {
-        acc = f32x16{};
-        const bf16* kr = ks + (blk * 32 + il) * L::KLD + half * 8;
-#pragma unroll
-        for (int t = 0; t <= KS; ++t) {
-            const bf16x8 ka = *(const bf16x8*)(kr + t * 16);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[t], acc, 0, 0, 0);
-        }
-    };
-    // acc[r] <-> key j0 + blk*32 + (r/4)*8 + half*4 + r%4, query qi
-    auto mask = [&](f32x16& acc, int j0, int blk) {
+    // acc[r] <-> key j0 + blk*32 + (r/4)*8 + half*4 + r%4, query qv: one
+    // per-lane threshold against compile-time key offsets
+    auto mask = [&](f32x16& acc, int j0, int blk, int qv) {
+        const int thr = qv - j0 - blk * 32 - half * 4;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            if (j0 + blk * 32 + (r >> 2) * 8 + half * 4 + (r & 3) > qi) acc[r] = -INFINITY;
+            if ((r >> 2) * 8 + (r & 3) > thr) acc[r] = -INFINITY;
     };
-    auto expo = [&](const f32x16& acc, bf16x8* pb) {
+    auto expo = [&](const f32x16& acc, bf16x8* pbk) {
         float l = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(acc[r]);
+        for (int r = 0; r < 16; ++r) pbk[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(acc[r]);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const bf16x2 pr = {pb[u][e], pb[u][e + 1]};
+                const bf16x2 pr = {pbk[u][e], pbk[u][e + 1]};
                 l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
             }
         return l;
-    };
-    auto pv = [&](const bf16* vs, int blk, const bf16x8* pb) {
-#pragma unroll
-        for (int uu = 0; uu < 2; ++uu) {
-            const int u = blk * 2 + uu;
-#pragma unroll
-            for (int bb = 0; bb < DB; ++bb) {
-                const bf16* vr = vs + (bb * 32 + il) * L::VLD + u * 16 + half * 4;
-                const bf16x4 lo = *(const bf16x4*)vr;
-                const bf16x4 hi = *(const bf16x4*)(vr + 8);
-                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                o[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[uu], o[bb], 0, 0, 0);
-            }
-        }
     };
     auto row_max = [&](float mx) {
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
@@ -441,145 +430,206 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, a1[r]);
         return row_max(mx);
     };
-
-    // QK of one tile into two 32-key blocks; block 0's K' fragments are all
-    // read before its MFMAs, block 1's are read while block 0 multiplies.
-    auto qk_tile = [&](const bf16* ks, f32x16& a0, f32x16& a1) {
+    // QK of one 64-key tile for query block c only (prologue and refresh).
+    auto qk_block = [&](const bf16* ks, int c, f32x16& a0, f32x16& a1) {
         const bf16* kr0 = ks + il * L::KLD + half * 8;
         const bf16* kr1 = kr0 + 32 * L::KLD;
-        bf16x8 f0[KS + 1], f1[KS + 1];
-#pragma unroll
-        for (int t = 0; t <= KS; ++t) f0[t] = *(const bf16x8*)(kr0 + t * 16);
-#pragma unroll
-        for (int t = 0; t <= KS; ++t) f1[t] = *(const bf16x8*)(kr1 + t * 16);
         a0 = f32x16{};
         a1 = f32x16{};
 #pragma unroll
-        for (int t = 0; t <= KS; ++t) a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[t], qf[t], a0, 0, 0, 0);
-#pragma unroll
-        for (int t = 0; t <= KS; ++t) a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[t], qf[t], a1, 0, 0, 0);
-        // order: 9 reads, then (MFMA, read) x 9, then 9 MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, KS + 1, 2);
-#pragma unroll
         for (int t = 0; t <= KS; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+            const bf16x8 f0 = *(const bf16x8*)(kr0 + t * 16);
+            const bf16x8 f1 = *(const bf16x8*)(kr1 + t * 16);
+            a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, qf[c][t], a0, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1, qf[c][t], a1, 0, 0, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, KS + 1, 2);
     };
-    auto mask_tile = [&](f32x16& a0, f32x16& a1, int j0) {
-        mask(a0, j0, 0);
-        mask(a1, j0, 1);
-    };
-    // Rare: tile t's probabilities were huge.  Raise the offset to the tile's
-    // row max, rescale what is accumulated, recompute the tile's logits.
-    auto refresh = [&](const bf16* ks, int t, bf16x8* pb0, bf16x8* pb1, float& lt) {
+    // key block kb of tile j0/64 reaches query block c's diagonal
+    auto needs_mask = [&](int j0, int kb) { return j0 + kb * 32 + 31 > qb; };
+
+    bf16x8 pb[QB][2][2];   // bf16 probabilities of the tile whose P.V is next
+    // Rare: tile t's probabilities were huge for query block c.  Raise the
+    // offset to the tile's row max, rescale what is accumulated, recompute.
+    auto refresh = [&](const bf16* ks, int t, int c, float& lt) {
         f32x16 a0, a1;
-        qk_tile(ks, a0, a1);
-        if (t * kBN + kBN - 1 > qb) mask_tile(a0, a1, t * kBN);
-        const float target = bf16_ceil(m_run + fmaxf(tile_max(a0, a1), 0.0f));
-        const float delta = target - m_run;
+        qk_block(ks, c, a0, a1);
+        if (needs_mask(t * kBN, 0)) mask(a0, t * kBN, 0, qi[c]);
+        if (needs_mask(t * kBN, 1)) mask(a1, t * kBN, 1, qi[c]);
+        const float target = bf16_ceil(m_run[c] + fmaxf(tile_max(a0, a1), 0.0f));
+        const float delta = target - m_run[c];
         const float alpha = __builtin_amdgcn_exp2f(-delta);
-        l_run *= alpha;
+        l_run[c] *= alpha;
 #pragma unroll
         for (int bb = 0; bb < DB; ++bb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[bb][r] *= alpha;
+            for (int r = 0; r < 16; ++r) o[c][bb][r] *= alpha;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             a0[r] -= delta;
             a1[r] -= delta;
         }
-        set_offset(target);
-        lt = expo(a0, pb0) + expo(a1, pb1);
+        set_offset(c, target);
+        lt = expo(a0, pb[c][0]) + expo(a1, pb[c][1]);
     };
 
-    // ---- prologue: K'(0), K'(1), V^T(0); tile 0's logits set the offset
+    // ---- prologue: K'(0), K'(1), V^T(0); tile 0's logits set the offsets
     load_k(0, 0);
     if (n_kt > 1) load_k(1, 1);
-    load_v(0);
-    store_v(0);
+    load_v(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    bf16x8 pb0[2], pb1[2];   // bf16 probabilities of the tile whose P.V is next
-    {
+#pragma unroll
+    for (int c = 0; c < QB; ++c) {
         f32x16 s0, s1;
-        qk_tile((const bf16*)kbufs, s0, s1);
-        if (kBN - 1 > qb) mask_tile(s0, s1, 0);
-        const float m0 = bf16_ceil(tile_max(s0, s1));   // key 0 is always visible
+        qk_block((const bf16*)kbufs, c, s0, s1);
+        if (needs_mask(0, 0)) mask(s0, 0, 0, qi[c]);
+        if (needs_mask(0, 1)) mask(s1, 0, 1, qi[c]);
+        const float m0 = bf16_ceil(tile_max(s0, s1));   // key 0 is visible to every query
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             s0[r] -= m0;
             s1[r] -= m0;
         }
-        set_offset(m0);
-        l_run = expo(s0, pb0) + expo(s1, pb1);
+        set_offset(c, m0);
+        l_run[c] = expo(s0, pb[c][0]) + expo(s1, pb[c][1]);
     }
     __syncthreads();   // K' buffer 0 is reloaded in iteration 0
 
     for (int j = 0; j < n_kt; ++j) {
         if (j + 2 < n_kt) load_k(j + 2, j & 1);
-        if (j + 1 < n_kt) load_v(j + 1);
+        if (j + 1 < n_kt) load_v(j + 1, (j + 1) & 1);
         const bf16* ksn = (const bf16*)(kbufs + ((j + 1) & 1) * L::K_BYTES);   // K'(j+1); stale past the end
         const bf16* vs = (const bf16*)(vbufs + (j & 1) * L::V_BYTES);
         const bool more = j + 1 < n_kt;
+        const int j1 = (j + 1) * kBN;
 
-        // R1: QK of tile j+1
-        f32x16 n0, n1;
-        qk_tile(ksn, n0, n1);
-        if (more && (j + 1) * kBN + kBN - 1 > qb) mask_tile(n0, n1, (j + 1) * kBN);
+        // R1: QK of key block 0 of tile j+1
+        f32x16 n[QB][2];
+        const bf16* kr0 = ksn + il * L::KLD + half * 8;
+        const bf16* kr1 = kr0 + 32 * L::KLD;
+        {
+            bf16x8 f0[KS + 1];
+#pragma unroll
+            for (int t = 0; t <= KS; ++t) f0[t] = *(const bf16x8*)(kr0 + t * 16);
+#pragma unroll
+            for (int c = 0; c < QB; ++c) n[c][0] = f32x16{};
+#pragma unroll
+            for (int t = 0; t <= KS; ++t)
+#pragma unroll
+                for (int c = 0; c < QB; ++c)
+                    n[c][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[t], qf[c][t], n[c][0], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+            for (int t = 0; t <= KS; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x008, QB, 1);
+            }
+        }
+        if (more && needs_mask(j1, 0)) {
+#pragma unroll
+            for (int c = 0; c < QB; ++c) mask(n[c][0], j1, 0, qi[c]);
+        }
 
-        // R2: P.V of tile j || exponentials of tile j+1
-        bf16x8 nb0[2], nb1[2];
-        pv(vs, 0, pb0);
-        pv(vs, 1, pb1);
-        float ln = expo(n0, nb0) + expo(n1, nb1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+        // R2: QK of key block 1 || exponentials of key block 0
+        bf16x8 nb[QB][2][2];
+        float ln[QB];
+#pragma unroll
+        for (int c = 0; c < QB; ++c) n[c][1] = f32x16{};
+#pragma unroll
+        for (int t = 0; t <= KS; ++t) {
+            const bf16x8 f1 = *(const bf16x8*)(kr1 + t * 16);
+#pragma unroll
+            for (int c = 0; c < QB; ++c)
+                n[c][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1, qf[c][t], n[c][1], 0, 0, 0);
+        }
+#pragma unroll
+        for (int c = 0; c < QB; ++c) ln[c] = expo(n[c][0], nb[c][0]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 2);
+#pragma unroll
+        for (int t = 0; t <= KS; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+#pragma unroll
+            for (int c = 0; c < QB; ++c) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+                __builtin_amdgcn_sched_group_barrier(0x400, 2, 2);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 2);
+            }
+        }
+        if (more && needs_mask(j1, 1)) {
+#pragma unroll
+            for (int c = 0; c < QB; ++c) mask(n[c][1], j1, 1, qi[c]);
+        }
+
+        // R3: P.V of tile j || exponentials of key block 1
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb) {
+                // keys of this 16-key step, in the P^T operand's order (vt_col)
+                const bf16x8 a = *(const bf16x8*)(vs + (bb * 32 + il) * L::VLD + u * 16 + half * 8);
+#pragma unroll
+                for (int c = 0; c < QB; ++c)
+                    o[c][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c][u >> 1][u & 1], o[c][bb], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < QB; ++c) ln[c] += expo(n[c][1], nb[c][1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
 #pragma unroll
         for (int i = 0; i < 4 * DB; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-            __builtin_amdgcn_sched_group_barrier(0x400, 2, 1);
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
-        }
-        // unconditional uses keep the exponentials in R2 (past the end they are unused)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            pb0[u] = nb0[u];
-            pb1[u] = nb1[u];
+            for (int c = 0; c < QB; ++c) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+                __builtin_amdgcn_sched_group_barrier(0x400, 2 / QB, 3);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2 / QB, 3);
+            }
         }
-        if (more && __builtin_amdgcn_ballot_w64(!(ln <= kSumLimit))) refresh(ksn, j + 1, pb0, pb1, ln);
-        l_run = more ? l_run + ln : l_run;
-        if (more) store_v((j + 1) & 1);
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's K' loads have landed in LDS
+        // unconditional uses keep the exponentials in R2/R3 (past the end they are unused)
+#pragma unroll
+        for (int c = 0; c < QB; ++c)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) pb[c][kb][u] = nb[c][kb][u];
+#pragma unroll
+        for (int c = 0; c < QB; ++c) {
+            if (more && __builtin_amdgcn_ballot_w64(!(ln[c] <= kSumLimit))) refresh(ksn, j + 1, c, ln[c]);
+            l_run[c] = more ? l_run[c] + ln[c] : l_run[c];
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's K'/V^T loads have landed in LDS
         __syncthreads();
     }
 
     // ---- epilogue: combine the two halves' partial sums, normalise, store
-    float l_tot;
-    {
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    }
-    if (!qvalid) return;
-    const float inv = 1.0f / l_tot;
-    bf16* orow = out + ((int64_t)(cs0 + qi) * hq + h) * D;
 #pragma unroll
-    for (int bb = 0; bb < DB; ++bb) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            bf16x4 v4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v4[e] = (bf16)(o[bb][g * 4 + e] * inv);
-            *(bf16x4*)(orow + bb * 32 + g * 8 + half * 4) = v4;
+    for (int c = 0; c < QB; ++c) {
+        float l_tot;
+        {
+            auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[c]), __float_as_uint(l_run[c]), false,
+                                                       false);
+            l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         }
+        if (qi[c] >= ms) continue;
+        const float inv = 1.0f / l_tot;
+        bf16* orow = out + ((int64_t)(cs0 + qi[c]) * hq + h) * D;
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 v4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v4[e] = (bf16)(o[c][bb][g * 4 + e] * inv);
+                *(bf16x4*)(orow + bb * 32 + g * 8 + half * 4) = v4;
+            }
+        }
+        if (lse && half == 0) lse[(int64_t)h * m_tot + cs0 + qi[c]] = (m_run[c] + __log2f(l_tot)) * kLn2;
     }
-    if (lse && half == 0) lse[(int64_t)h * m_tot + cs0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
-template <int D, int HW>
+template <int D, int HW, int QB>
 int launch_fwd(const AttnArgs& a, hipStream_t st) {
-    constexpr int BMT = 32 * (4 / HW);
+    constexpr int BMT = 32 * QB * (4 / HW);
     const int grp = a.hq / a.hkv;
     const int n_qtiles = (a.max_kept_seqlen + BMT - 1) / BMT;
     const int n_hblk = a.hkv * (grp / HW);
@@ -588,43 +638,64 @@ int launch_fwd(const AttnArgs& a, hipStream_t st) {
     const size_t shm = (size_t)AttnLds<D>::SMEM;
     static bool attr_set = false;   // idempotent; racing first calls set the same value
     if (!attr_set) {
-        if (hipFuncSetAttribute((const void*)attn_fwd_kernel<D, HW>,
+        if (hipFuncSetAttribute((const void*)attn_fwd_kernel<D, HW, QB>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) != hipSuccess)
             return TG_ERR_HIP;
         attr_set = true;
     }
-    hipLaunchKernelGGL((attn_fwd_kernel<D, HW>), dim3((unsigned)nblk), dim3(256), shm, st, a.q,
+    hipLaunchKernelGGL((attn_fwd_kernel<D, HW, QB>), dim3((unsigned)nblk), dim3(256), shm, st, a.q,
                        a.q_stride, a.ws_k, a.ws_vt, a.ws_cs, (int)a.rope, a.gain, a.qk_scale_log2,
                        a.cu_kept, a.n_seqs, a.m_tot, a.mp, a.hq, grp, n_qtiles, n_hblk, a.out, a.lse);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 
+// One query block per wave: two query blocks (QB = 2) halve LDS traffic per
+// flop but need one wave per SIMD, and measured slower on every workload here
+// (128k kept 8448: 469 vs 421 us), so only QB = 1 is instantiated.
+template <int D, int HW>
+int launch_fwd_qb(const AttnArgs& a, hipStream_t st) {
+    return launch_fwd<D, HW, 1>(a, st);
+}
+
 template <int D>
-int launch_all(const AttnArgs& a, hipStream_t st) {
+int launch_prep(const AttnArgs& a, hipStream_t st) {
     RopeFreqs fr;
     for (int f = 0; f < 64; ++f) fr.inv_freq[f] = f < D / 2 ? exp2(-(2.0 * f / D) * a.rope_log2_base) : 0.0;
     // grid.y = kv heads, plus one extra row of groups for the padding fill
     hipLaunchKernelGGL(attn_prep_kernel<D>, dim3((unsigned)((a.m_tot + 63) / 64), a.hkv + 1), dim3(256), 0, st, a.k,
                        a.v, a.kv_stride, a.key_score, a.pos, a.cu_kept, a.n_seqs, a.m_tot, a.hkv, a.mp, fr,
                        (int)a.rope, a.ws_k, a.ws_vt, a.ws_cs);
-    if (hipGetLastError() != hipSuccess) return TG_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
+template <int D>
+int launch_fwd_grp(const AttnArgs& a, hipStream_t st) {
     const int grp = a.hq / a.hkv;
     switch (grp) {
-        case 1: return launch_fwd<D, 1>(a, st);
-        case 2: return launch_fwd<D, 2>(a, st);
+        case 1: return launch_fwd_qb<D, 1>(a, st);
+        case 2: return launch_fwd_qb<D, 2>(a, st);
         case 4:
-        case 8: return launch_fwd<D, 4>(a, st);
+        case 8: return launch_fwd_qb<D, 4>(a, st);
         default: return TG_ERR_UNSUPPORTED;
     }
 }
 
 }  // namespace
 
-int launch_attn(const AttnArgs& a, hipStream_t st) {
+int launch_attn_prep(const AttnArgs& a, hipStream_t st) {
     if (a.m_tot == 0) return TG_OK;
     switch (a.d) {
-        case 64: return launch_all<64>(a, st);
-        case 128: return launch_all<128>(a, st);
+        case 64: return launch_prep<64>(a, st);
+        case 128: return launch_prep<128>(a, st);
+        default: return TG_ERR_UNSUPPORTED;
+    }
+}
+
+int launch_attn_fwd(const AttnArgs& a, hipStream_t st) {
+    if (a.m_tot == 0) return TG_OK;
+    switch (a.d) {
+        case 64: return launch_fwd_grp<64>(a, st);
+        case 128: return launch_fwd_grp<128>(a, st);
         default: return TG_ERR_UNSUPPORTED;
     }
 }

@@ -61,7 +61,8 @@ struct AttnArgs {
 int64_t attn_padded_rows(int n_seqs, int64_t m_tot);
 size_t attn_workspace_layout(int n_seqs, int64_t m_tot, int hkv, int d, size_t* off_k,
                              size_t* off_vt, size_t* off_cs);
-int launch_attn(const AttnArgs& a, hipStream_t st);
+int launch_attn_prep(const AttnArgs& a, hipStream_t st);
+int launch_attn_fwd(const AttnArgs& a, hipStream_t st);
 
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
 // lane l writes LDS bytes [ldst + 16 l, ldst + 16 l + 16); ldst must be the
@@ -84,7 +85,15 @@ __device__ __forceinline__ int find_seq(const int* __restrict__ cu, int n, int64
 // First padded workspace row of kept sequence s: a multiple of 8 (16-byte
 // aligned bf16 rows for vector loads), and sequences never overlap.
 __device__ __host__ __forceinline__ int64_t padded_seq_start(int64_t cu_kept_s, int s) {
-    return (cu_kept_s + 8 * (int64_t)s + 7) & ~(int64_t)7;
+    return (cu_kept_s + 16 * (int64_t)s + 15) & ~(int64_t)15;
+}
+
+// Column of key row r in the V^T workspace: within every aligned group of 16
+// keys the middle two quads are swapped (keys 4-7 <-> 8-11), which is the key
+// order of the P^T operand taken straight from the S^T accumulators, so one
+// 16-B LDS read gives a lane its whole A-operand slice.  An involution.
+__device__ __host__ __forceinline__ int64_t vt_col(int64_t r) {
+    return (r & ~(int64_t)12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
 }  // namespace tg

@@ -151,6 +151,38 @@ def test_attn_validation(lib):
     assert a(m=0) == 0
 
 
+def test_attn_prepare_forward_validation(lib):
+    L = lib
+    need = L.tg_attn_workspace_bytes(1, 100, 8, 128)
+    p = lambda **kw: L.tg_attn_prepare(*[kw.get(k, v) for k, v in [
+        ("k", FAKE), ("v", FAKE), ("kvs", 1024), ("ks", FAKE), ("pos", FAKE), ("ck", FAKE), ("ns", 1),
+        ("m", 100), ("hkv", 8), ("d", 128), ("rb", 1e6), ("ws", FAKE), ("wsb", need), ("st", None)]])
+    assert p(rb=float("inf")) == 1
+    assert p(d=80) == 2
+    assert p(kvs=1000) == 1            # below Hkv * D
+    assert p(hkv=0) == 1
+    assert p(k=None) == 1
+    assert p(pos=None) == 1
+    assert p(v=MIS) == 1
+    assert p(ns=0) == 1                # kept tokens but no sequence
+    assert p(wsb=need - 1) == 3
+    assert p(m=0) == 0
+    f = lambda **kw: L.tg_attn_forward(*[kw.get(k, v) for k, v in [
+        ("q", FAKE), ("qs", 2048), ("g", FAKE), ("tau", 0.9), ("ck", FAKE), ("ns", 1), ("m", 100), ("mx", 100),
+        ("hq", 16), ("hkv", 8), ("d", 128), ("rb", 1e6), ("out", FAKE), ("lse", None), ("ws", FAKE),
+        ("wsb", need), ("st", None)]])
+    assert f(tau=0.0) == 1
+    assert f(hq=12) == 1
+    assert f(hq=24, qs=3072) == 2
+    assert f(qs=2040) == 1
+    assert f(mx=101) == 1
+    assert f(g=None) == 1
+    assert f(out=MIS) == 1
+    assert f(ws=ctypes.c_void_p(0x1010)) == 3
+    assert f(wsb=need - 1) == 3
+    assert f(m=0) == 0
+
+
 def test_library_has_no_undefined_internal_symbols(lib):
     """Every kernel stub must be defined: an undefined tg:: symbol only shows
     up when the library is loaded for real."""

@@ -317,6 +317,27 @@ def test_attention_bias_shift_invariance_gpu():
     np.testing.assert_allclose(l2 - l1, (c["gain"] * 0.75)[:, None] * np.ones_like(l1), atol=4e-3)
 
 
+def test_attention_prepare_forward_split():
+    """tg_attn_prepare + tg_attn_forward give exactly the one-shot result, and one
+    prepared kept-only cache serves a second query set."""
+    w = workloads.custom([1300, 600], [100, 40], [500, 260], n_q_heads=16, n_kv_heads=8, head_dim=128, seed=11)
+    _print_case("attn prepare/forward")
+    c = _attn_case(w)
+    ck = c["ck"]
+    maxlen = int(np.diff(ck).max())
+    q, k, v = _dev(c["q"]), _dev(c["k"]), _dev(c["v"])
+    sk, gain, pk, ckd = _dev(c["sk"]), _dev(c["gain"]), _i32(c["pk"]), _i32(ck)
+    o1, l1 = tg.tg_keybias_attn_prefill(q, k, v, sk, gain, c["tau"], pk, ckd, maxlen, rope_base=1e6)
+    ws = tg.tg_attn_prepare(k, v, sk, pk, ckd, rope_base=1e6)
+    o2, l2 = tg.tg_attn_forward(q, gain, c["tau"], ckd, maxlen, 8, ws, rope_base=1e6)
+    q2 = torch.flip(q, dims=[0]).contiguous()     # other queries, same keys
+    o3, l3 = tg.tg_attn_forward(q2, gain, c["tau"], ckd, maxlen, 8, ws, rope_base=1e6)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    c3 = dict(c, q=torch.flip(c["q"], dims=[0]).contiguous())
+    _check_attn(c3, o3.float().cpu().numpy(), l3.cpu().numpy(), 1e6, _sample_rows(ck, 16))
+
+
 # --------------------------------------------------------------- end to end ----
 @pytest.mark.parametrize("name", ["tiny", "16k"])
 def test_gated_layer_end_to_end(name):
