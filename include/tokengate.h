@@ -84,9 +84,9 @@ int tg_kept_counts(int32_t n_seqs, const int32_t* cu_seqlens_h, const int32_t* d
  *   b2            scalar fp32 output bias
  *   scores        [device, out] n_tokens fp32
  * Requirements: d_model % 8 == 0, x_row_stride >= d_model and % 8 == 0,
- * x and w1 16-byte aligned.  bf16: d_model % 32 == 0 and d_hid in {64, 128,
- * 192, 256}; fp32: 1 <= d_hid <= 1024 and d_model <= 2048 (TG_ERR_UNSUPPORTED
- * otherwise).  n_tokens == 0 is a no-op.
+ * x and w1 16-byte aligned.  bf16: d_model % 64 == 0, x_row_stride < 2^23
+ * and d_hid in {64, 128, 192, 256}; fp32: 1 <= d_hid <= 1024 and d_model <=
+ * 2048 (TG_ERR_UNSUPPORTED otherwise).  n_tokens == 0 is a no-op.
  */
 int tg_gate_score(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d_model,
                   int64_t x_row_stride, const void* w1, const float* b1, const float* w2,

@@ -85,7 +85,9 @@ def test_gate_validation(lib):
     assert g(x=MIS) == E
     assert g(w2=None) == E
     assert g(dh=100) == U
-    assert g(d=2056, stride=2056) == U           # bf16 path needs d_model % 32 == 0
+    assert g(d=2056, stride=2056) == U           # bf16 path needs d_model % 64 == 0
+    assert g(d=2080, stride=2080) == U
+    assert g(stride=1 << 23) == U                # 32-bit per-workgroup offsets
     assert g(dt=0, d=4096, stride=4096) == U     # fp32 path limit
     assert g(n=0) == 0                          # empty: no launch
 
