@@ -35,6 +35,7 @@ METRIC = "ms/gated layer + key-bias attn TFLOP/s (frac bf16 peak) at 32k/128k, 1
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PROFILE_PMC = os.path.join(ROOT, "profiles", "attn_fwd_128k_pmc.md")
+COPY_BYTES = 256 << 20         # --calibrate-copy: bytes read (and written) per copy
 
 
 def attn_flops(cu_kept, hq, d):
@@ -230,6 +231,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-sweep", action="store_true", help="skip the 32k budget sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run 3 plain device copies of 256 MiB, the reference kernel for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -239,6 +243,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     tg.load()
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     w = workloads.long128k()
     layer = Layer(w)
