@@ -28,15 +28,15 @@
 //     MFMA puts one query per lane (lane & 31): row statistics are per-lane
 //     scalars combined across the two 32-lane halves with one permlane32 swap;
 //     P^T feeds O^T = V^T.P^T straight from the S^T accumulators (8 consecutive
-//     accumulators are one 16-key MFMA step, V^T read in the matching order).
+//     accumulators are one 16-key MFMA step, V^T stored in the matching order).
 //     A running offset m (set from the first tile's exact row max, kept
 //     bf16-exact) rides in Q' column 3 against 1.0 in K' column 3, so the MFMA
 //     emits u = t - m and p = exp2(u) needs no max or subtraction.  Row sums
-//     use v_dot2 on the bf16 P that the P.V MFMA consumes; a block whose sum
+//     use v_dot2 on the bf16 P that the P.V MFMA consumes; a tile whose sum
 //     exceeds 2^62 (some p very large) takes a rare path that raises m to the
-//     block max and rescales O and l (the result is exact either way).  Each
-//     64-key tile is two 32-key blocks: block 0's exponentials overlap block
-//     1's QK MFMAs, and block 1's overlap the previous tile's P.V MFMAs.
+//     tile max and rescales O and l (the result is exact either way).  The
+//     loop is a three-stage pipeline (QK of tile j+2 || exponentials of tile
+//     j+1 || P.V of tile j), described at the kernel.
 //     All q heads of a KV group that fit in the workgroup share each K/V tile.
 //     Causality uses the kept order (positions increase within a sequence, so
 //     pos_j <= pos_i  <=>  j <= i).  Blocks are ordered head-fastest so that,
@@ -45,6 +45,7 @@
 #include <math.h>
 
 #include "tg_common.hpp"
+
 
 namespace tg {
 
@@ -71,6 +72,7 @@ size_t attn_workspace_layout(int n_seqs, int64_t m_tot, int hkv, int d, size_t* 
 namespace {
 
 constexpr int kBN = 64;     // keys per tile
+constexpr int kWaves = 4;   // waves per attention workgroup
 constexpr int kExtra = 16;  // extra K'/Q' columns carrying the key bias
 
 struct RopeFreqs {
@@ -236,47 +238,43 @@ struct AttnLds {
     static constexpr int K_INSTR = kBN * KROW / 64;    // load instructions per K' tile (19 / 11)
     static constexpr int V_INSTR = D * VROW / 64;      // ... per V^T tile (18 / 9)
     static_assert(kBN * KROW % 64 == 0 && D * VROW % 64 == 0, "tiles must be whole load instructions");
-    static constexpr int KPW = (K_INSTR + 3) / 4;      // per wave
-    static constexpr int VPW = (V_INSTR + 3) / 4;
     static constexpr int K_BYTES = kBN * KLD * 2;
     static constexpr int V_BYTES = D * VLD * 2;
     static constexpr int SMEM = 2 * K_BYTES + 2 * V_BYTES;   // two K' and two V^T buffers
 };
 
-// HW q heads per workgroup (1, 2 or 4); each of the 4 waves owns QW = 32 QB
-// query tokens of one head (QB blocks of 32); WB = 4 / HW waves per head;
-// BMT = QW WB tokens per workgroup.  Every K'/V^T fragment read from LDS feeds
-// QB MFMAs, so LDS traffic per flop falls as 1/QB; QB = 2 needs one wave per
-// SIMD (about 400 registers).
+// HW q heads per workgroup (1, 2 or 4); each of the NW waves owns 32 query
+// tokens of one head; WB = NW / HW waves per head; BMT = 32 WB tokens per
+// workgroup, all reading the same K'/V^T tiles.
 //
-// Software pipeline per wave, iteration j (K' runs one tile ahead of V^T):
-//   R1  QK MFMAs of tile j+1, key block 0 (K' fragments of block 1 read);
-//   R2  QK MFMAs of tile j+1, key block 1  ||  exponentials of key block 0;
-//   R3  P.V MFMAs of tile j                ||  exponentials of key block 1;
-//       (rare) offset refresh if tile j+1 produced a huge probability;
-//   K'(j+2) goes straight to LDS and V^T(j+1) through registers meanwhile.
-// Masks are applied between the regions on the (at most two) tiles that reach
-// a wave's diagonal; tiles wholly past it are masked to zero probability.
-template <int D, int HW, int QB>
-__global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_fwd_kernel(
+// Three-stage software pipeline.  Iteration j is one scheduling region of
+// 34 MFMAs (D = 128): the P.V MFMAs of tile j, then the QK MFMAs of tile j+2,
+// with the 32 exponentials of tile j+1 (whose logits are already in
+// registers) spread over them, one pair per MFMA or two.  No MFMA waits on an
+// exponential of the same iteration and no exponential waits on an MFMA.
+// Every operand fragment is read from LDS four MFMAs ahead of its use; empty
+// volatile asm statements pin the reads, the MFMAs and the exponentials to
+// their slots (the scheduler would otherwise pull each MFMA up against its
+// read, exposing the LDS latency on every MFMA).  Steps run in pairs with the
+// two sets of logits / probabilities swapped, so nothing is copied.
+template <int D, int HW, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
     const bf16* __restrict__ q, int64_t q_stride, const bf16* __restrict__ ws_k,
     const bf16* __restrict__ ws_vt, const float2* __restrict__ ws_cs, int rope,
     const float* __restrict__ gain, float qk_scale_log2, const int* __restrict__ cu_kept, int n_seqs,
     int64_t m_tot, int64_t mp, int hq, int grp, int n_qtiles, int n_hblk, bf16* __restrict__ out,
     float* __restrict__ lse) {
     using L = AttnLds<D>;
-    constexpr int WB = 4 / HW;
-    constexpr int QW = 32 * QB;
-    constexpr int BMT = QW * WB;
-    constexpr int KS = D / 16;      // MFMA k-steps over head_dim (+1 for the extra columns)
+    constexpr int WB = NW / HW;
+    constexpr int BMT = 32 * WB;
+    constexpr int KS = D / 16;
     constexpr int KD = L::KD;
-    constexpr int DB = D / 32;      // 32-row blocks of O^T
+    constexpr int DB = D / 32;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int il = lane & 31, half = lane >> 5;
 
-    // head-fastest block order; largest query tiles first
     const int b = blockIdx.x;
     const int hidx = b % n_hblk;
     const int rest = b / n_hblk;
@@ -290,20 +288,16 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_fwd_kernel(
     const int nsub = grp / HW;
     const int hk = hidx / nsub;
     const int h = hk * grp + (hidx % nsub) * HW + wave / WB;
-    const int qb = q0 + (wave % WB) * QW;    // first query (sequence-local) of this wave
-    int qi[QB];                              // this lane's query in block c
-#pragma unroll
-    for (int c = 0; c < QB; ++c) qi[c] = qb + 32 * c + il;
+    const int qb = q0 + (wave % WB) * 32;
+    const int qi = qb + il;
+    const bool qvalid = qi < ms;
     const int64_t prow0 = padded_seq_start(cs0, s);
     const int kend = min(ms, q0 + BMT);
     const int n_kt = (kend + kBN - 1) / kBN;
 
-    // ---- Q' fragments (B operand of S^T = K' Q'^T): rotated, scaled, + extra columns
-    bf16x8 qf[QB][KS + 1];
-#pragma unroll
-    for (int c = 0; c < QB; ++c) {
-        const bool qvalid = qi[c] < ms;
-        const bf16* qrow = q + (int64_t)(cs0 + (qvalid ? qi[c] : 0)) * q_stride + (int64_t)h * D;
+    bf16x8 qf[KS + 1];
+    {
+        const bf16* qrow = q + (int64_t)(cs0 + (qvalid ? qi : 0)) * q_stride + (int64_t)h * D;
         float xf[KS][8];
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
@@ -312,7 +306,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_fwd_kernel(
             for (int e = 0; e < 8; ++e) xf[t][e] = (float)raw[e];
         }
         if (rope && qvalid) {
-            const float2* csr = ws_cs + (int64_t)(cs0 + qi[c]) * (D / 2);
+            const float2* csr = ws_cs + (int64_t)(cs0 + qi) * (D / 2);
 #pragma unroll
             for (int t = 0; t < KS / 2; ++t) {
                 const float4* c4 = (const float4*)(csr + t * 16 + half * 8);
@@ -333,77 +327,81 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_fwd_kernel(
 #pragma unroll
         for (int t = 0; t < KS; ++t)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qf[c][t][e] = (bf16)(xf[t][e] * qk_scale_log2);
-        qf[c][KS] = bf16x8{};
+            for (int e = 0; e < 8; ++e) qf[t][e] = (bf16)(xf[t][e] * qk_scale_log2);
+        qf[KS] = bf16x8{};
         if (half == 0) {
             bf16 gh, glo;
             split_bf16(gain[h] * kLog2e, &gh, &glo);
-            qf[c][KS][0] = gh;
-            qf[c][KS][1] = gh;
-            qf[c][KS][2] = glo;
+            qf[KS][0] = gh;
+            qf[KS][1] = gh;
+            qf[KS][2] = glo;
         }
     }
 
-    // ---- LDS-direct tile loads.  Load instruction g of a tile is issued by
-    // wave g % 4 and copies one 16-B chunk per lane; the per-lane source
-    // offsets are fixed for the whole kernel.
-    int koff[L::KPW], voff[L::VPW];
+    constexpr int KPW = (L::K_INSTR + NW - 1) / NW;
+    constexpr int VPW = (L::V_INSTR + NW - 1) / NW;
+    uint32_t koff[KPW], voff[VPW];   // element offsets, then bytes
 #pragma unroll
-    for (int i = 0; i < L::KPW; ++i) {
-        const int slot = (wave + 4 * i) * 64 + lane;
+    for (int i = 0; i < KPW; ++i) {
+        const int slot = (wave + NW * i) * 64 + lane;
         const int r = slot / L::KROW, c = slot % L::KROW;
         koff[i] = r * KD + (c < L::KCHUNK ? c : 0) * 8;
     }
 #pragma unroll
-    for (int i = 0; i < L::VPW; ++i) {
-        const int slot = (wave + 4 * i) * 64 + lane;
+    for (int i = 0; i < VPW; ++i) {
+        const int slot = (wave + NW * i) * 64 + lane;
         const int r = slot / L::VROW, c = slot % L::VROW;
-        voff[i] = r * (int)mp + (c < L::VCHUNK ? c : 0) * 8;   // D * mp < 2^31 (checked at launch)
+        voff[i] = (uint32_t)r * (uint32_t)mp + (c < L::VCHUNK ? c : 0) * 8;
     }
-    const bf16* kbase = ws_k + ((int64_t)hk * mp + prow0) * KD;
-    const bf16* vbase = ws_vt + (int64_t)hk * D * mp + prow0;
+    // this head's K' rows and V^T columns from the sequence start, as buffer
+    // resources: 32-bit per-lane offsets, the tile offset in a scalar register
+    const __amdgpu_buffer_rsrc_t krs =
+        make_rsrc(ws_k + ((int64_t)hk * mp + prow0) * KD, (uint32_t)((mp - prow0) * KD * 2));
+    const __amdgpu_buffer_rsrc_t vrs =
+        make_rsrc(ws_vt + (int64_t)hk * D * mp + prow0, (uint32_t)(((int64_t)D * mp - prow0) * 2));
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) koff[i] *= 2;   // bytes
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) voff[i] *= 2;
     char* const kbufs = smem;
     char* const vbufs = smem + 2 * L::K_BYTES;
     auto load_k = [&](int t, int buf) {
-        const bf16* src = kbase + (int64_t)t * kBN * KD;
+        const uint32_t so = (uint32_t)t * (kBN * KD * 2);
         char* dst = kbufs + buf * L::K_BYTES;
 #pragma unroll
-        for (int i = 0; i < L::KPW; ++i)
-            if (wave + 4 * i < L::K_INSTR) lds_load16(src + koff[i], dst + (wave + 4 * i) * 1024);
+        for (int i = 0; i < KPW; ++i)
+            if (wave + NW * i < L::K_INSTR) lds_load16_buf(krs, koff[i], so, dst + (wave + NW * i) * 1024);
     };
     auto load_v = [&](int t, int buf) {
-        const bf16* src = vbase + t * kBN;
+        const uint32_t so = (uint32_t)t * (kBN * 2);
         char* dst = vbufs + buf * L::V_BYTES;
 #pragma unroll
-        for (int i = 0; i < L::VPW; ++i)
-            if (wave + 4 * i < L::V_INSTR) lds_load16(src + voff[i], dst + (wave + 4 * i) * 1024);
+        for (int i = 0; i < VPW; ++i)
+            if (wave + NW * i < L::V_INSTR) lds_load16_buf(vrs, voff[i], so, dst + (wave + NW * i) * 1024);
     };
 
-    f32x16 o[QB][DB];
+    f32x16 o[DB];
 #pragma unroll
-    for (int c = 0; c < QB; ++c)
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) o[c][bb] = f32x16{};
-    // Running offset m per query block (log2 units), bf16-exact because Q'
-    // carries -m in its extra column 3 against a 1.0 in K', so the MFMA emits
-    // u = t - m directly.
-    float m_run[QB], l_run[QB];
+    for (int bb = 0; bb < DB; ++bb) o[bb] = f32x16{};
+    float m_run = 0.0f, l_run = 0.0f;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-    // A tile whose row sum exceeds this had some p > ~2^57: refresh the offset.
     constexpr float kSumLimit = 0x1p62f;
 
-    auto set_offset = [&](int c, float m) {
-        m_run[c] = m;
-        if (half == 0) qf[c][KS][3] = (bf16)(-m);
+    auto set_offset = [&](float m) {
+        m_run = m;
+        if (half == 0) qf[KS][3] = (bf16)(-m);
     };
-    // acc[r] <-> key j0 + blk*32 + (r/4)*8 + half*4 + r%4, query qv: one
-    // per-lane threshold against compile-time key offsets
-    auto mask = [&](f32x16& acc, int j0, int blk, int qv) {
-        const int thr = qv - j0 - blk * 32 - half * 4;
+    auto mask = [&](f32x16& acc, int j0, int blk) {
+        const int thr = qi - j0 - blk * 32 - half * 4;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             if ((r >> 2) * 8 + (r & 3) > thr) acc[r] = -INFINITY;
+    };
+    auto needs_mask = [&](int j0) { return j0 + kBN - 1 > qb; };
+    auto mask_tile = [&](f32x16& a0, f32x16& a1, int j0) {
+        mask(a0, j0, 0);
+        mask(a1, j0, 1);
     };
     auto expo = [&](const f32x16& acc, bf16x8* pbk) {
         float l = 0.0f;
@@ -418,20 +416,16 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_fwd_kernel(
             }
         return l;
     };
-    auto row_max = [&](float mx) {
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    };
     auto tile_max = [&](const f32x16& a0, const f32x16& a1) {
         float mx = a0[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, a0[r]);
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, a1[r]);
-        return row_max(mx);
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     };
-    // QK of one 64-key tile for query block c only (prologue and refresh).
-    auto qk_block = [&](const bf16* ks, int c, f32x16& a0, f32x16& a1) {
+    auto qk_tile = [&](const bf16* ks, f32x16& a0, f32x16& a1) {
         const bf16* kr0 = ks + il * L::KLD + half * 8;
         const bf16* kr1 = kr0 + 32 * L::KLD;
         a0 = f32x16{};
@@ -440,221 +434,189 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_fwd_kernel(
         for (int t = 0; t <= KS; ++t) {
             const bf16x8 f0 = *(const bf16x8*)(kr0 + t * 16);
             const bf16x8 f1 = *(const bf16x8*)(kr1 + t * 16);
-            a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, qf[c][t], a0, 0, 0, 0);
-            a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1, qf[c][t], a1, 0, 0, 0);
+            a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, qf[t], a0, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1, qf[t], a1, 0, 0, 0);
         }
     };
-    // key block kb of tile j0/64 reaches query block c's diagonal
-    auto needs_mask = [&](int j0, int kb) { return j0 + kb * 32 + 31 > qb; };
 
-    bf16x8 pb[QB][2][2];   // bf16 probabilities of the tile whose P.V is next
-    // Rare: tile t's probabilities were huge for query block c.  Raise the
-    // offset to the tile's row max, rescale what is accumulated, recompute.
-    auto refresh = [&](const bf16* ks, int t, int c, float& lt) {
-        f32x16 a0, a1;
-        qk_block(ks, c, a0, a1);
-        if (needs_mask(t * kBN, 0)) mask(a0, t * kBN, 0, qi[c]);
-        if (needs_mask(t * kBN, 1)) mask(a1, t * kBN, 1, qi[c]);
-        const float target = bf16_ceil(m_run[c] + fmaxf(tile_max(a0, a1), 0.0f));
-        const float delta = target - m_run[c];
-        const float alpha = __builtin_amdgcn_exp2f(-delta);
-        l_run[c] *= alpha;
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[c][bb][r] *= alpha;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            a0[r] -= delta;
-            a1[r] -= delta;
-        }
-        set_offset(c, target);
-        lt = expo(a0, pb[c][0]) + expo(a1, pb[c][1]);
-    };
-
-    // ---- prologue: K'(0), K'(1), V^T(0); tile 0's logits set the offsets
+    // ---- prologue: S(0) sets the offset and gives P(0); S(1) is left in registers
     load_k(0, 0);
     if (n_kt > 1) load_k(1, 1);
     load_v(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-#pragma unroll
-    for (int c = 0; c < QB; ++c) {
+    bf16x8 pb[2][2];
+    f32x16 s1a, s1b;   // logits of the tile whose exponentials are next
+    {
         f32x16 s0, s1;
-        qk_block((const bf16*)kbufs, c, s0, s1);
-        if (needs_mask(0, 0)) mask(s0, 0, 0, qi[c]);
-        if (needs_mask(0, 1)) mask(s1, 0, 1, qi[c]);
+        qk_tile((const bf16*)kbufs, s0, s1);
+        if (needs_mask(0)) mask_tile(s0, s1, 0);
         const float m0 = bf16_ceil(tile_max(s0, s1));   // key 0 is visible to every query
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             s0[r] -= m0;
             s1[r] -= m0;
         }
-        set_offset(c, m0);
-        l_run[c] = expo(s0, pb[c][0]) + expo(s1, pb[c][1]);
+        set_offset(m0);
+        l_run = expo(s0, pb[0]) + expo(s1, pb[1]);
+        qk_tile((const bf16*)(kbufs + L::K_BYTES), s1a, s1b);   // stale if n_kt == 1 (unused)
+        if (n_kt > 1 && needs_mask(kBN)) mask_tile(s1a, s1b, kBN);
     }
-    __syncthreads();   // K' buffer 0 is reloaded in iteration 0
+    __syncthreads();   // every wave is done with K'(0) before K'(2) replaces it
+    if (n_kt > 2) load_k(2, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
-    for (int j = 0; j < n_kt; ++j) {
-        if (j + 2 < n_kt) load_k(j + 2, j & 1);
+    // One tile step.  (sa, sb, pc) hold the logits of tile j+1 and the
+    // probabilities of tile j; the step writes the logits of tile j+2 into
+    // (ta, tb) and the probabilities of tile j+1 into pn.  The loop below runs
+    // steps in pairs with the two sets swapped, so nothing is copied.
+    auto step = [&](int j, f32x16& sa, f32x16& sb, bf16x8 (&pc)[2][2], f32x16& ta, f32x16& tb,
+                    bf16x8 (&pn)[2][2]) {
+        if (j + 3 < n_kt) load_k(j + 3, (j + 1) & 1);
         if (j + 1 < n_kt) load_v(j + 1, (j + 1) & 1);
-        const bf16* ksn = (const bf16*)(kbufs + ((j + 1) & 1) * L::K_BYTES);   // K'(j+1); stale past the end
+        const bf16* ks2 = (const bf16*)(kbufs + (j & 1) * L::K_BYTES);   // K'(j+2); stale past the end
         const bf16* vs = (const bf16*)(vbufs + (j & 1) * L::V_BYTES);
-        const bool more = j + 1 < n_kt;
-        const int j1 = (j + 1) * kBN;
-
-        // R1: QK of key block 0 of tile j+1
-        f32x16 n[QB][2];
-        const bf16* kr0 = ksn + il * L::KLD + half * 8;
+        const bool more1 = j + 1 < n_kt, more2 = j + 2 < n_kt;
+        const int j2 = (j + 2) * kBN;
+        const bf16* kr0 = ks2 + il * L::KLD + half * 8;
         const bf16* kr1 = kr0 + 32 * L::KLD;
-        {
-            bf16x8 f0[KS + 1];
-#pragma unroll
-            for (int t = 0; t <= KS; ++t) f0[t] = *(const bf16x8*)(kr0 + t * 16);
-#pragma unroll
-            for (int c = 0; c < QB; ++c) n[c][0] = f32x16{};
-#pragma unroll
-            for (int t = 0; t <= KS; ++t)
-#pragma unroll
-                for (int c = 0; c < QB; ++c)
-                    n[c][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[t], qf[c][t], n[c][0], 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-            for (int t = 0; t <= KS; ++t) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-                __builtin_amdgcn_sched_group_barrier(0x008, QB, 1);
-            }
-        }
-        if (more && needs_mask(j1, 0)) {
-#pragma unroll
-            for (int c = 0; c < QB; ++c) mask(n[c][0], j1, 0, qi[c]);
-        }
 
-        // R2: QK of key block 1 || exponentials of key block 0
-        bf16x8 nb[QB][2][2];
-        float ln[QB];
+        // MFMA i < 4 DB: P.V k-step i / DB of O^T block i % DB (with the
+        // exponentials of key block 0 of tile j+1); then QK k-step (i - 4 DB)/2
+        // of key block (i - 4 DB) % 2 of tile j+2 (with those of key block 1).
+        constexpr int NP = 4 * DB, NI = NP + 2 * (KS + 1), PF = 4;
+        auto frag = [&](int i) -> bf16x8 {
+            if (i < NP) return *(const bf16x8*)(vs + ((i % DB) * 32 + il) * L::VLD + (i / DB) * 16 + half * 8);
+            const int k = i - NP;
+            return *(const bf16x8*)(((k & 1) ? kr1 : kr0) + (k >> 1) * 16);
+        };
+        bf16x8 ring[PF];
 #pragma unroll
-        for (int c = 0; c < QB; ++c) n[c][1] = f32x16{};
+        for (int i = 0; i < PF; ++i) ring[i] = frag(i);
+        ta = f32x16{};
+        tb = f32x16{};
+        float lsum[2] = {0.0f, 0.0f};
 #pragma unroll
-        for (int t = 0; t <= KS; ++t) {
-            const bf16x8 f1 = *(const bf16x8*)(kr1 + t * 16);
+        for (int i = 0; i < NI; ++i) {
+            const bf16x8 a = ring[i % PF];
+            if (i + PF < NI) ring[i % PF] = frag(i + PF);
+            // The memory clobber keeps the read above from sinking toward its
+            // use; re-defining this MFMA's register operand here keeps the
+            // MFMA from rising toward its read.  Together they hold every
+            // LDS read PF MFMAs ahead of the MFMA that consumes it.
+            __asm__ volatile("" ::: "memory");
+            if (i < NP) {
+                const int u = i / DB;
+                __asm__ volatile("" : "+v"(pc[u >> 1][u & 1]));
+                o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pc[u >> 1][u & 1], o[i % DB], 0, 0, 0);
+            } else {
+                const int k = i - NP;
+                __asm__ volatile("" : "+v"(qf[k >> 1]));
+                if (k & 1) tb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k >> 1], tb, 0, 0, 0);
+                else ta = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k >> 1], ta, 0, 0, 0);
+            }
+            // exponentials of tile j+1: 16 pairs spread evenly over the NI
+            // MFMAs (key block 0 with the P.V ones, block 1 with the QK ones),
+            // packed to bf16 and summed a pair at a time
 #pragma unroll
-            for (int c = 0; c < QB; ++c)
-                n[c][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1, qf[c][t], n[c][1], 0, 0, 0);
-        }
-#pragma unroll
-        for (int c = 0; c < QB; ++c) ln[c] = expo(n[c][0], nb[c][0]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 2);
-#pragma unroll
-        for (int t = 0; t <= KS; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
-#pragma unroll
-            for (int c = 0; c < QB; ++c) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-                __builtin_amdgcn_sched_group_barrier(0x400, 2, 2);
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 2);
+            for (int pr_i = 0; pr_i < 16; ++pr_i) {
+                if (pr_i * NI / 16 != i) continue;
+                const int kb = pr_i >> 3, r = (pr_i & 7) * 2;
+                // not before this step's MFMA (these logits are dead after this)
+                if (kb) __asm__ volatile("" : "+v"(sb[r]), "+v"(sb[r + 1]));
+                else __asm__ volatile("" : "+v"(sa[r]), "+v"(sa[r + 1]));
+                const float x0 = kb ? sb[r] : sa[r], x1 = kb ? sb[r + 1] : sa[r + 1];
+                const float e0 = __builtin_amdgcn_exp2f(x0);
+                const float e1 = __builtin_amdgcn_exp2f(x1);
+                pn[kb][r >> 3][r & 7] = (bf16)e0;
+                pn[kb][r >> 3][(r & 7) + 1] = (bf16)e1;
+                const bf16x2 pr = {pn[kb][r >> 3][r & 7], pn[kb][r >> 3][(r & 7) + 1]};
+                lsum[kb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[kb], false);
+                __asm__ volatile("" ::"v"(lsum[kb]));          // and done before the next step
             }
         }
-        if (more && needs_mask(j1, 1)) {
+        float ln = lsum[0] + lsum[1];
+        // the refresh test consumes the exponentials before any branch
+        if (more1 && __builtin_amdgcn_ballot_w64(!(ln <= kSumLimit))) {
+            // Rare: tile j+1's probabilities were huge.  Raise the offset to its
+            // row max, rescale what is accumulated, redo its exponentials; tile
+            // j+2's logits used the old offset and shift with it.  (The empty
+            // volatile asm keeps this block a branch: flattened into selects it
+            // would cost its whole arithmetic on every tile.)
+            __asm__ volatile("");
+            const float target = bf16_ceil(m_run + fmaxf(tile_max(sa, sb), 0.0f));
+            const float delta = target - m_run;
+            const float alpha = __builtin_amdgcn_exp2f(-delta);
+            l_run *= alpha;
 #pragma unroll
-            for (int c = 0; c < QB; ++c) mask(n[c][1], j1, 1, qi[c]);
-        }
-
-        // R3: P.V of tile j || exponentials of key block 1
+            for (int bb = 0; bb < DB; ++bb)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+                for (int r = 0; r < 16; ++r) o[bb][r] *= alpha;
 #pragma unroll
-            for (int bb = 0; bb < DB; ++bb) {
-                // keys of this 16-key step, in the P^T operand's order (vt_col)
-                const bf16x8 a = *(const bf16x8*)(vs + (bb * 32 + il) * L::VLD + u * 16 + half * 8);
-#pragma unroll
-                for (int c = 0; c < QB; ++c)
-                    o[c][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c][u >> 1][u & 1], o[c][bb], 0, 0, 0);
+            for (int r = 0; r < 16; ++r) {
+                sa[r] -= delta;
+                sb[r] -= delta;
+                ta[r] -= delta;
+                tb[r] -= delta;
             }
+            set_offset(target);
+            ln = expo(sa, pn[0]) + expo(sb, pn[1]);
         }
-#pragma unroll
-        for (int c = 0; c < QB; ++c) ln[c] += expo(n[c][1], nb[c][1]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
-#pragma unroll
-        for (int i = 0; i < 4 * DB; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
-#pragma unroll
-            for (int c = 0; c < QB; ++c) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
-                __builtin_amdgcn_sched_group_barrier(0x400, 2 / QB, 3);
-                __builtin_amdgcn_sched_group_barrier(0x002, 2 / QB, 3);
-            }
-        }
-        // unconditional uses keep the exponentials in R2/R3 (past the end they are unused)
-#pragma unroll
-        for (int c = 0; c < QB; ++c)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) pb[c][kb][u] = nb[c][kb][u];
-#pragma unroll
-        for (int c = 0; c < QB; ++c) {
-            if (more && __builtin_amdgcn_ballot_w64(!(ln[c] <= kSumLimit))) refresh(ksn, j + 1, c, ln[c]);
-            l_run[c] = more ? l_run[c] + ln[c] : l_run[c];
-        }
+        l_run = more1 ? l_run + ln : l_run;
+        if (more2 && needs_mask(j2)) mask_tile(ta, tb, j2);
         __builtin_amdgcn_s_waitcnt(0);   // this wave's K'/V^T loads have landed in LDS
         __syncthreads();
+    };
+    f32x16 s2a, s2b;
+    bf16x8 pb2[2][2];
+    for (int j = 0; j < n_kt; j += 2) {
+        step(j, s1a, s1b, pb, s2a, s2b, pb2);
+        if (j + 1 < n_kt) step(j + 1, s2a, s2b, pb2, s1a, s1b, pb);
     }
 
-    // ---- epilogue: combine the two halves' partial sums, normalise, store
-#pragma unroll
-    for (int c = 0; c < QB; ++c) {
-        float l_tot;
-        {
-            auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[c]), __float_as_uint(l_run[c]), false,
-                                                       false);
-            l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        }
-        if (qi[c] >= ms) continue;
-        const float inv = 1.0f / l_tot;
-        bf16* orow = out + ((int64_t)(cs0 + qi[c]) * hq + h) * D;
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                bf16x4 v4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v4[e] = (bf16)(o[c][bb][g * 4 + e] * inv);
-                *(bf16x4*)(orow + bb * 32 + g * 8 + half * 4) = v4;
-            }
-        }
-        if (lse && half == 0) lse[(int64_t)h * m_tot + cs0 + qi[c]] = (m_run[c] + __log2f(l_tot)) * kLn2;
+    float l_tot;
+    {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
+    if (!qvalid) return;
+    const float inv = 1.0f / l_tot;
+    bf16* orow = out + ((int64_t)(cs0 + qi) * hq + h) * D;
+#pragma unroll
+    for (int bb = 0; bb < DB; ++bb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            bf16x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = (bf16)(o[bb][g * 4 + e] * inv);
+            *(bf16x4*)(orow + bb * 32 + g * 8 + half * 4) = v4;
+        }
+    }
+    if (lse && half == 0) lse[(int64_t)h * m_tot + cs0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
-template <int D, int HW, int QB>
+template <int D, int HW, int NW>
 int launch_fwd(const AttnArgs& a, hipStream_t st) {
-    constexpr int BMT = 32 * QB * (4 / HW);
+    constexpr int BMT = 32 * (NW / HW);
     const int grp = a.hq / a.hkv;
     const int n_qtiles = (a.max_kept_seqlen + BMT - 1) / BMT;
     const int n_hblk = a.hkv * (grp / HW);
     const int64_t nblk = (int64_t)n_qtiles * a.n_seqs * n_hblk;
-    if (nblk > 0x7fffffff || (int64_t)D * a.mp >= ((int64_t)1 << 31)) return TG_ERR_UNSUPPORTED;
+    // buffer offsets into one head's K' rows ((D+16)*2 B each) stay 32-bit
+    if (nblk > 0x7fffffff || (int64_t)(D + kExtra) * 2 * a.mp >= ((int64_t)1 << 32)) return TG_ERR_UNSUPPORTED;
     const size_t shm = (size_t)AttnLds<D>::SMEM;
-    static bool attr_set = false;   // idempotent; racing first calls set the same value
+    static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute((const void*)attn_fwd_kernel<D, HW, QB>,
+        if (hipFuncSetAttribute((const void*)attn_fwd_kernel<D, HW, NW>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) != hipSuccess)
             return TG_ERR_HIP;
         attr_set = true;
     }
-    hipLaunchKernelGGL((attn_fwd_kernel<D, HW, QB>), dim3((unsigned)nblk), dim3(256), shm, st, a.q,
+    hipLaunchKernelGGL((attn_fwd_kernel<D, HW, NW>), dim3((unsigned)nblk), dim3(NW * 64), shm, st, a.q,
                        a.q_stride, a.ws_k, a.ws_vt, a.ws_cs, (int)a.rope, a.gain, a.qk_scale_log2,
                        a.cu_kept, a.n_seqs, a.m_tot, a.mp, a.hq, grp, n_qtiles, n_hblk, a.out, a.lse);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
-}
-
-// One query block per wave: two query blocks (QB = 2) halve LDS traffic per
-// flop but need one wave per SIMD, and measured slower on every workload here
-// (128k kept 8448: 469 vs 421 us), so only QB = 1 is instantiated.
-template <int D, int HW>
-int launch_fwd_qb(const AttnArgs& a, hipStream_t st) {
-    return launch_fwd<D, HW, 1>(a, st);
 }
 
 template <int D>
@@ -672,10 +634,10 @@ template <int D>
 int launch_fwd_grp(const AttnArgs& a, hipStream_t st) {
     const int grp = a.hq / a.hkv;
     switch (grp) {
-        case 1: return launch_fwd_qb<D, 1>(a, st);
-        case 2: return launch_fwd_qb<D, 2>(a, st);
+        case 1: return launch_fwd<D, 1, kWaves>(a, st);
+        case 2: return launch_fwd<D, 2, kWaves>(a, st);
         case 4:
-        case 8: return launch_fwd_qb<D, 4>(a, st);
+        case 8: return launch_fwd<D, 4, kWaves>(a, st);
         default: return TG_ERR_UNSUPPORTED;
     }
 }
