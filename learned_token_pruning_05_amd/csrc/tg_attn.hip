@@ -104,7 +104,8 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
     bf16* __restrict__ ws_vt, float2* __restrict__ ws_cs) {
     constexpr int HALF = D / 2, KD = D + kExtra, FPW = HALF / 4, VLD = D + 2;
     __shared__ __attribute__((aligned(16))) bf16 vs[64 * VLD];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = blockIdx.y;
     if (h == hkv) {
         // Zero the padding rows between sequences (and after the last one), so
@@ -272,7 +273,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
     constexpr int DB = D / 32;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index in a scalar register: every test on it is a scalar branch
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int il = lane & 31, half = lane >> 5;
 
     const int b = blockIdx.x;

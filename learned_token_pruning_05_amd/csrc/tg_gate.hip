@@ -31,8 +31,9 @@ constexpr int kRowChunks = Slab<kBK>::ROW_CHUNKS;
 constexpr int kLdk = Slab<kBK>::LDK;
 
 __device__ __forceinline__ float silu_f32(float a) {
-    // a * sigmoid(a); exp2 of a finite argument, saturating correctly at +-inf.
-    return a / (1.0f + __builtin_amdgcn_exp2f(-a * kLog2e));
+    // a * sigmoid(a) with the hardware reciprocal (1 ulp): a / (1 + 2^(-a log2 e)).
+    // For a -> -inf the denominator overflows to +inf and the product is -0.
+    return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * kLog2e));
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
@@ -73,8 +74,6 @@ __global__ __launch_bounds__(BM * 2, 1) void gate_bf16_kernel(
     constexpr int NH = 64 * CB;
     constexpr int XI = BM * kRowChunks / 64;           // load instructions per X slab
     constexpr int WI = NH * kRowChunks / 64;           // ... per W1 slab
-    constexpr int NI = XI + WI;
-    constexpr int IPW = (NI + NW - 1) / NW;            // per wave (upper bound)
     constexpr int SLAB = (BM + NH) * kLdk;             // elements per slab buffer
     constexpr int RED_BYTES = BM * 65 * 4;             // epilogue partial sums
     constexpr int LDS_BYTES = kStages * SLAB * 2 > RED_BYTES ? kStages * SLAB * 2 : RED_BYTES;
@@ -82,39 +81,71 @@ __global__ __launch_bounds__(BM * 2, 1) void gate_bf16_kernel(
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
     bf16* const lds0 = (bf16*)lds_raw;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: wave tests branch on SCC
     const int wr = wave >> 1, wc = wave & 1;
     const int il = lane & 31, half = lane >> 5;
     const int64_t row0 = (int64_t)blockIdx.x * BM;
-    const bf16* const xblk = x + row0 * x_stride;
-    // this wave's load instructions: g = wave + NW * i for g < NI
-    const int my_ni = (NI - wave + NW - 1) / NW;
+    const int rows = (int)min((int64_t)BM, n - row0);
 
-    int off[IPW];
+    // W1 slabs: LDS-direct, instruction g = wave + NW i (g < WI), one 16-B
+    // chunk per lane; the pad chunk of each padded row reloads chunk 0.
+    constexpr int WPW = (WI + NW - 1) / NW;
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(w1, (uint32_t)((int64_t)NH * d_model * 2));
+    uint32_t woff[WPW];
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int g = wave + NW * i;
-        off[i] = 0;
-        if (g < XI) {
-            const int slot = g * 64 + lane;
-            const int r = slot / kRowChunks, c = slot % kRowChunks;
-            const int rr = row0 + r < n ? r : (int)(n - 1 - row0);   // clamp rows past the end
-            off[i] = rr * (int)x_stride + (c < kBK / 8 ? c : 0) * 8;
-        } else if (g < NI) {
-            const int slot = (g - XI) * 64 + lane;
-            const int r = slot / kRowChunks, c = slot % kRowChunks;
-            off[i] = r * d_model + (c < kBK / 8 ? c : 0) * 8;
-        }
+    for (int i = 0; i < WPW; ++i) {
+        const int slot = (wave + NW * i) * 64 + lane;
+        const int r = slot / kRowChunks, c = slot % kRowChunks;
+        woff[i] = (uint32_t)((r * d_model + (c < kBK / 8 ? c : 0) * 8) * 2);
     }
-    auto issue = [&](int kb, int buf) {
-        const int k0 = kb * kBK;
-        char* dst = (char*)(lds0 + buf * SLAB);
+    auto issue_w = [&](int kb, int buf) {
+        bf16* dst = lds0 + buf * SLAB + BM * kLdk;
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int g = wave + NW * i;
-            if (g < XI) lds_load16(xblk + k0 + off[i], dst + g * 1024);
-            else if (g < NI) lds_load16(w1 + k0 + off[i], dst + BM * kLdk * 2 + (g - XI) * 1024);
-        }
+        for (int i = 0; i < WPW; ++i)
+            if (wave + NW * i < WI) lds_load16_buf(wrs, woff[i], (uint32_t)kb * (kBK * 2), dst + (wave + NW * i) * 512);
+    };
+    // X slabs: coalesced 16-B loads into registers (8 lanes per 128-B row
+    // slice), written to the slab's LDS buffer one iteration later.  With the
+    // LDS buffer in flight as well, two X slabs are in flight per workgroup.
+    constexpr int XPT = BM * (kBK / 8) / NT;   // 16-B chunks per thread per slab (4)
+    const __amdgpu_buffer_rsrc_t xrs =
+        make_rsrc(x + row0 * x_stride, (uint32_t)(((int64_t)(rows - 1) * x_stride + d_model) * 2));
+    uint32_t xoff[XPT];
+    int xlds[XPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int c = tid + NT * i;
+        const int r = c / (kBK / 8), ch = c % (kBK / 8);
+        xoff[i] = (uint32_t)(((int64_t)min(r, rows - 1) * x_stride + ch * 8) * 2);   // rows past the end: clamped
+        xlds[i] = r * kLdk + ch * 8;
+    }
+    // 128-token tiles (one wave per SIMD) keep X on the LDS-direct path,
+    // which measured faster there
+    constexpr bool XREG = BM == 256;
+    const __amdgpu_buffer_rsrc_t xrs_lds = xrs;
+    constexpr int XI_W = (XI + NW - 1) / NW;
+    uint32_t xloff[XREG ? 1 : XI_W];
+#pragma unroll
+    for (int i = 0; i < (XREG ? 1 : XI_W); ++i) {
+        const int slot = (wave + NW * i) * 64 + lane;
+        const int r = slot / kRowChunks, c = slot % kRowChunks;
+        xloff[i] = (uint32_t)(((int64_t)min(r, rows - 1) * x_stride + (c < kBK / 8 ? c : 0) * 8) * 2);
+    }
+    auto issue_x_lds = [&](int kb, int buf) {
+        bf16* dst = lds0 + buf * SLAB;
+#pragma unroll
+        for (int i = 0; i < XI_W; ++i)
+            if (wave + NW * i < XI) lds_load16_buf(xrs_lds, xloff[i], (uint32_t)kb * (kBK * 2), dst + (wave + NW * i) * 512);
+    };
+    auto load_x = [&](int kb, u32x4 (&xr)[XPT]) {
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) xr[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff[i], kb * (kBK * 2), 0);
+    };
+    auto store_x = [&](const u32x4 (&xr)[XPT], int buf) {
+        bf16* dst = lds0 + buf * SLAB;
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) *(u32x4*)(dst + xlds[i]) = xr[i];
     };
 
     f32x16 acc[2][CB];
@@ -124,39 +155,84 @@ __global__ __launch_bounds__(BM * 2, 1) void gate_bf16_kernel(
         for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x16{};
 
     const int nk = d_model / kBK;
-    constexpr int AHEAD = kStages - 1;   // slabs in flight while one is consumed
+    // One slab: 4 k-steps of 2 x CB MFMAs.  Fragments of k-step ks+1 are read
+    // while k-step ks multiplies (two fragment sets); empty volatile asm
+    // statements keep those reads ahead of the MFMAs and each MFMA in its
+    // slot, so no MFMA waits on a read issued just before it.
+    auto mma_slab = [&](int buf) {
+        const bf16* xs = lds0 + buf * SLAB + (wr * 64 + il) * kLdk + half * 8;
+        const bf16* ws = lds0 + buf * SLAB + BM * kLdk + (wc * CB * 32 + il) * kLdk + half * 8;
+        constexpr int NF = 2 + CB;   // fragments per k-step: 2 of X, CB of W1
+        auto frag = [&](int ks, int f) -> bf16x8 {
+            return f < 2 ? *(const bf16x8*)(xs + f * 32 * kLdk + ks * 16)
+                         : *(const bf16x8*)(ws + (f - 2) * 32 * kLdk + ks * 16);
+        };
+        bf16x8 fr[2][NF];
 #pragma unroll
-    for (int p = 0; p < AHEAD; ++p)
-        if (p < nk) issue(p, p);
-    // slab 0 must land; slabs 1 .. AHEAD-1 may still be in flight
-    if (AHEAD > 1 && nk > 1) wait_vm_le(my_ni * (AHEAD - 1));
-    else __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int kb = 0; kb < nk; ++kb) {
-        const int buf = kb % kStages;
-        const bool more = kb + AHEAD < nk;
-        if (more) issue(kb + AHEAD, (kb + AHEAD) % kStages);
-        const bf16* xs = lds0 + buf * SLAB;
-        const bf16* ws = xs + BM * kLdk;
+        for (int f = 0; f < NF; ++f) fr[0][f] = frag(0, f);
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
-            bf16x8 a[2], b[CB];
+            const int c = ks & 1;
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                a[rb] = *(const bf16x8*)(xs + (wr * 64 + rb * 32 + il) * kLdk + ks * 16 + half * 8);
+            for (int m = 0; m < 2 * CB; ++m) {
+                if (ks + 1 < kBK / 16 && m < NF) {
+                    fr[c ^ 1][m] = frag(ks + 1, m);
+                    __asm__ volatile("" ::: "memory");
+                }
+                const int rb = m / CB, cb = m % CB;
+                __asm__ volatile("" : "+v"(fr[c][rb]), "+v"(fr[c][2 + cb]));
+                acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[c][rb], fr[c][2 + cb], acc[rb][cb], 0, 0, 0);
+            }
+            // fewer MFMAs than fragments (CB = 1): read the rest now
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-                b[cb] = *(const bf16x8*)(ws + (wc * CB * 32 + cb * 32 + il) * kLdk + ks * 16 + half * 8);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
+            for (int f = 2 * CB; f < NF; ++f)
+                if (ks + 1 < kBK / 16) fr[c ^ 1][f] = frag(ks + 1, f);
         }
-        // slab kb+1 must have landed; later slabs may stay in flight
-        if (more && AHEAD > 1) wait_vm_le(my_ni * (AHEAD - 1));
+    };
+    // Iteration kb computes slab kb from LDS buffer kb % 2 while W1(kb+1)
+    // lands in the other buffer and X(kb+2) loads into the registers X(kb)
+    // came through; at its end X(kb+1), loaded since the previous iteration,
+    // is stored from registers into the other buffer.  Each X slab thus has
+    // two iterations to arrive.
+    auto step = [&](int kb, u32x4 (&xcur)[XPT], u32x4 (&xnext)[XPT]) {
+        const int buf = kb & 1;
+        if (kb + 1 < nk) issue_w(kb + 1, buf ^ 1);
+        if (kb + 2 < nk) load_x(kb + 2, xcur);
+        mma_slab(buf);
+        if (kb + 1 < nk) store_x(xnext, buf ^ 1);
+        // W1(kb+1) (issued before X(kb+2)) must land; X(kb+2) may stay in flight
+        if (kb + 2 < nk) wait_vm_le(XPT);
         else __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+
+    if constexpr (XREG) {
+        u32x4 xa[XPT], xb[XPT];
+        load_x(0, xa);
+        if (nk > 1) load_x(1, xb);
+        issue_w(0, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        store_x(xa, 0);
+        __syncthreads();
+        for (int kb = 0; kb < nk; kb += 2) {
+            step(kb, xa, xb);
+            if (kb + 1 < nk) step(kb + 1, xb, xa);
+        }
+    } else {
+        // both operands LDS-direct, one slab in flight while one is consumed
+        issue_x_lds(0, 0);
+        issue_w(0, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        for (int kb = 0; kb < nk; ++kb) {
+            if (kb + 1 < nk) {
+                issue_x_lds(kb + 1, (kb + 1) & 1);
+                issue_w(kb + 1, (kb + 1) & 1);
+            }
+            mma_slab(kb & 1);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
     }
 
     // Epilogue: per token, sum over this wave's hidden units of SiLU(a + b1) * w2.
