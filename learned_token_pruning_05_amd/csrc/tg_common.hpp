@@ -80,6 +80,29 @@ __device__ __forceinline__ void lds_load16_buf(__amdgpu_buffer_rsrc_t r, uint32_
                                               (int)soff, 0, 0);
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (LDS / export counters left unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (7 << 4) | (0xf << 8); }
+
+// Wait until at most n (wave-uniform, 0..12) vector-memory operations remain.
+__device__ __forceinline__ void wait_vm_le(int n) {
+    switch (n) {
+        case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2)); break;
+        case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3)); break;
+        case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); break;
+        case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5)); break;
+        case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6)); break;
+        case 7: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7)); break;
+        case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
+        case 9: __builtin_amdgcn_s_waitcnt(vmcnt_imm(9)); break;
+        case 10: __builtin_amdgcn_s_waitcnt(vmcnt_imm(10)); break;
+        case 11: __builtin_amdgcn_s_waitcnt(vmcnt_imm(11)); break;
+        case 12: __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); break;
+        default: __builtin_amdgcn_s_waitcnt(0); break;
+    }
+}
+
 __device__ __forceinline__ void lds_load16(const void* gsrc, void* ldst) {
     __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)ldst, 16, 0, 0);
 }

@@ -36,28 +36,6 @@ __device__ __forceinline__ float silu_f32(float a) {
     return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * kLog2e));
 }
 
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (LDS / export counters left unconstrained).
-constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (7 << 4) | (0xf << 8); }
-
-// Wait until at most n (wave-uniform, 0..12) vector-memory operations remain.
-__device__ __forceinline__ void wait_vm_le(int n) {
-    switch (n) {
-        case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1)); break;
-        case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2)); break;
-        case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3)); break;
-        case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); break;
-        case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5)); break;
-        case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6)); break;
-        case 7: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7)); break;
-        case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
-        case 9: __builtin_amdgcn_s_waitcnt(vmcnt_imm(9)); break;
-        case 10: __builtin_amdgcn_s_waitcnt(vmcnt_imm(10)); break;
-        case 11: __builtin_amdgcn_s_waitcnt(vmcnt_imm(11)); break;
-        case 12: __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); break;
-        default: __builtin_amdgcn_s_waitcnt(0); break;
-    }
-}
 
 // BM tokens per workgroup (BM / 64 row groups of waves x 2 hidden-column
 // groups); CB = 32-wide hidden blocks per wave, d_hid = 64 * CB.  Both operands
