@@ -143,18 +143,17 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(
     for (int i = tid; i < kBins; i += kHistThreads) h[i] = 0u;
     __syncthreads();
     const float* sc = scores + q.start;
-    for (int base = c0; base < c0 + kHistChunk; base += kHistThreads * 8) {
-        float v[8];
+    constexpr int PER = kHistChunk / kHistThreads;   // all of a thread's scores loaded first
+    float v[PER];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = base + j * kHistThreads + tid;
-            v[j] = (i >= q.db && i < q.de) ? sc[i] : 0.0f;
-        }
+    for (int j = 0; j < PER; ++j) {
+        const int i = c0 + j * kHistThreads + tid;
+        v[j] = (i >= q.db && i < q.de) ? sc[i] : 0.0f;
+    }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = base + j * kHistThreads + tid;
-            hist_add(h, score_key(v[j]) >> 21, i >= q.db && i < q.de);
-        }
+    for (int j = 0; j < PER; ++j) {
+        const int i = c0 + j * kHistThreads + tid;
+        hist_add(h, score_key(v[j]) >> 21, i >= q.db && i < q.de);
     }
     __syncthreads();
     uint32_t* dst = part + ((int64_t)s * nch_hist + c) * kBins;
