@@ -32,7 +32,7 @@
 //     A running offset m (set from the first tile's exact row max, kept
 //     bf16-exact) rides in Q' column 3 against 1.0 in K' column 3, so the MFMA
 //     emits u = t - m and p = exp2(u) needs no max or subtraction.  Row sums
-//     use v_dot2 on the bf16 P that the P.V MFMA consumes; a tile whose sum
+//     add up the bf16 P that the P.V MFMA consumes; a tile whose sum
 //     exceeds 2^62 (some p very large) takes a rare path that raises m to the
 //     tile max and rescales O and l (the result is exact either way).  The
 //     loop is a three-stage pipeline (QK of tile j+2 || exponentials of tile
@@ -388,7 +388,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
     for (int bb = 0; bb < DB; ++bb) o[bb] = f32x16{};
     float m_run = 0.0f, l_run = 0.0f;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
     constexpr float kSumLimit = 0x1p62f;
 
     auto set_offset = [&](float m) {
@@ -407,17 +406,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
         mask(a1, j0, 1);
     };
     auto expo = [&](const f32x16& acc, bf16x8* pbk) {
-        float l = 0.0f;
+        float l0 = 0.0f, l1 = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pbk[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(acc[r]);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const bf16x2 pr = {pbk[u][e], pbk[u][e + 1]};
-                l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
-            }
-        return l;
+        for (int r = 0; r < 16; r += 2) {
+            const bf16x2 pr = {(bf16)__builtin_amdgcn_exp2f(acc[r]), (bf16)__builtin_amdgcn_exp2f(acc[r + 1])};
+            pbk[r >> 3][r & 7] = pr[0];
+            pbk[r >> 3][(r & 7) + 1] = pr[1];
+            const uint32_t pw = __builtin_bit_cast(uint32_t, pr);
+            l0 += __uint_as_float(pw << 16);
+            l1 += __uint_as_float(pw & 0xffff0000u);
+        }
+        return l0 + l1;
     };
     auto tile_max = [&](const f32x16& a0, const f32x16& a1) {
         float mx = a0[0];
@@ -499,7 +498,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
         for (int i = 0; i < PF; ++i) ring[i] = frag(i);
         ta = f32x16{};
         tb = f32x16{};
-        float lsum[2] = {0.0f, 0.0f};
+        float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const bf16x8 a = ring[i % PF];
@@ -532,14 +531,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
                 const float x0 = kb ? sb[r] : sa[r], x1 = kb ? sb[r + 1] : sa[r + 1];
                 const float e0 = __builtin_amdgcn_exp2f(x0);
                 const float e1 = __builtin_amdgcn_exp2f(x1);
-                pn[kb][r >> 3][r & 7] = (bf16)e0;
-                pn[kb][r >> 3][(r & 7) + 1] = (bf16)e1;
-                const bf16x2 pr = {pn[kb][r >> 3][r & 7], pn[kb][r >> 3][(r & 7) + 1]};
-                lsum[kb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[kb], false);
-                __asm__ volatile("" ::"v"(lsum[kb]));          // and done before the next step
+                const bf16x2 pr = {(bf16)e0, (bf16)e1};
+                pn[kb][r >> 3][r & 7] = pr[0];
+                pn[kb][r >> 3][(r & 7) + 1] = pr[1];
+                // sums of the bf16 values with plain fp32 adds: v_dot2 would
+                // stall the matrix pipe, these co-issue with the MFMAs
+                const uint32_t pw = __builtin_bit_cast(uint32_t, pr);
+                lsum[kb] += __uint_as_float(pw << 16);
+                lsum[2 + kb] += __uint_as_float(pw & 0xffff0000u);
+                __asm__ volatile("" ::"v"(lsum[kb]), "v"(lsum[2 + kb]));   // and done before the next step
             }
         }
-        float ln = lsum[0] + lsum[1];
+        float ln = (lsum[0] + lsum[2]) + (lsum[1] + lsum[3]);
         // the refresh test consumes the exponentials before any branch
         if (more1 && __builtin_amdgcn_ballot_w64(!(ln <= kSumLimit))) {
             // Rare: tile j+1's probabilities were huge.  Raise the offset to its
