@@ -76,7 +76,7 @@ constexpr int kWaves = 4;   // waves per attention workgroup
 constexpr int kExtra = 16;  // extra K'/Q' columns carrying the key bias
 
 struct RopeFreqs {
-    double inv_freq[64];   // base^(-2f/D), f < D/2
+    double rev[64];   // base^(-2f/D) / (2 pi): turns of frequency f per position, f < D/2
 };
 
 __device__ __forceinline__ void split_bf16(float x, bf16* hi, bf16* lo) {
@@ -93,132 +93,124 @@ __device__ __forceinline__ float bf16_ceil(float x) {
 }
 
 // ---------------------------------------------------------------- pre-pass --
-// One workgroup per (64 kept tokens, kv head); lane = token.  Head-0 groups
-// also store the (cos, sin) table the queries use.  A last group row zero-fills
-// the padding rows (below).
+// One workgroup per (64 padded rows, kv head).  Padded rows are 64-aligned
+// tiles of the K'/V^T layout, so every store is a whole coalesced tile: K'
+// rows are contiguous, and V^T rows are 128-B runs.  A padded row holds the
+// token at its offset in its sequence, or zeros (rows between and after
+// sequences, so that key tiles can be loaded whole: their probabilities are
+// then 0).  Head-0 groups also store the (cos, sin) table the queries use.
 template <int D>
 __global__ __launch_bounds__(256) void attn_prep_kernel(
     const bf16* __restrict__ k, const bf16* __restrict__ v, int64_t kv_stride,
     const float* __restrict__ key_score, const int* __restrict__ pos, const int* __restrict__ cu_kept,
     int n_seqs, int64_t m_tot, int hkv, int64_t mp, RopeFreqs fr, int rope, bf16* __restrict__ ws_k,
     bf16* __restrict__ ws_vt, float2* __restrict__ ws_cs) {
-    constexpr int HALF = D / 2, KD = D + kExtra, FPW = HALF / 4, VLD = D + 2;
-    __shared__ __attribute__((aligned(16))) bf16 vs[64 * VLD];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    constexpr int HALF = D / 2, KD = D + kExtra, NPAIR = D / 16, NC8 = D / 8;
+    // V^T tile: row d holds the 64 columns vt_col(r) of this tile; 8-column
+    // groups are XOR-swizzled by (d / 8) % 8 so the transposing 2-byte writes
+    // of 16 lanes spread over the banks, while 16-B reads stay contiguous.
+    __shared__ __attribute__((aligned(16))) bf16 vs[D * 64];
+    __shared__ int tok[64];
+    const int tid = threadIdx.x;
     const int h = blockIdx.y;
-    if (h == hkv) {
-        // Zero the padding rows between sequences (and after the last one), so
-        // that key tiles can be loaded whole: rows past a sequence's end are then
-        // either zeros or other sequences' finite data, and their probabilities
-        // are 0.  Grid-stride over (padded row, kv head); a row is padding iff it
-        // lies past the end of the sequence whose padded start precedes it.
-        const int64_t nthreads = (int64_t)gridDim.x * 256;
-        for (int64_t idx = (int64_t)blockIdx.x * 256 + tid; idx < mp * hkv; idx += nthreads) {
-            const int64_t r = idx / hkv;
-            const int hh = (int)(idx % hkv);
-            int lo = 0, hi = n_seqs;   // last sequence whose padded start is <= r (or 0)
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (padded_seq_start(cu_kept[mid], mid) <= r) lo = mid; else hi = mid;
-            }
-            const int64_t p0 = padded_seq_start(cu_kept[lo], lo);
-            if (r >= p0 && r < p0 + (cu_kept[lo + 1] - cu_kept[lo])) continue;   // a token row
-            bf16* kr = ws_k + ((int64_t)hh * mp + r) * KD;
-#pragma unroll
-            for (int c = 0; c < KD; c += 8) *(bf16x8*)(kr + c) = bf16x8{};
-            bf16* vr = ws_vt + (int64_t)hh * D * mp + vt_col(r);
-            for (int d = 0; d < D; ++d) vr[(int64_t)d * mp] = (bf16)0.0f;
+    const int64_t p0 = (int64_t)blockIdx.x * 64;
+    if (tid < 64) {
+        // last sequence whose padded start is <= row (or 0), then the token
+        const int64_t r = p0 + tid;
+        int lo = 0, hi = n_seqs;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (padded_seq_start(cu_kept[mid], mid) <= r) lo = mid; else hi = mid;
         }
-        return;
+        const int64_t ps = padded_seq_start(cu_kept[lo], lo);
+        const int len = cu_kept[lo + 1] - cu_kept[lo];
+        tok[tid] = (r >= ps && r < ps + len) ? cu_kept[lo] + (int)(r - ps) : -1;
     }
-    const int64_t m0 = (int64_t)blockIdx.x * 64;
-    const int64_t m = m0 + lane;
-    const bool valid = m < m_tot;
-    int64_t prow = 0;
-    if (valid) {
-        const int s = find_seq(cu_kept, n_seqs, m);
-        prow = padded_seq_start(cu_kept[s], s) + (m - cu_kept[s]);
+    __syncthreads();
+
+    // V rows, coalesced (lanes over 16-B chunks of a row), transposed into LDS
+    constexpr int VIT = 64 * NC8 / 256;
+#pragma unroll
+    for (int i = 0; i < VIT; ++i) {
+        const int item = tid + 256 * i;
+        const int r = item / NC8, c8 = item % NC8;
+        const int m = tok[r];
+        const bf16x8 x = m >= 0 ? *(const bf16x8*)(v + (int64_t)m * kv_stride + (int64_t)h * D + c8 * 8) : bf16x8{};
+        const int col = (int)vt_col(r) ^ ((c8 & 7) * 8);   // d / 8 == c8 for all 8 values
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vs[(c8 * 8 + e) * 64 + col] = x[e];
     }
-    // V^T through LDS: coalesced row loads first (their latency overlaps the
-    // rotary work), then per channel d the 64 lanes store 64 consecutive rows.
-    constexpr int VCH = 64 * (D / 8) / 256;
-    bf16x8 vx[VCH];
+
+    // K' rows: item (row, chunk pair p) rotates chunks p and p + D/16 (the
+    // rotate-half partners), lanes over p so loads and stores are coalesced
+    constexpr int KIT = 64 * NPAIR / 256;
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-        const int ch = tid + 256 * i;
-        const int r = ch / (D / 8), c8 = ch % (D / 8);
-        vx[i] = (m0 + r < m_tot) ? *(const bf16x8*)(v + (m0 + r) * kv_stride + (int64_t)h * D + c8 * 8) : bf16x8{};
-    }
-    // K' row: rotated key + bias columns
-    const int f0 = wave * FPW;
-    if (valid) {
-        float cn[FPW], sn[FPW];
-        if (rope) {
-            const double p = (double)pos[m];
-            const double two_pi = 6.283185307179586;
-#pragma unroll
-            for (int e = 0; e < FPW; ++e) {
-                const double ang = p * fr.inv_freq[f0 + e];
-                const double red = ang - two_pi * rint(ang * (1.0 / two_pi));
-                sincosf((float)red, &sn[e], &cn[e]);
-            }
-            if (h == 0) {
-                float4* dst = (float4*)(ws_cs + m * HALF + f0);
-#pragma unroll
-                for (int e = 0; e < FPW; e += 2) dst[e / 2] = make_float4(cn[e], sn[e], cn[e + 1], sn[e + 1]);
-            }
-        }
-        const bf16* src = k + m * kv_stride + (int64_t)h * D;
-        bf16* dst = ws_k + ((int64_t)h * mp + prow) * KD;
-#pragma unroll
-        for (int c = 0; c < FPW / 8; ++c) {
-            bf16x8 x1 = *(const bf16x8*)(src + f0 + c * 8);
-            bf16x8 x2 = *(const bf16x8*)(src + HALF + f0 + c * 8);
+    for (int i = 0; i < (KIT > 0 ? KIT : 1); ++i) {
+        const int item = tid + 256 * i;
+        if (KIT == 0 && item >= 64 * NPAIR) break;
+        const int r = item / NPAIR, p = item % NPAIR;
+        const int m = tok[r];
+        bf16x8 x1 = bf16x8{}, x2 = bf16x8{};
+        if (m >= 0) {
+            const bf16* src = k + (int64_t)m * kv_stride + (int64_t)h * D;
+            x1 = *(const bf16x8*)(src + p * 8);
+            x2 = *(const bf16x8*)(src + HALF + p * 8);
             if (rope) {
+                // angle in turns, reduced in fp64 to [-1/2, 1/2]; the hardware
+                // sine and cosine take turns
+                float cn[8], sn[8];
+                const double ppos = (double)pos[m];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const double t = ppos * fr.rev[p * 8 + e];
+                    const float tr = (float)(t - rint(t));
+                    sn[e] = __builtin_amdgcn_sinf(tr);
+                    cn[e] = __builtin_amdgcn_cosf(tr);
+                }
+                if (h == 0) {
+                    float4* dst = (float4*)(ws_cs + (int64_t)m * HALF + p * 8);
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) dst[e / 2] = make_float4(cn[e], sn[e], cn[e + 1], sn[e + 1]);
+                }
                 bf16x8 y1, y2;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float a = (float)x1[e], b = (float)x2[e];
-                    const float cc = cn[c * 8 + e], ss = sn[c * 8 + e];
-                    y1[e] = (bf16)(a * cc - b * ss);
-                    y2[e] = (bf16)(b * cc + a * ss);
+                    y1[e] = (bf16)(a * cn[e] - b * sn[e]);
+                    y2[e] = (bf16)(b * cn[e] + a * sn[e]);
                 }
                 x1 = y1;
                 x2 = y2;
             }
-            *(bf16x8*)(dst + f0 + c * 8) = x1;
-            *(bf16x8*)(dst + HALF + f0 + c * 8) = x2;
         }
-        if (wave == 0) {
-            bf16x8 extra[2] = {bf16x8{}, bf16x8{}};
-            bf16 sh, sl;
-            split_bf16(key_score[m], &sh, &sl);
-            extra[0][0] = sh;
-            extra[0][1] = sl;
-            extra[0][2] = sh;
-            extra[0][3] = (bf16)1.0f;
-            *(bf16x8*)(dst + D) = extra[0];
-            *(bf16x8*)(dst + D + 8) = extra[1];
+        bf16* dst = ws_k + ((int64_t)h * mp + p0 + r) * KD;
+        *(bf16x8*)(dst + p * 8) = x1;
+        *(bf16x8*)(dst + HALF + p * 8) = x2;
+        if (p == 0) {
+            // bias columns: (s_hi, s_lo, s_hi, 1) against Q' (g_hi, g_hi, g_lo, -m)
+            bf16x8 extra = bf16x8{};
+            if (m >= 0) {
+                bf16 sh, sl;
+                split_bf16(key_score[m], &sh, &sl);
+                extra[0] = sh;
+                extra[1] = sl;
+                extra[2] = sh;
+                extra[3] = (bf16)1.0f;
+            }
+            *(bf16x8*)(dst + D) = extra;
+            *(bf16x8*)(dst + D + 8) = bf16x8{};
         }
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-        const int ch = tid + 256 * i;
-        const int r = ch / (D / 8), c8 = ch % (D / 8);
-        uint32_t* d32 = (uint32_t*)(vs + r * VLD + c8 * 8);   // VLD rows are 4-byte aligned
-        const uint32_t* xs = (const uint32_t*)&vx[i];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) d32[u] = xs[u];
     }
     __syncthreads();
-    if (valid) {
-        bf16* dst = ws_vt + ((int64_t)h * D) * mp + vt_col(prow);
-#pragma unroll 8
-        for (int dd = 0; dd < D / 4; ++dd) {
-            const int d = wave * (D / 4) + dd;
-            dst[(int64_t)d * mp] = vs[lane * VLD + d];
-        }
+
+    // V^T stores: lanes over the 8 16-B column groups of a d row
+    constexpr int TIT = D * 8 / 256;
+#pragma unroll
+    for (int i = 0; i < TIT; ++i) {
+        const int item = tid + 256 * i;
+        const int d = item / 8, q = item % 8;
+        const bf16x8 x = *(const bf16x8*)(vs + d * 64 + ((q ^ ((d >> 3) & 7)) * 8));
+        *(bf16x8*)(ws_vt + ((int64_t)h * D + d) * mp + p0 + q * 8) = x;
     }
 }
 
@@ -628,9 +620,10 @@ int launch_fwd(const AttnArgs& a, hipStream_t st) {
 template <int D>
 int launch_prep(const AttnArgs& a, hipStream_t st) {
     RopeFreqs fr;
-    for (int f = 0; f < 64; ++f) fr.inv_freq[f] = f < D / 2 ? exp2(-(2.0 * f / D) * a.rope_log2_base) : 0.0;
-    // grid.y = kv heads, plus one extra row of groups for the padding fill
-    hipLaunchKernelGGL(attn_prep_kernel<D>, dim3((unsigned)((a.m_tot + 63) / 64), a.hkv + 1), dim3(256), 0, st, a.k,
+    for (int f = 0; f < 64; ++f)
+        fr.rev[f] = f < D / 2 ? exp2(-(2.0 * f / D) * a.rope_log2_base) / 6.283185307179586 : 0.0;
+    // one group per (64 padded rows, kv head); a.mp is a multiple of 64
+    hipLaunchKernelGGL(attn_prep_kernel<D>, dim3((unsigned)(a.mp / 64), a.hkv), dim3(256), 0, st, a.k,
                        a.v, a.kv_stride, a.key_score, a.pos, a.cu_kept, a.n_seqs, a.m_tot, a.hkv, a.mp, fr,
                        (int)a.rope, a.ws_k, a.ws_vt, a.ws_cs);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;

@@ -338,6 +338,61 @@ def test_attention_prepare_forward_split():
     _check_attn(c3, o3.float().cpu().numpy(), l3.cpu().numpy(), 1e6, _sample_rows(ck, 16))
 
 
+def _padded_start(cu_s, s):
+    return (int(cu_s) + 16 * s + 15) & ~15
+
+
+def _vt_col(r):
+    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1)
+
+
+def test_attention_prepare_layout():
+    """The kept-only cache that tg_attn_prepare writes, read back directly: rotated
+    keys within one bf16 rounding of the fp64 rotation, the bias columns, V^T in
+    its permuted column order, zero padding rows, and the (cos, sin) table."""
+    w = workloads.custom([900, 2500, 300], [40, 100, 20], [300, 1700, 120], n_q_heads=8, n_kv_heads=4,
+                         head_dim=128, seed=21)
+    _print_case("attn prepare layout")
+    c = _attn_case(w)
+    ck = c["ck"]
+    m, hkv, d = c["k"].shape
+    n_seqs = len(ck) - 1
+    ws = tg.tg_attn_prepare(_dev(c["k"]), _dev(c["v"]), _dev(c["sk"]), _i32(c["pk"]), _i32(ck), rope_base=1e6)
+    torch.cuda.synchronize()
+    mp = ((m + 16 * n_seqs + 16 + 63) & ~63) + 64
+    al = lambda b: (b + 255) & ~255
+    kb, vb = al(hkv * mp * (d + 16) * 2), al(hkv * mp * d * 2)
+    raw = ws.cpu()
+    kp = raw[:hkv * mp * (d + 16) * 2].view(torch.bfloat16).view(hkv, mp, d + 16).float().numpy()
+    vt = raw[kb:kb + hkv * mp * d * 2].view(torch.bfloat16).view(hkv, d, mp).float().numpy()
+    cs = raw[kb + vb:kb + vb + m * (d // 2) * 8].view(torch.float32).view(m, d // 2, 2).numpy()
+    kf, vf = c["k"].float().numpy(), c["v"].float().numpy()
+    ref_k = oracle.rope(kf, c["pk"], 1e6)                    # fp64 rotation of the bf16 keys
+    rows = np.concatenate([_padded_start(ck[s], s) + np.arange(ck[s + 1] - ck[s]) for s in range(n_seqs)])
+    got_k = kp[:, rows, :d].transpose(1, 0, 2)
+    # one bf16 rounding (at most one ulp either side of a rounding boundary) of an
+    # fp32 rotation whose sine and cosine are good to ~1e-6
+    ek = np.abs(got_k - ref_k) - np.abs(ref_k) * 2.0 ** -8
+    print(f"   K' excess over one bf16 ulp: {ek.max():.3g}", flush=True)
+    assert ek.max() <= 2e-5
+    sk = c["sk"].astype(np.float64)
+    hi = torch.from_numpy(c["sk"]).to(torch.bfloat16).float().numpy().astype(np.float64)
+    np.testing.assert_array_equal(kp[:, rows, d], np.broadcast_to(hi, (hkv, m)))
+    np.testing.assert_array_equal(kp[:, rows, d + 2], np.broadcast_to(hi, (hkv, m)))
+    assert np.all(np.abs(kp[:, rows, d] + kp[:, rows, d + 1] - sk[None, :]) <= np.abs(sk) * 2.0 ** -16 + 1e-30)
+    np.testing.assert_array_equal(kp[:, rows, d + 3], 1.0)
+    np.testing.assert_array_equal(kp[:, rows, d + 4:], 0.0)
+    cols = np.array([_vt_col(int(r)) for r in rows])
+    np.testing.assert_array_equal(vt[:, :, cols].transpose(2, 0, 1), vf)
+    pad = np.setdiff1d(np.arange(mp), rows)
+    assert not kp[:, pad, :].any()
+    assert not vt[:, :, np.array([_vt_col(int(r)) for r in pad])].any()
+    ang = c["pk"].astype(np.float64)[:, None] * 1e6 ** (-2.0 * np.arange(d // 2) / d)[None, :]
+    ec, es = np.abs(cs[..., 0] - np.cos(ang)).max(), np.abs(cs[..., 1] - np.sin(ang)).max()
+    print(f"   cos/sin table max error: {ec:.3g} {es:.3g}", flush=True)
+    assert ec <= 1e-5 and es <= 1e-5
+
+
 # --------------------------------------------------------------- end to end ----
 @pytest.mark.parametrize("name", ["tiny", "16k"])
 def test_gated_layer_end_to_end(name):
