@@ -10,7 +10,7 @@
 // with key == T that are kept (the r lowest-indexed ones).  Five launches, no
 // cross-workgroup waiting, no zero-filled state, and every pass over all
 // tokens spread over many workgroups:
-//   H  every 8192-token chunk writes the 2048-bin histogram of its document
+//   H  every 4096-token chunk writes the 2048-bin histogram of its document
 //      keys' top 11 bits (plain stores, one row per chunk);
 //   B  one workgroup per sequence sums the chunk histograms and finds the
 //      bucket b1 holding T;
@@ -30,8 +30,8 @@ namespace tg {
 namespace {
 
 constexpr int kBins = 2048;
-constexpr int kHistChunk = 8192;            // tokens per histogram workgroup
-constexpr int kHistThreads = 256;
+constexpr int kHistChunk = 4096;            // tokens per histogram workgroup
+constexpr int kHistThreads = 1024;
 constexpr int kWriteChunk = 2048;           // tokens per write workgroup
 constexpr int kWriteThreads = 256;
 constexpr int kWriteItems = kWriteChunk / kWriteThreads;
@@ -270,6 +270,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     __shared__ uint32_t sh_scan[kSelWaves];
     __shared__ uint32_t sh_out[2];
     const int s = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const SeqInfo q(s, cu, db, de, kd);
     if (!q.needs_select()) return;   // the write kernel handles "all" and "none" directly
     const int nch = (q.n + kWriteChunk - 1) / kWriteChunk;
@@ -306,7 +307,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     };
     const bool in_lds = nc <= kCandCap;
     if (in_lds) {
-        for (uint32_t g = tid; g < nc; g += kSelThreads) cand[g] = cand_at(g);
+        // a wave per chunk copies the chunk's slice (coalesced) to its offset
+        for (int c = w; c < nch; c += kSelWaves) {
+            const uint32_t o = coff[c], n_c = coff[c + 1] - o;
+            const uint2* src = cg + (int64_t)c * kWriteChunk;
+            for (uint32_t i = lane; i < n_c; i += 64) cand[o + i] = src[i];
+        }
         __syncthreads();
     }
     auto get = [&](uint32_t g) { return in_lds ? cand[g] : cand_at(g); };
@@ -335,11 +341,22 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const uint32_t T = prefix;
     const uint32_t r = rem;
 
-    // candidates above / equal to T, per write chunk; offsets by exclusive scan
-    for (uint32_t i = tid; i < nc; i += kSelThreads) {
-        const uint2 e = get(i);
-        if (e.x > T) atomicAdd(&ca[e.y / kWriteChunk], 1u);
-        else if (e.x == T) atomicAdd(&cb[e.y / kWriteChunk], 1u);
+    // candidates above / equal to T, per write chunk (a wave per chunk, counted
+    // by ballots over its slice); offsets by exclusive scan
+    for (int c = w; c < nch; c += kSelWaves) {
+        const uint32_t o = coff[c], n_c = coff[c + 1] - o;
+        const uint2* src = cg + (int64_t)c * kWriteChunk;
+        uint32_t na = 0, nb = 0;
+        for (uint32_t i0 = 0; i0 < n_c; i0 += 64) {
+            const uint32_t i = i0 + lane;
+            const uint32_t key = i < n_c ? (in_lds ? cand[o + i].x : src[i].x) : 0u;
+            na += (uint32_t)__popcll(__ballot(i < n_c && key > T));
+            nb += (uint32_t)__popcll(__ballot(i < n_c && key == T));
+        }
+        if (lane == 0) {
+            ca[c] += na;
+            cb[c] = nb;
+        }
     }
     __syncthreads();
     uint32_t run_a = 0, run_b = 0;
