@@ -30,6 +30,8 @@ Parity status per function:
                       invariants)
   keybias_attention   pinned (textbook causal SDPA reduction, shift invariance,
                       pruning == masking, tau placement, GQA, varlen, closed forms)
+  keybias_decode      pinned (equals the prefill row of a kept token placed at its
+                      position, closed forms, no-visible-key case, shift invariance)
 """
 
 from __future__ import annotations
@@ -265,6 +267,61 @@ def keybias_attention(q, k, v, s_kept, gain, tau, pos, cu_kept,
                 den = e.sum(axis=1, keepdims=True)
                 out[a + ri, h, :] = (e @ vs[:, hk, :]) / den
                 lse[h, a + ri] = (mx + np.log(den))[:, 0]
+    return out, lse
+
+
+def keybias_decode(q_new, q_pos, k, v, s_kept, gain, tau, pos, cu_kept, rope_base: float = 1e6):
+    """One decode step of token-gated attention over the kept-only cache.
+
+    [ES] "¿Qué es la atención con control de acceso por tokens…?": above the
+    gate layer only kept tokens have keys and values (pruned tokens never get
+    KV entries), and every kept key carries its gate-score bias.  A token
+    generated after the prefill therefore attends to that kept cache.
+
+    Reading (the pages do not describe decoding): the new query of sequence s
+    sits at original position q_pos[s] and uses the prefill logit
+        l_j = <R(q, q_pos[s]), R(k_j, pos_j)> / (sqrt(D) * tau) + g_h * s_j
+    over the kept keys j of s with pos_j <= q_pos[s].  The new token's own key
+    is part of the cache only if the caller appended it.  A query that sees no
+    key gets O = 0 and LSE = -inf.
+
+    q_new: [S, Hq, D]; q_pos: [S]; k, v: [M, Hkv, D]; s_kept: [M]; gain: [Hq];
+    pos: [M]; cu_kept: [S+1].  Returns (O [S, Hq, D], LSE [Hq, S]) float64.
+    """
+    q_new = np.asarray(q_new, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    s_kept = np.asarray(s_kept, dtype=np.float64)
+    gain = np.asarray(gain, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    ck = np.asarray(cu_kept, dtype=np.int64)
+    n_seqs, hq, d = q_new.shape
+    hkv = k.shape[1]
+    if hq % hkv != 0:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    if not (tau > 0 and math.isfinite(tau)):
+        raise ValueError("tau must be positive and finite")
+    grp = hq // hkv
+    scale = 1.0 / (math.sqrt(d) * float(tau))
+    out = np.zeros((n_seqs, hq, d))
+    lse = np.full((hq, n_seqs), -np.inf)
+    for si in range(n_seqs):
+        a, b = int(ck[si]), int(ck[si + 1])
+        vis = np.nonzero(pos[a:b] <= q_pos[si])[0]
+        if vis.size == 0:
+            continue
+        qr = rope(q_new[si:si + 1], q_pos[si:si + 1], rope_base)[0]     # [Hq, D]
+        kr = rope(k[a:b], pos[a:b], rope_base)[vis]                      # [n_vis, Hkv, D]
+        vv = v[a:b][vis]
+        for h in range(hq):
+            hk = h // grp
+            logit = (kr[:, hk, :] @ qr[h]) * scale + gain[h] * s_kept[a:b][vis]
+            mx = logit.max()
+            e = np.exp(logit - mx)
+            den = e.sum()
+            out[si, h] = (e @ vv[:, hk, :]) / den
+            lse[h, si] = mx + math.log(den)
     return out, lse
 
 

@@ -353,3 +353,52 @@ def test_attention_rejects_bad_params():
         oracle.keybias_attention(z, z[:, :1], z[:, :1], np.zeros(2), np.ones(2), 0.0, [0, 1], [0, 2])
     with pytest.raises(ValueError):
         oracle.keybias_attention(np.zeros((2, 3, 4)), z, z, np.zeros(2), np.ones(3), 1.0, [0, 1], [0, 2])
+
+
+# ------------------------------------------------------------------ decode ----
+def _decode_case(seed, lens, hq, hkv, d):
+    r = np.random.default_rng(seed)
+    ck = np.concatenate([[0], np.cumsum(lens)])
+    m = int(ck[-1])
+    q, k, v = (r.standard_normal((m, h, d)) for h in (hq, hkv, hkv))
+    s = r.standard_normal(m)
+    g = r.uniform(0.5, 2, hq)
+    pos = np.concatenate([np.sort(r.choice(4000, L, replace=False)) for L in lens])
+    return q, k, v, s, g, pos, ck
+
+
+@pytest.mark.parametrize("base", [0.0, 1e6])
+def test_decode_equals_prefill_row(base):
+    """A query placed at a kept token's position, with that token's q, sees the
+    same keys as that token's prefill row (keys after it masked), so decode ==
+    the prefill oracle's row: pins the position mask, RoPE at the query
+    position, bias, gain, tau and GQA against the independently pinned prefill."""
+    q, k, v, s, g, pos, ck = _decode_case(31, [9, 1, 17, 6], 8, 2, 16)
+    full_o, full_l = oracle.keybias_attention(q, k, v, s, g, 0.87, pos, ck, rope_base=base)
+    r = np.random.default_rng(5)
+    for trial in range(3):
+        rows = np.array([r.integers(ck[i], ck[i + 1]) if trial else ck[i + 1] - 1 for i in range(len(ck) - 1)])
+        o, l = oracle.keybias_decode(q[rows], pos[rows], k, v, s, g, 0.87, pos, ck, rope_base=base)
+        np.testing.assert_allclose(o, full_o[rows], atol=1e-12)
+        np.testing.assert_allclose(l, full_l[:, rows], atol=1e-12)
+
+
+def test_decode_closed_forms_and_empty():
+    q, k, v, s, g, pos, ck = _decode_case(32, [7, 12], 2, 1, 8)
+    qp = np.array([pos[ck[1] - 1] + 50, pos[ck[1] + 4]])      # all of seq 0; first 5 keys of seq 1
+    o, l = oracle.keybias_decode(np.zeros((2, 2, 8)), qp, k, v, s, np.zeros(2), 1.0, pos, ck)
+    np.testing.assert_allclose(o[0, :, :], np.broadcast_to(v[0:7, 0].mean(0), (2, 8)), atol=1e-14)
+    np.testing.assert_allclose(o[1, :, :], np.broadcast_to(v[7:12, 0].mean(0), (2, 8)), atol=1e-14)
+    np.testing.assert_allclose(l, np.log([[7, 5], [7, 5]]), atol=1e-14)
+    # a query before every key sees nothing: O = 0, LSE = -inf
+    o, l = oracle.keybias_decode(q[[0, 7]], np.array([pos[0] - 1, pos[7] - 1]), k, v, s, g, 1.0, pos, ck)
+    assert not o.any() and np.all(l == -np.inf)
+
+
+def test_decode_shift_invariance():
+    q, k, v, s, g, pos, ck = _decode_case(33, [11, 4], 4, 2, 8)
+    qp = pos[[10, 14]] + 3
+    o1, l1 = oracle.keybias_decode(q[[3, 12]], qp, k, v, s, g, 0.9, pos, ck)
+    o2, l2 = oracle.keybias_decode(q[[3, 12]], qp, k, v, s - 1.5, g, 0.9, pos, ck)
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    np.testing.assert_allclose(l1 - l2, (g * 1.5)[:, None] * np.ones((1, 2)), atol=1e-12)
