@@ -10,8 +10,9 @@ Prints one JSON line: ms per gated layer at 128k (headline: steps bracketed by
 synchronisations, no events inside), per-stage times from a second pass with
 HIP events recorded on the launch stream between the calls, the attention
 kernel's roofline against
-the bf16 MFMA peak, top-K + gather bandwidth against HBM, the 32k budget sweep,
-and the CPU oracle timed on a bounded sample of the same workload.
+the bf16 MFMA peak, top-K + gather bandwidth against HBM, one decode step over
+the kept-only cache against HBM, the 32k budget sweep, and the CPU oracle timed
+on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -143,6 +144,37 @@ class Layer:
         return attn_flops(self.ck_h, self.w.n_q_heads, self.w.head_dim)
 
 
+def measure_decode(layer: Layer, steps=50, warmup=5):
+    """One decode step (tg_attn_decode: one new query per sequence) over the
+    kept-only cache the layer's tg_attn_prepare left in its workspace; HBM-bound
+    by the cache read (K' (D+16) x 2 B + V^T D x 2 B per kept key and kv head)."""
+    w = layer.w
+    dev = layer.q.device
+    g = torch.Generator(device="cpu").manual_seed(11)
+    qn = torch.randn(w.n_seqs, w.n_q_heads, w.head_dim, generator=g).to(torch.bfloat16).to(dev)
+    q_pos = torch.from_numpy(np.asarray(w.seqlens, dtype=np.int32)).to(dev)   # past every kept position
+    out = torch.empty((w.n_seqs, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.n_q_heads, w.n_seqs), dtype=torch.float32, device=dev)
+    wsd = torch.empty(max(1, tg.tg_attn_decode_workspace_bytes(w.n_seqs, layer.max_kept, w.n_q_heads,
+                                                                w.head_dim)), dtype=torch.uint8, device=dev)
+    f = lambda: tg.tg_attn_decode(qn, q_pos, layer.gain, layer.tau, layer.pk, layer.ck, layer.max_kept,
+                                  w.n_kv_heads, layer.ws, rope_base=w.rope_base, out=out, lse=lse, workspace=wsd)
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    cache = float(layer.m * w.n_kv_heads * (4 * w.head_dim + 32))
+    return {"us_per_step": round(us, 2), "cache_bytes": cache, "gbs": round(cache / us / 1e3, 1),
+            "frac_hbm": round(cache / us / 1e3 / PEAK_HBM_GBS, 4), "queries": w.n_seqs,
+            "kernels": "attn_decode_split_kernel + attn_decode_combine_kernel (tg_attn_decode)"}
+
+
 def pmc_traffic():
     """HBM bytes per attention launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source (else None)."""
@@ -258,6 +290,7 @@ def main():
     af = layer.attn_work()
     attn_s = r["stage_ms"][Layer.STAGES.index("attn_fwd")] * 1e-3
     achieved = af / attn_s / 1e12
+    decode = measure_decode(layer)
 
     sweep = {}
     if not args.no_sweep:
@@ -295,6 +328,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": pmc_traffic()},
         "gated_layer_128k": head,
+        "decode_128k": decode,
         "sweep_32k": sweep,
         "cpu_baseline": cpu,
     }

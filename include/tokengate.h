@@ -219,6 +219,47 @@ int tg_attn_forward(const void* q, int64_t q_row_stride, const float* head_gain,
                     double rope_base, void* out, float* lse, const void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* Workspace bytes tg_attn_decode needs for its per-split partials. */
+size_t tg_attn_decode_workspace_bytes(int32_t n_seqs, int32_t max_kept_seqlen, int32_t n_q_heads,
+                                      int32_t head_dim);
+
+/*
+ * One decode step of token-gated attention over the kept-only cache that
+ * tg_attn_prepare wrote (spke.com article, pruned-forward phase: above the
+ * gate only kept tokens have keys and values; token-gated attention section:
+ * each kept key keeps its gate-score bias).  The pages do not describe
+ * decoding; this is the prefill logit for one new query per sequence:
+ *     l_j = <R(q_s, q_pos[s]), R(k_j, pos_j)> / (sqrt(D) * tau) + head_gain[h] * key_score[j]
+ * over the kept keys j of sequence s with pos_j <= q_pos[s]; O = softmax_j(l) V,
+ * lse[h][s] = log sum_j exp(l_j).  The new token's own key is attended only
+ * if the caller placed it in the cache.  A query that sees no key gets O = 0
+ * and lse = -inf.  fp32 logits, probabilities and sums (no bf16 rounding of
+ * q or P); the keys and values are the cache's bf16.
+ *   q             [device] bf16, sequence s head h at q + s*q_row_stride + h*D
+ *   q_pos         [device] n_seqs int32 original position of each new query
+ *   head_gain, tau  as for tg_keybias_attn_prefill
+ *   pos           [device] n_kept_total int32: the kept positions the cache
+ *                 was prepared with
+ *   cu_kept, n_seqs, n_kept_total, n_kv_heads, head_dim, rope_base: those of
+ *                 the tg_attn_prepare call that filled `cache` (which must
+ *                 precede this call in stream order; the cache is only read)
+ *   max_kept_seqlen  host upper bound of max_s M_s
+ *   cache         [device] that tg_attn_prepare workspace, cache_bytes >=
+ *                 tg_attn_workspace_bytes(n_seqs, n_kept_total, n_kv_heads, head_dim)
+ *   out           [device, out] bf16 n_seqs x n_q_heads x D, dense
+ *   lse           [device, out] fp32 n_q_heads x n_seqs, or NULL
+ *   workspace     [device] >= tg_attn_decode_workspace_bytes(...) bytes, 256-B
+ *                 aligned, overwritten
+ * Requirements: head_dim in {64, 128}; group size Hq/Hkv in {1, 2, 4, 8};
+ * q_row_stride >= Hq*D.  Errors as for the prefill; nothing is launched
+ * unless every check passes.
+ */
+int tg_attn_decode(const void* q, int64_t q_row_stride, const int32_t* q_pos, const float* head_gain,
+                   float tau, const int32_t* pos, const int32_t* cu_kept, int32_t n_seqs,
+                   int64_t n_kept_total, int32_t max_kept_seqlen, int32_t n_q_heads, int32_t n_kv_heads,
+                   int32_t head_dim, double rope_base, const void* cache, size_t cache_bytes, void* out,
+                   float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,6 +10,8 @@ from . import _lib  # noqa: F401
 from ._lib import (  # noqa: F401
     TokenGateError,
     load,
+    tg_attn_decode,
+    tg_attn_decode_workspace_bytes,
     tg_attn_forward,
     tg_attn_prepare,
     tg_attn_workspace_bytes,

@@ -37,6 +37,9 @@ SIGNATURES = {
     "tg_attn_prepare": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _D, _P, _SZ, _P]),
     "tg_attn_forward": (ctypes.c_int, [_P, _I64, _P, _F, _P, _I32, _I64, _I32, _I32, _I32, _I32, _D, _P, _P,
                                        _P, _SZ, _P]),
+    "tg_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "tg_attn_decode": (ctypes.c_int, [_P, _I64, _P, _P, _F, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _D, _P,
+                                      _SZ, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -229,3 +232,36 @@ def tg_keybias_attn_prefill(q, k, v, key_score, head_gain, tau: float, pos, cu_k
                                         _ptr(lse), _ptr(workspace), workspace.numel(), _stream(q))
     _check("tg_keybias_attn_prefill", st)
     return out, lse
+
+
+def tg_attn_decode_workspace_bytes(n_seqs, max_kept_seqlen, n_q_heads, head_dim) -> int:
+    return int(load().tg_attn_decode_workspace_bytes(n_seqs, max_kept_seqlen, n_q_heads, head_dim))
+
+
+def tg_attn_decode(q, q_pos, head_gain, tau: float, pos, cu_kept, max_kept_seqlen: int, n_kv_heads: int, cache,
+                   rope_base: float = 1e6, out=None, lse=None, want_lse: bool = True, workspace=None):
+    """One new query per sequence over a cache filled by tg_attn_prepare.
+
+    q: [S, Hq, D] bf16 (row stride between sequences allowed); q_pos: [S] int32;
+    pos, cu_kept: the kept positions and offsets the cache was prepared with.
+    Returns (out [S, Hq, D] bf16, lse [Hq, S] fp32 or None).
+    """
+    if q.dim() != 3 or q.dtype != torch.bfloat16 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+        raise ValueError("q must be bf16 [S, Hq, D] with contiguous heads")
+    n_seqs, hq, d = q.shape
+    m = int(pos.shape[0])
+    dev = q.device
+    if out is None:
+        out = torch.empty((n_seqs, hq, d), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((hq, n_seqs), dtype=torch.float32, device=dev)
+    need = tg_attn_decode_workspace_bytes(n_seqs, int(max_kept_seqlen), hq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = load().tg_attn_decode(_ptr(q), q.stride(0), _ptr(q_pos), _ptr(head_gain), float(tau), _ptr(pos),
+                               _ptr(cu_kept), n_seqs, m, int(max_kept_seqlen), hq, int(n_kv_heads), d,
+                               float(rope_base), _ptr(cache), cache.numel(), _ptr(out), _ptr(lse), _ptr(workspace),
+                               workspace.numel(), _stream(q))
+    _check("tg_attn_decode", st)
+    return out, lse
+

@@ -64,6 +64,32 @@ size_t attn_workspace_layout(int n_seqs, int64_t m_tot, int hkv, int d, size_t* 
 int launch_attn_prep(const AttnArgs& a, hipStream_t st);
 int launch_attn_fwd(const AttnArgs& a, hipStream_t st);
 
+struct DecodeArgs {
+    const bf16* q;          // [n_seqs] rows of [Hq][D], q_stride elements apart
+    int64_t q_stride;
+    const int* q_pos;       // [n_seqs] original position of each new query
+    const float* gain;
+    float qk_scale_log2;    // log2(e) / (sqrt(D) * tau)
+    const int* pos;         // [M] kept positions
+    const int* cu_kept;
+    int n_seqs;
+    int64_t m_tot;
+    int max_kept_seqlen;
+    int hq, hkv, d;
+    double rope_log2_base;
+    bool rope;
+    const bf16* ws_k;       // the prepared cache (see AttnArgs)
+    const bf16* ws_vt;
+    int64_t mp;
+    bf16* out;              // [n_seqs][Hq][D]
+    float* lse;             // [Hq][n_seqs] or null
+    void* ws;               // decode partials
+};
+int decode_chunks(int max_kept_seqlen);
+size_t decode_part_o_bytes(int n_seqs, int max_kept_seqlen, int hq, int d);
+size_t decode_workspace_bytes(int n_seqs, int max_kept_seqlen, int hq, int d);
+int launch_attn_decode(const DecodeArgs& a, hipStream_t st);
+
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
 // lane l writes LDS bytes [ldst + 16 l, ldst + 16 l + 16); ldst must be the
 // same for the whole wave.

@@ -185,6 +185,33 @@ def test_attn_prepare_forward_validation(lib):
     assert f(m=0) == 0
 
 
+def test_attn_decode_validation(lib):
+    L = lib
+    cache = L.tg_attn_workspace_bytes(1, 100, 8, 128)
+    need = L.tg_attn_decode_workspace_bytes(1, 100, 16, 128)
+    assert need >= 2 * 16 * 128 * 4 and L.tg_attn_decode_workspace_bytes(1, 100, 16, 96) == 0
+    a = lambda **kw: L.tg_attn_decode(*[kw.get(k, v) for k, v in [
+        ("q", FAKE), ("qs", 2048), ("qp", FAKE), ("g", FAKE), ("tau", 0.9), ("pos", FAKE), ("ck", FAKE),
+        ("ns", 1), ("m", 100), ("mx", 100), ("hq", 16), ("hkv", 8), ("d", 128), ("rb", 1e6), ("cache", FAKE),
+        ("cb", cache), ("out", FAKE), ("lse", None), ("ws", FAKE), ("wsb", need), ("st", None)]])
+    assert a(tau=0.0) == 1
+    assert a(rb=float("nan")) == 1
+    assert a(hq=12) == 1               # not a multiple of Hkv
+    assert a(d=96) == 2                # unsupported head_dim
+    assert a(hq=24, qs=3072) == 2      # group size 3
+    assert a(qs=2000) == 1             # stride below Hq * D
+    assert a(mx=101) == 1              # longer than the total
+    assert a(mx=0) == 1                # kept keys but no length
+    assert a(q=None) == 1
+    assert a(qp=None) == 1
+    assert a(pos=None) == 1
+    assert a(cb=cache - 1) == 3        # cache smaller than the prepared layout
+    assert a(cache=ctypes.c_void_p(0x1010)) == 3
+    assert a(wsb=need - 1) == 3
+    assert a(ws=ctypes.c_void_p(0x1010)) == 3
+    assert a(ns=0) == 0                # nothing to do, nothing launched
+
+
 def test_library_has_no_undefined_internal_symbols(lib):
     """Every kernel stub must be defined: an undefined tg:: symbol only shows
     up when the library is loaded for real."""

@@ -393,6 +393,86 @@ def test_attention_prepare_layout():
     assert ec <= 1e-5 and es <= 1e-5
 
 
+# ------------------------------------------------------------------ decode ----
+def _run_decode(c, q_new, q_pos, rope_base):
+    ck = c["ck"]
+    maxlen = int(np.diff(ck).max()) if len(ck) > 1 else 0
+    hkv = c["k"].shape[1]
+    ws = tg.tg_attn_prepare(_dev(c["k"]), _dev(c["v"]), _dev(c["sk"]), _i32(c["pk"]), _i32(ck), rope_base=rope_base)
+    out, lse = tg.tg_attn_decode(_dev(q_new), _i32(q_pos), _dev(c["gain"]), c["tau"], _i32(c["pk"]), _i32(ck),
+                                 maxlen, hkv, ws, rope_base=rope_base)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _check_decode(c, q_new, q_pos, rope_base, out, lse):
+    f = lambda t: t.float().numpy()
+    ref_o, ref_l = oracle.keybias_decode(f(q_new), q_pos, f(c["k"]), f(c["v"]), c["sk"], c["gain"], c["tau"],
+                                         c["pk"], c["ck"], rope_base=rope_base)
+    assert np.isfinite(out).all()
+    eo = np.abs(out - ref_o).max()
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(np.isfinite(lse), fin)
+    el = np.abs(lse[fin] - ref_l[fin]).max() if fin.any() else 0.0
+    print(f"   max|dO|={eo:.3g} max|dLSE|={el:.3g}", flush=True)
+    assert eo <= ATTN_TOL and el <= ATTN_TOL
+
+
+def _new_queries(c, seed, offset=1):
+    ck, pk = c["ck"], c["pk"]
+    n_seqs, hq, d = len(ck) - 1, c["q"].shape[1], c["q"].shape[2]
+    g = torch.Generator().manual_seed(seed)
+    q_new = torch.randn(n_seqs, hq, d, generator=g).to(torch.bfloat16)
+    last = np.array([pk[ck[i + 1] - 1] if ck[i + 1] > ck[i] else 0 for i in range(n_seqs)], dtype=np.int64)
+    return q_new, (last + offset).astype(np.int32)
+
+
+@pytest.mark.parametrize("name", ["tiny", "16k", "128k", "varlen"])
+def test_decode_configs(name):
+    """One new query per sequence, one position past the last kept token, over the
+    kept-only cache of the workload's prefill."""
+    _print_case(f"decode {name}")
+    w = workloads.by_name(name)
+    c = _attn_case(w)
+    q_new, q_pos = _new_queries(c, 7)
+    out, lse = _run_decode(c, q_new, q_pos, w.rope_base)
+    _check_decode(c, q_new, q_pos, w.rope_base, out, lse)
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(64, 4, 4), (64, 8, 2), (128, 16, 8), (128, 8, 1), (128, 16, 2)])
+@pytest.mark.parametrize("rope", [0.0, 1e6])
+def test_decode_shapes_ragged(d, hq, hkv, rope):
+    """Ragged kept lengths (an empty sequence, one key, tile and chunk edges)."""
+    lens = [0, 1, 63, 64, 65, 200, 129]
+    w = workloads.custom([n + 8 for n in lens], [8 if n else 0 for n in lens], [max(n - 8, 0) for n in lens],
+                         n_q_heads=hq, n_kv_heads=hkv, head_dim=d, seed=d + hq + hkv + 3, tau=0.91)
+    _print_case(f"decode shape d={d} hq={hq} hkv={hkv} rope={rope}")
+    c = _attn_case(w)
+    q_new, q_pos = _new_queries(c, d + hq, offset=5)
+    out, lse = _run_decode(c, q_new, q_pos, rope)
+    _check_decode(c, q_new, q_pos, rope, out, lse)
+
+
+def test_decode_position_mask_and_empty():
+    """A query inside a sequence sees only the keys at or before its position; one
+    before every key gets O = 0, LSE = -inf; decode at a kept token's own
+    position with its own q matches the prefill row (both against the oracle)."""
+    w = workloads.custom([700, 400, 300], [30, 20, 10], [300, 150, 90], n_q_heads=8, n_kv_heads=2,
+                         head_dim=128, seed=41)
+    _print_case("decode masks")
+    c = _attn_case(w)
+    ck, pk = c["ck"], c["pk"]
+    q_new, _ = _new_queries(c, 3)
+    q_pos = np.array([pk[ck[0] + 100], pk[ck[1]] - 1, pk[ck[3] - 1] + 9], dtype=np.int32)
+    out, lse = _run_decode(c, q_new, q_pos, 1e6)
+    _check_decode(c, q_new, q_pos, 1e6, out, lse)
+    assert not out[1].any() and np.all(lse[:, 1] == -np.inf)
+    rows = np.array([ck[0] + 37, ck[2] - 1, ck[2] + 5])
+    q_own = c["q"][rows].contiguous()
+    out2, lse2 = _run_decode(c, q_own, pk[rows].astype(np.int32), 1e6)
+    _check_decode(c, q_own, pk[rows].astype(np.int32), 1e6, out2, lse2)
+
+
 # --------------------------------------------------------------- end to end ----
 @pytest.mark.parametrize("name", ["tiny", "16k"])
 def test_gated_layer_end_to_end(name):
