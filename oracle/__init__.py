@@ -12,7 +12,10 @@ from .tokengate_oracle import (  # noqa: F401
     keybias_attention,
     keybias_decode,
     kept_counts,
+    random_k_select,
+    random_scores,
     rope,
     silu,
+    splitmix64,
     topk_select,
 )

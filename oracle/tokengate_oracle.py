@@ -25,6 +25,9 @@ each function's docstring.
 Parity status per function:
   gate_score          pinned (torch fp64 linear+silu, closed forms, scalar loop)
   topk_select         pinned (brute-force sort, exhaustive tiny cases, invariants)
+  splitmix64          pinned (published reference outputs for seed 0)
+  random_k_select     pinned (budget and question invariants, determinism, selection
+                      frequencies uniform over seeds)
   gather_kept         pinned (definition, invariants)
   rope                pinned (complex-rotation form, norm and relative-position
                       invariants)
@@ -154,6 +157,44 @@ def topk_select(scores, cu_seqlens, doc_begin, doc_end, k_doc):
     kept = np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
     assert kept.shape[0] == cu_kept[-1]
     return kept, cu_kept
+
+
+def splitmix64(seed: int, n: int) -> np.ndarray:
+    """The first n outputs of SplitMix64 seeded with `seed` (uint64).
+
+    SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+    generators", OOPSLA 2014; the 64-bit finalizer of Vigna's reference
+    implementation): the state advances by the golden-ratio increment
+    0x9E3779B97F4A7C15 and each state is mixed by two xor-shift-multiply
+    rounds and a final xor-shift.  Output i depends only on seed + (i+1)
+    increments, so it is a counter-based generator.
+    """
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed) + (np.arange(1, n + 1, dtype=np.uint64) * np.uint64(0x9E3779B97F4A7C15))
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+        return z ^ (z >> np.uint64(31))
+
+
+def random_scores(seed: int, n: int) -> np.ndarray:
+    """Uniform random scores in [0, 1) for n tokens: the top 24 bits of
+    SplitMix64 output t (t = global token index), times 2^-24 (exact in fp32)."""
+    return ((splitmix64(seed, n) >> np.uint64(40)).astype(np.float64) * 2.0 ** -24).astype(np.float32)
+
+
+def random_k_select(seed, cu_seqlens, doc_begin, doc_end, k_doc):
+    """Random-K selector mode ([RU] "Техническая реализация" and the ablation the
+    pages report: random token selection on the co-adapted backbone).
+
+    Reading: the same budget and the same always-kept question as the learned
+    selector, but the K_eff document tokens of each sequence are a seeded
+    uniform random subset: the selector of topk_select applied to
+    random_scores(seed, N_tot) instead of the gate's scores (24-bit scores, so
+    equal draws are possible and keep the lower index, as for gate scores).
+    Returns (kept_idx, cu_kept) as topk_select does.
+    """
+    n = int(np.asarray(cu_seqlens)[-1])
+    return topk_select(random_scores(seed, n), cu_seqlens, doc_begin, doc_end, k_doc)
 
 
 # ----------------------------------------------------------------------------

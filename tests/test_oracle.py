@@ -402,3 +402,58 @@ def test_decode_shift_invariance():
     o2, l2 = oracle.keybias_decode(q[[3, 12]], qp, k, v, s - 1.5, g, 0.9, pos, ck)
     np.testing.assert_allclose(o1, o2, atol=1e-12)
     np.testing.assert_allclose(l1 - l2, (g * 1.5)[:, None] * np.ones((1, 2)), atol=1e-12)
+
+
+# -------------------------------------------------------------- random-K ----
+def test_splitmix64_reference_outputs():
+    """SplitMix64 seeded with 0 (Steele, Lea and Flood 2014; Vigna's reference
+    implementation) starts 0xe220a8397b1dcdaf, 0x6e789e6aa1b965f4, 0x06c45d188009454f."""
+    got = oracle.splitmix64(0, 3)
+    assert [int(x) for x in got] == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    # counter-based: output i of seed s is output 0 of seed s + i * increment
+    g = 0x9E3779B97F4A7C15
+    a = oracle.splitmix64(12345, 6)
+    for i in range(6):
+        assert int(oracle.splitmix64((12345 + i * g) % 2 ** 64, 1)[0]) == int(a[i])
+
+
+def test_random_scores_exact_24_bit_grid():
+    s = oracle.random_scores(7, 1000)
+    assert s.dtype == np.float32 and np.all((s >= 0) & (s < 1))
+    np.testing.assert_array_equal(s.astype(np.float64) * 2 ** 24, np.floor(s.astype(np.float64) * 2 ** 24))
+    raw = oracle.splitmix64(7, 1000)
+    np.testing.assert_array_equal((s.astype(np.float64) * 2 ** 24).astype(np.uint64), raw >> np.uint64(40))
+
+
+def test_random_k_budget_question_and_determinism():
+    cu = [0, 300, 350, 1000]
+    db, de, kd = [0, 0, 0], [280, 50, 600], [40, 60, 0]     # budgets: partial, above n_doc, zero
+    kept, ck = oracle.random_k_select(9, cu, db, de, kd)
+    np.testing.assert_array_equal(ck, oracle.kept_counts(cu, db, de, kd))
+    for i in range(3):
+        a, b = cu[i], cu[i + 1]
+        ks = kept[ck[i]:ck[i + 1]] - a
+        assert np.all(np.diff(ks) > 0)
+        assert set(range(de[i], b - a)) <= set(ks.tolist())          # question always kept
+        assert np.sum(ks < de[i]) == min(kd[i], de[i] - db[i])
+    k2, _ = oracle.random_k_select(9, cu, db, de, kd)
+    np.testing.assert_array_equal(kept, k2)
+    k3, _ = oracle.random_k_select(10, cu, db, de, kd)
+    assert not np.array_equal(kept, k3)
+
+
+def test_random_k_uniform_over_seeds():
+    """Each document token is kept with frequency K / n_doc over seeds (binomial
+    bound at ~5 sigma per token), and pairs of tokens are not correlated."""
+    n_doc, k, seeds = 40, 10, 2000
+    cnt = np.zeros(n_doc)
+    pair = 0
+    for sd in range(seeds):
+        kept, _ = oracle.random_k_select(sd, [0, n_doc + 4], [0], [n_doc], [k])
+        doc = kept[kept < n_doc]
+        cnt[doc] += 1
+        pair += (0 in doc) and (1 in doc)
+    p = k / n_doc
+    assert np.all(np.abs(cnt / seeds - p) <= 5 * np.sqrt(p * (1 - p) / seeds))
+    pp = k * (k - 1) / (n_doc * (n_doc - 1))                        # without-replacement pair rate
+    assert abs(pair / seeds - pp) <= 5 * np.sqrt(pp * (1 - pp) / seeds)
