@@ -11,8 +11,9 @@ synchronisations, no events inside), per-stage times from a second pass with
 HIP events recorded on the launch stream between the calls, the attention
 kernel's roofline against
 the bf16 MFMA peak, top-K + gather bandwidth against HBM, one decode step over
-the kept-only cache against HBM, the 32k budget sweep, and the CPU oracle timed
-on a bounded sample of the same workload.
+the kept-only cache against HBM, the same attention over all 131072 tokens (the
+full-prefill comparator), the 32k budget sweep, and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -175,6 +176,46 @@ def measure_decode(layer: Layer, steps=50, warmup=5):
             "kernels": "attn_decode_split_kernel + attn_decode_combine_kernel (tg_attn_decode)"}
 
 
+def measure_full_prefill(w: workloads.Workload, pruned_layer_ms: float, reps=3):
+    """The same attention at K = n_doc (every token kept, no gate/select/gather):
+    tg_attn_prepare + tg_attn_forward over all N tokens, beside the pruned layer,
+    as a per-layer analogue of the pages' full-vs-pruned prefill comparison."""
+    dev = torch.device("cuda:0")
+    n = w.n_tokens
+    ck = np.array([0, n], dtype=np.int32)
+    g = torch.Generator(device="cpu").manual_seed(4)
+    q = (torch.randn(n, w.n_q_heads, w.head_dim, generator=g)).to(torch.bfloat16).to(dev)
+    k = (torch.randn(n, w.n_kv_heads, w.head_dim, generator=g)).to(torch.bfloat16).to(dev)
+    v = (torch.randn(n, w.n_kv_heads, w.head_dim, generator=g)).to(torch.bfloat16).to(dev)
+    sk = torch.randn(n, generator=g).to(dev)
+    gain, tau = w.attn_params()
+    gain = torch.from_numpy(gain).to(dev)
+    pos = torch.arange(n, dtype=torch.int32, device=dev)
+    ckd = torch.from_numpy(ck).to(dev)
+    ws = torch.empty(tg.tg_attn_workspace_bytes(1, n, w.n_kv_heads, w.head_dim), dtype=torch.uint8, device=dev)
+    out = torch.empty((n, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.n_q_heads, n), dtype=torch.float32, device=dev)
+    prep = lambda: tg.tg_attn_prepare(k, v, sk, pos, ckd, rope_base=w.rope_base, workspace=ws)
+    fwd = lambda: tg.tg_attn_forward(q, gain, tau, ckd, n, w.n_kv_heads, ws, rope_base=w.rope_base, out=out, lse=lse)
+    prep(); fwd()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_prep, t_fwd = [], []
+    for _ in range(reps):
+        e[0].record(); prep(); e[1].record(); fwd(); e[2].record()
+        torch.cuda.synchronize()
+        t_prep.append(e[0].elapsed_time(e[1]))
+        t_fwd.append(e[1].elapsed_time(e[2]))
+    fl = attn_flops(ck, w.n_q_heads, w.head_dim)
+    fwd_ms, prep_ms = float(np.median(t_fwd)), float(np.median(t_prep))
+    del q, k, v, ws, out, lse
+    torch.cuda.empty_cache()
+    return {"tokens": n, "attn_prep_ms": round(prep_ms, 3), "attn_fwd_ms": round(fwd_ms, 3),
+            "attn_fwd_tflops": round(fl / fwd_ms / 1e9, 2),
+            "attn_fwd_frac_bf16_peak": round(fl / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "full_over_pruned_layer": round((prep_ms + fwd_ms) / pruned_layer_ms, 2)}
+
+
 def pmc_traffic():
     """HBM bytes per attention launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source (else None)."""
@@ -291,6 +332,9 @@ def main():
     attn_s = r["stage_ms"][Layer.STAGES.index("attn_fwd")] * 1e-3
     achieved = af / attn_s / 1e12
     decode = measure_decode(layer)
+    del layer
+    torch.cuda.empty_cache()
+    full = measure_full_prefill(w, r["wall_ms"])
 
     sweep = {}
     if not args.no_sweep:
@@ -322,13 +366,14 @@ def main():
         "config": {"workload": "128k: 1 sequence, N=131072 (130816 document + 256 question), keep 8192 "
                                "document tokens (M=8448), d_model 2048 bf16, gate 2048->256->1, 16 q / 8 kv "
                                "heads, head_dim 128, RoPE 1e6, causal key-bias attention over kept tokens",
-                   "global_batch": 1, "seq_len": w.n_tokens, "kept": layer.m, "parallelism": "none (1 GPU)"},
+                   "global_batch": 1, "seq_len": w.n_tokens, "kept": head["kept"], "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": "attn_fwd_kernel (tg_attn_forward)",
                      "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": pmc_traffic()},
         "gated_layer_128k": head,
         "decode_128k": decode,
+        "full_prefill_128k": full,
         "sweep_32k": sweep,
         "cpu_baseline": cpu,
     }

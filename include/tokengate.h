@@ -124,6 +124,27 @@ int tg_topk_select(const float* scores, int32_t n_seqs, int64_t n_tokens_total, 
                    const int32_t* k_doc, const int32_t* cu_kept, int32_t* kept_idx,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes tg_random_k_select needs: 4 bytes per token for the random
+ * scores plus what tg_topk_select needs. */
+size_t tg_random_k_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen);
+
+/*
+ * Random-K selector mode: the ablation the pages report, where a random
+ * token choice replaces the learned gate (aikraft.ru article, section
+ * "Техническая реализация").  Same budget, same always-kept question and same
+ * output as tg_topk_select, but the K_eff document tokens of each sequence
+ * are a seeded uniform random subset: tg_topk_select applied to the scores
+ * r_t = top 24 bits of SplitMix64 output t for `seed`, times 2^-24, where t
+ * is the global token index (SplitMix64: Steele, Lea and Flood, OOPSLA 2014;
+ * output t = finalizer of seed + (t+1) * 0x9E3779B97F4A7C15).  Equal draws
+ * keep the lower index.  Arguments, requirements and errors as for
+ * tg_topk_select, without `scores`; workspace >= tg_random_k_workspace_bytes.
+ */
+int tg_random_k_select(uint64_t seed, int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen,
+                       const int32_t* cu_seqlens, const int32_t* doc_begin, const int32_t* doc_end,
+                       const int32_t* k_doc, const int32_t* cu_kept, int32_t* kept_idx, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /*
  * Compaction of the kept set (spke.com article, pruned-forward phase: layers
  * above the gate see only the kept tokens and never create KV for the rest):

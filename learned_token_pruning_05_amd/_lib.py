@@ -37,6 +37,8 @@ SIGNATURES = {
     "tg_attn_prepare": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _D, _P, _SZ, _P]),
     "tg_attn_forward": (ctypes.c_int, [_P, _I64, _P, _F, _P, _I32, _I64, _I32, _I32, _I32, _I32, _D, _P, _P,
                                        _P, _SZ, _P]),
+    "tg_random_k_workspace_bytes": (_SZ, [_I32, _I64, _I32]),
+    "tg_random_k_select": (ctypes.c_int, [ctypes.c_uint64, _I32, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tg_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "tg_attn_decode": (ctypes.c_int, [_P, _I64, _P, _P, _F, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _D, _P,
                                       _SZ, _P, _P, _P, _SZ, _P]),
@@ -142,6 +144,24 @@ def tg_topk_select(scores, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, n_kep
                             _ptr(doc_end), _ptr(k_doc), _ptr(cu_kept), _ptr(kept_idx), _ptr(workspace),
                             workspace.numel(), _stream(scores))
     _check("tg_topk_select", st)
+    return kept_idx
+
+
+def tg_random_k_select(seed: int, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, n_tokens: int, n_kept_total: int,
+                       max_seqlen: int, kept_idx=None, workspace=None):
+    """Random-K selector mode: as tg_topk_select over seeded SplitMix64 scores."""
+    n_seqs = cu_seqlens.shape[0] - 1
+    dev = cu_seqlens.device
+    if kept_idx is None:
+        kept_idx = torch.empty(n_kept_total, dtype=torch.int32, device=dev)
+    lib = load()
+    if workspace is None:
+        need = lib.tg_random_k_workspace_bytes(n_seqs, n_tokens, max_seqlen)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.tg_random_k_select(int(seed) % (1 << 64), n_seqs, n_tokens, max_seqlen, _ptr(cu_seqlens),
+                                _ptr(doc_begin), _ptr(doc_end), _ptr(k_doc), _ptr(cu_kept), _ptr(kept_idx),
+                                _ptr(workspace), workspace.numel(), _stream(cu_seqlens))
+    _check("tg_random_k_select", st)
     return kept_idx
 
 

@@ -87,6 +87,27 @@ int tg_topk_select(const float* scores, int32_t n_seqs, int64_t n_tokens_total, 
                        k_doc, cu_kept, kept_idx, workspace, (hipStream_t)stream);
 }
 
+size_t tg_random_k_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen) {
+    if (n_seqs < 0 || n_tokens_total < 0 || max_seqlen < 0) return 0;
+    return random_k_workspace_bytes(n_seqs, n_tokens_total, max_seqlen);
+}
+
+int tg_random_k_select(uint64_t seed, int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen,
+                       const int32_t* cu_seqlens, const int32_t* doc_begin, const int32_t* doc_end,
+                       const int32_t* k_doc, const int32_t* cu_kept, int32_t* kept_idx, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (n_seqs < 0 || n_tokens_total < 0 || n_tokens_total > INT32_MAX || max_seqlen < 0 ||
+        max_seqlen > n_tokens_total)
+        return TG_ERR_INVALID_ARG;
+    if (max_seqlen > topk_max_seqlen()) return TG_ERR_UNSUPPORTED;
+    if (n_seqs == 0 || n_tokens_total == 0) return TG_OK;
+    if (!cu_seqlens || !doc_begin || !doc_end || !k_doc || !cu_kept || !kept_idx) return TG_ERR_INVALID_ARG;
+    const size_t need = random_k_workspace_bytes(n_seqs, n_tokens_total, max_seqlen);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return TG_ERR_WORKSPACE;
+    return launch_random_k(seed, n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end, k_doc,
+                           cu_kept, kept_idx, workspace, (hipStream_t)stream);
+}
+
 int tg_gather_kept(const void* x, int32_t x_dtype, int32_t d_model, int64_t x_row_stride,
                    const float* scores, const int32_t* kept_idx, int64_t n_kept_total,
                    int32_t n_seqs, const int32_t* cu_seqlens, const int32_t* cu_kept,

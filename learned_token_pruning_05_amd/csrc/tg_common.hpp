@@ -30,6 +30,10 @@ int topk_max_seqlen();
 int launch_topk(const float* scores, int n_seqs, int64_t n_tokens, int max_seqlen,
                 const int* cu_seqlens, const int* doc_begin, const int* doc_end, const int* k_doc,
                 const int* cu_kept, int* kept_idx, void* ws, hipStream_t st);
+size_t random_k_workspace_bytes(int n_seqs, int64_t n_tokens, int max_seqlen);
+int launch_random_k(uint64_t seed, int n_seqs, int64_t n_tokens, int max_seqlen, const int* cu_seqlens,
+                    const int* doc_begin, const int* doc_end, const int* k_doc, const int* cu_kept,
+                    int* kept_idx, void* ws, hipStream_t st);
 int launch_gather(const void* x, int esize, int d_model, int64_t x_stride, const float* scores,
                   const int* kept_idx, int64_t m_tot, int n_seqs, const int* cu_seqlens,
                   const int* cu_kept, void* x_kept, float* s_kept, int* pos_kept, hipStream_t st);

@@ -489,7 +489,37 @@ TopkLayout topk_layout(int n_seqs, int64_t n_tokens, int max_seqlen) {
     return L;
 }
 
+// Random-K selector mode: uniform scores in [0, 1) from SplitMix64 (Steele,
+// Lea and Flood 2014): output t of the generator seeded with `seed` is the
+// finalizer of seed + (t+1) * 0x9E3779B97F4A7C15, so each token's draw is
+// independent of the others; the top 24 bits times 2^-24 are exact in fp32.
+__global__ __launch_bounds__(256) void random_scores_kernel(uint64_t seed, int64_t n, float* __restrict__ out) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= n) return;
+    uint64_t z = seed + (uint64_t)(t + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    out[t] = (float)(uint32_t)(z >> 40) * 0x1p-24f;
+}
+
 }  // namespace
+
+size_t random_k_workspace_bytes(int n_seqs, int64_t n_tokens, int max_seqlen) {
+    return al256((size_t)n_tokens * 4) + topk_workspace_bytes(n_seqs, n_tokens, max_seqlen);
+}
+
+int launch_random_k(uint64_t seed, int n_seqs, int64_t n_tokens, int max_seqlen, const int* cu_seqlens,
+                    const int* doc_begin, const int* doc_end, const int* k_doc, const int* cu_kept,
+                    int* kept_idx, void* ws, hipStream_t stm) {
+    if (n_seqs == 0 || n_tokens == 0) return TG_OK;
+    float* sc = (float*)ws;
+    hipLaunchKernelGGL(random_scores_kernel, dim3((unsigned)((n_tokens + 255) / 256)), dim3(256), 0, stm, seed,
+                       n_tokens, sc);
+    if (hipGetLastError() != hipSuccess) return TG_ERR_HIP;
+    return launch_topk(sc, n_seqs, n_tokens, max_seqlen, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, kept_idx,
+                       (char*)ws + al256((size_t)n_tokens * 4), stm);
+}
 
 size_t topk_workspace_bytes(int n_seqs, int64_t n_tokens, int max_seqlen) {
     return topk_layout(n_seqs, n_tokens, max_seqlen).total;

@@ -212,6 +212,23 @@ def test_attn_decode_validation(lib):
     assert a(ns=0) == 0                # nothing to do, nothing launched
 
 
+def test_random_k_validation(lib):
+    L = lib
+    need = L.tg_random_k_workspace_bytes(2, 1000, 600)
+    assert need >= 1000 * 4 + L.tg_topk_workspace_bytes(2, 1000, 600)
+    a = lambda **kw: L.tg_random_k_select(*[kw.get(k, v) for k, v in [
+        ("seed", 5), ("ns", 2), ("n", 1000), ("mx", 600), ("cu", FAKE), ("db", FAKE), ("de", FAKE), ("kd", FAKE),
+        ("ck", FAKE), ("out", FAKE), ("ws", FAKE), ("wsb", need), ("st", None)]])
+    assert a(n=-1) == 1
+    assert a(mx=1001) == 1            # longer than the total
+    assert a(cu=None) == 1
+    assert a(out=None) == 1
+    assert a(wsb=need - 1) == 3
+    assert a(ws=ctypes.c_void_p(0x1010)) == 3
+    assert a(ns=0) == 0
+    assert a(n=0, mx=0) == 0
+
+
 def test_library_has_no_undefined_internal_symbols(lib):
     """Every kernel stub must be defined: an undefined tg:: symbol only shows
     up when the library is loaded for real."""

@@ -197,6 +197,19 @@ def test_topk_deterministic_repeat():
 
 
 # ----------------------------------------------------------------- gather ----
+@pytest.mark.parametrize("name,seed", [("tiny", 0), ("16k", 1), ("128k", 2), ("varlen", 3), ("32k@25%", 2 ** 64 - 1)])
+def test_random_k_bit_exact(name, seed):
+    """Random-K selector mode: bit-exact against the oracle's SplitMix64 scores
+    and selector, every config shape, seeds up to 2^64 - 1."""
+    _print_case(f"random-K {name} seed={seed}")
+    w = workloads.by_name(name)
+    kept_ref, ck = oracle.random_k_select(seed, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+    kept = tg.tg_random_k_select(seed, _i32(w.cu_seqlens), _i32(w.doc_begin), _i32(w.doc_end), _i32(w.k_doc_arr),
+                                 _i32(ck), w.n_tokens, int(ck[-1]), int(max(w.seqlens)))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kept.cpu().numpy(), kept_ref)
+
+
 @pytest.mark.parametrize("name", ["tiny", "16k", "128k", "varlen"])
 def test_gather_bit_exact(name):
     _print_case(f"gather {name}")
