@@ -10,6 +10,7 @@ from .tokengate_oracle import (  # noqa: F401
     gated_layer,
     gather_kept,
     keybias_attention,
+    keybias_attention_gate_grads,
     keybias_decode,
     kept_counts,
     random_k_select,

@@ -33,6 +33,9 @@ Parity status per function:
                       invariants)
   keybias_attention   pinned (textbook causal SDPA reduction, shift invariance,
                       pruning == masking, tau placement, GQA, varlen, closed forms)
+  keybias_attention_gate_grads
+                      pinned (central finite differences of the forward, closed
+                      forms: g = 0 gives ds = 0, sum_j ds_j = 0, tau scaling)
   keybias_decode      pinned (equals the prefill row of a kept token placed at its
                       position, closed forms, no-visible-key case, shift invariance)
 """
@@ -309,6 +312,67 @@ def keybias_attention(q, k, v, s_kept, gain, tau, pos, cu_kept,
                 out[a + ri, h, :] = (e @ vs[:, hk, :]) / den
                 lse[h, a + ri] = (mx + np.log(den))[:, 0]
     return out, lse
+
+
+def keybias_attention_gate_grads(q, k, v, s_kept, gain, tau, pos, cu_kept, d_out, rope_base: float = 1e6):
+    """Gradients of a loss L through token-gated attention with respect to the
+    gate-side parameters: the kept keys' scores s_j, the per-head gains g_h and
+    the temperature tau, given dL/dO ([ES] "¿Qué es la atención…?": the gain and
+    the temperature are learned, and the bias is how the loss reaches the gate's
+    scores during training).
+
+    From the forward definition (keybias_attention), per sequence and q head h:
+        P_ij = softmax_j(l_ij),  dP_ij = <dO_i, v_j>,  Delta_i = sum_j P_ij dP_ij,
+        dS_ij = P_ij (dP_ij - Delta_i)      (= dL/dl_ij)
+    and with l_ij = <q~_i, k~_j> / (sqrt(D) tau) + g_h s_j:
+        dL/ds_j  = sum_h g_h sum_i dS_hij
+        dL/dg_h  = sum_ij s_j dS_hij
+        dL/dtau  = sum_hij dS_hij * (-<q~_i, k~_j> / (sqrt(D) tau^2)).
+    d_out: [M, Hq, D].  Returns (ds [M], dg [Hq], dtau) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    s_kept = np.asarray(s_kept, dtype=np.float64)
+    gain = np.asarray(gain, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    ck = np.asarray(cu_kept, dtype=np.int64)
+    m_tot, hq, d = q.shape
+    hkv = k.shape[1]
+    if hq % hkv != 0:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    if not (tau > 0 and math.isfinite(tau)):
+        raise ValueError("tau must be positive and finite")
+    grp = hq // hkv
+    scale = 1.0 / (math.sqrt(d) * float(tau))
+    ds = np.zeros(m_tot)
+    dg = np.zeros(hq)
+    dtau = 0.0
+    for si in range(len(ck) - 1):
+        a, b = int(ck[si]), int(ck[si + 1])
+        if a == b:
+            continue
+        p = pos[a:b]
+        qr = rope(q[a:b], p, rope_base)
+        kr = rope(k[a:b], p, rope_base)
+        vs = v[a:b]
+        mask = p[None, :] > p[:, None]
+        for h in range(hq):
+            hk = h // grp
+            qk = (qr[:, h, :] @ kr[:, hk, :].T) * scale
+            logit = qk + gain[h] * s_kept[a:b][None, :]
+            logit[mask] = -np.inf
+            e = np.exp(logit - logit.max(axis=1, keepdims=True))
+            pr = e / e.sum(axis=1, keepdims=True)
+            dp = d_out[a:b, h, :] @ vs[:, hk, :].T
+            delta = (pr * dp).sum(axis=1, keepdims=True)
+            dsm = pr * (dp - delta)
+            col = dsm.sum(axis=0)
+            ds[a:b] += gain[h] * col
+            dg[h] += float(s_kept[a:b] @ col)
+            dtau += float((dsm * (-qk / float(tau))).sum())
+    return ds, dg, dtau
 
 
 def keybias_decode(q_new, q_pos, k, v, s_kept, gain, tau, pos, cu_kept, rope_base: float = 1e6):

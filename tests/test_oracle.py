@@ -457,3 +457,48 @@ def test_random_k_uniform_over_seeds():
     assert np.all(np.abs(cnt / seeds - p) <= 5 * np.sqrt(p * (1 - p) / seeds))
     pp = k * (k - 1) / (n_doc * (n_doc - 1))                        # without-replacement pair rate
     assert abs(pair / seeds - pp) <= 5 * np.sqrt(pp * (1 - pp) / seeds)
+
+
+# ------------------------------------------------------- gate-side gradients ----
+def _grad_case(seed, lens, hq, hkv, d):
+    r = np.random.default_rng(seed)
+    ck = np.concatenate([[0], np.cumsum(lens)])
+    m = int(ck[-1])
+    q, k, v = (r.standard_normal((m, h, d)) for h in (hq, hkv, hkv))
+    s = r.standard_normal(m)
+    g = r.uniform(0.5, 2, hq)
+    pos = np.concatenate([np.sort(r.choice(300, L, replace=False)) for L in lens])
+    d_out = r.standard_normal((m, hq, d))
+    return q, k, v, s, g, pos, ck, d_out
+
+
+@pytest.mark.parametrize("base", [0.0, 1e6])
+def test_gate_grads_match_finite_differences(base):
+    """Central differences of L = sum(dO * O) from the (independently pinned)
+    forward oracle, for every s_j, every g_h and tau."""
+    q, k, v, s, g, pos, ck, d_out = _grad_case(51, [6, 1, 9], 4, 2, 8)
+    tau = 0.9
+    loss = lambda s_, g_, t_: float((d_out * oracle.keybias_attention(q, k, v, s_, g_, t_, pos, ck,
+                                                                      rope_base=base)[0]).sum())
+    ds, dg, dtau = oracle.keybias_attention_gate_grads(q, k, v, s, g, tau, pos, ck, d_out, rope_base=base)
+    h = 1e-5
+    fd_s = np.array([(loss(s + h * e, g, tau) - loss(s - h * e, g, tau)) / (2 * h) for e in np.eye(len(s))])
+    fd_g = np.array([(loss(s, g + h * e, tau) - loss(s, g - h * e, tau)) / (2 * h) for e in np.eye(len(g))])
+    fd_t = (loss(s, g, tau + h) - loss(s, g, tau - h)) / (2 * h)
+    np.testing.assert_allclose(ds, fd_s, atol=1e-7)
+    np.testing.assert_allclose(dg, fd_g, atol=1e-7)
+    assert abs(dtau - fd_t) <= 1e-7
+
+
+def test_gate_grads_closed_forms():
+    q, k, v, s, g, pos, ck, d_out = _grad_case(52, [10, 7], 4, 1, 16)
+    ds, dg, dtau = oracle.keybias_attention_gate_grads(q, k, v, s, g, 0.8, pos, ck, d_out)
+    # softmax rows sum to one: sum_j dS_ij = 0, so the scores' gradient sums to zero per sequence
+    for i in range(len(ck) - 1):
+        assert abs(ds[ck[i]:ck[i + 1]].sum()) <= 1e-10
+    # no gain: the loss does not see the scores
+    ds0, _, _ = oracle.keybias_attention_gate_grads(q, k, v, s, np.zeros(4), 0.8, pos, ck, d_out)
+    assert np.abs(ds0).max() == 0.0
+    # (q, tau) -> (c q, c tau) leaves the forward unchanged, so c dL/dtau(c q, c tau) = dL/dtau(q, tau)
+    _, _, dt2 = oracle.keybias_attention_gate_grads(2.0 * q, k, v, s, g, 1.6, pos, ck, d_out)
+    assert abs(2.0 * dt2 - dtau) <= 1e-10 * max(1.0, abs(dtau))
