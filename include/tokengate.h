@@ -281,6 +281,53 @@ int tg_attn_decode(const void* q, int64_t q_row_stride, const int32_t* q_pos, co
                    int32_t head_dim, double rope_base, const void* cache, size_t cache_bytes, void* out,
                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes tg_attn_gate_grads needs: the prepared queries (Hq rows of
+ * D+16 bf16 per padded kept row) plus four fp32 values per q head and kept
+ * token and a few per-block partials. */
+size_t tg_attn_gate_grads_workspace_bytes(int32_t n_seqs, int64_t n_kept_total, int32_t max_kept_seqlen,
+                                          int32_t n_q_heads, int32_t head_dim);
+
+/*
+ * Gate-side gradients of token-gated attention (spke.com article, section on
+ * token-gated attention: the per-head gain and the temperature are learned,
+ * and the score bias is how the loss reaches the gate's scores in training).
+ * With the logit of tg_keybias_attn_prefill, P = softmax_j(l), dO = dL/dO and
+ *     dS_ij = P_ij (<dO_i, v_j> - <dO_i, O_i>)      (= dL/dl_ij),
+ * this writes
+ *     d_score[j] = sum_h head_gain[h] sum_i dS_hij
+ *     d_gain[h]  = sum_ij key_score[j] dS_hij
+ *     d_tau[0]   = -(1/tau) sum_hij dS_hij <R(q_i), R(k_j)> / (sqrt(D) tau)
+ * (sums over each sequence's causal pairs).  P is recomputed from the
+ * forward's lse; the q.k logits run on bf16 MFMA as in the forward, and
+ * every sum is fp32.  Deterministic: no atomics.
+ *   q, q_row_stride       the forward's queries
+ *   v, kv_row_stride      the values tg_attn_prepare was given (kv head hk of
+ *                         token m at v + m*kv_row_stride + hk*D)
+ *   key_score, head_gain, tau, cu_kept, n_seqs, n_kept_total, max_kept_seqlen,
+ *   n_q_heads, n_kv_heads, head_dim, rope_base: those of the forward
+ *   out           [device] bf16 n_kept_total x n_q_heads x D: the forward's O
+ *   lse           [device] fp32 n_q_heads x n_kept_total: the forward's lse
+ *   d_out         [device] bf16 dL/dO, token m head h at d_out + m*d_out_row_stride + h*D
+ *   cache         [device] the workspace tg_attn_prepare filled for this
+ *                 forward (read only), cache_bytes >= tg_attn_workspace_bytes(...)
+ *   d_score       [device, out] fp32 n_kept_total
+ *   d_gain        [device, out] fp32 n_q_heads
+ *   d_tau         [device, out] fp32 1
+ *   workspace     [device] >= tg_attn_gate_grads_workspace_bytes(...) bytes,
+ *                 256-B aligned, overwritten
+ * Requirements as for the prefill, and d_out_row_stride >= Hq*D, a multiple of
+ * 8; out, d_out and v 16-B aligned.  With no kept token d_gain and d_tau are
+ * set to zero.  Errors as for the prefill; nothing is launched unless every
+ * check passes.
+ */
+int tg_attn_gate_grads(const void* q, int64_t q_row_stride, const void* v, int64_t kv_row_stride,
+                       const float* key_score, const float* head_gain, float tau, const int32_t* cu_kept,
+                       int32_t n_seqs, int64_t n_kept_total, int32_t max_kept_seqlen, int32_t n_q_heads,
+                       int32_t n_kv_heads, int32_t head_dim, double rope_base, const void* out,
+                       const float* lse, const void* d_out, int64_t d_out_row_stride, const void* cache,
+                       size_t cache_bytes, float* d_score, float* d_gain, float* d_tau, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

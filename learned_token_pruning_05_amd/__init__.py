@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     tg_attn_decode,
     tg_attn_decode_workspace_bytes,
     tg_attn_forward,
+    tg_attn_gate_grads,
+    tg_attn_gate_grads_workspace_bytes,
     tg_attn_prepare,
     tg_attn_workspace_bytes,
     tg_gate_score,

@@ -42,6 +42,9 @@ SIGNATURES = {
     "tg_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "tg_attn_decode": (ctypes.c_int, [_P, _I64, _P, _P, _F, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _D, _P,
                                       _SZ, _P, _P, _P, _SZ, _P]),
+    "tg_attn_gate_grads_workspace_bytes": (_SZ, [_I32, _I64, _I32, _I32, _I32]),
+    "tg_attn_gate_grads": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _F, _P, _I32, _I64, _I32, _I32, _I32, _I32,
+                                          _D, _P, _P, _P, _I64, _P, _SZ, _P, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -285,3 +288,44 @@ def tg_attn_decode(q, q_pos, head_gain, tau: float, pos, cu_kept, max_kept_seqle
     _check("tg_attn_decode", st)
     return out, lse
 
+
+
+def tg_attn_gate_grads_workspace_bytes(n_seqs, n_kept_total, max_kept_seqlen, n_q_heads, head_dim) -> int:
+    return int(load().tg_attn_gate_grads_workspace_bytes(n_seqs, n_kept_total, max_kept_seqlen, n_q_heads,
+                                                         head_dim))
+
+
+def tg_attn_gate_grads(q, v, key_score, head_gain, tau: float, cu_kept, max_kept_seqlen: int, out, lse, d_out,
+                       cache, rope_base: float = 1e6, d_score=None, d_gain=None, d_tau=None, workspace=None):
+    """dL/dscore, dL/dgain, dL/dtau of a forward run over `cache` (tg_attn_prepare).
+
+    q: [M, Hq, D], v: [M, Hkv, D], out: [M, Hq, D] (the forward's, dense),
+    lse: [Hq, M] (the forward's), d_out: [M, Hq, D] bf16.
+    Returns (d_score [M], d_gain [Hq], d_tau [1]) fp32.
+    """
+    _check_q(q)
+    _check_q(d_out)
+    if v.stride(2) != 1 or v.stride(1) != v.shape[2]:
+        raise ValueError("heads must be contiguous within a token row")
+    if not out.is_contiguous():
+        raise ValueError("out must be dense [M, Hq, D]")
+    m, hq, d = q.shape
+    hkv = v.shape[1]
+    n_seqs = cu_kept.shape[0] - 1
+    dev = q.device
+    if d_score is None:
+        d_score = torch.empty(m, dtype=torch.float32, device=dev)
+    if d_gain is None:
+        d_gain = torch.empty(hq, dtype=torch.float32, device=dev)
+    if d_tau is None:
+        d_tau = torch.empty(1, dtype=torch.float32, device=dev)
+    need = tg_attn_gate_grads_workspace_bytes(n_seqs, m, int(max_kept_seqlen), hq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = load().tg_attn_gate_grads(_ptr(q), q.stride(0), _ptr(v), v.stride(0), _ptr(key_score), _ptr(head_gain),
+                                   float(tau), _ptr(cu_kept), n_seqs, m, int(max_kept_seqlen), hq, hkv, d,
+                                   float(rope_base), _ptr(out), _ptr(lse), _ptr(d_out), d_out.stride(0),
+                                   _ptr(cache), cache.numel(), _ptr(d_score), _ptr(d_gain), _ptr(d_tau),
+                                   _ptr(workspace), workspace.numel(), _stream(q))
+    _check("tg_attn_gate_grads", st)
+    return d_score, d_gain, d_tau

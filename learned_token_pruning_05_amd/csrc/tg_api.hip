@@ -315,3 +315,85 @@ int tg_attn_decode(const void* q, int64_t q_row_stride, const int32_t* q_pos, co
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t tg_attn_gate_grads_workspace_bytes(int32_t n_seqs, int64_t n_kept_total, int32_t max_kept_seqlen,
+                                          int32_t n_q_heads, int32_t head_dim) {
+    if (n_seqs < 0 || n_kept_total < 0 || max_kept_seqlen < 0 || n_q_heads <= 0 ||
+        (head_dim != 64 && head_dim != 128))
+        return 0;
+    return bwd_workspace_bytes(n_seqs, n_kept_total, max_kept_seqlen, n_q_heads, head_dim);
+}
+
+int tg_attn_gate_grads(const void* q, int64_t q_row_stride, const void* v, int64_t kv_row_stride,
+                       const float* key_score, const float* head_gain, float tau, const int32_t* cu_kept,
+                       int32_t n_seqs, int64_t n_kept_total, int32_t max_kept_seqlen, int32_t n_q_heads,
+                       int32_t n_kv_heads, int32_t head_dim, double rope_base, const void* out,
+                       const float* lse, const void* d_out, int64_t d_out_row_stride, const void* cache,
+                       size_t cache_bytes, float* d_score, float* d_gain, float* d_tau, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (!isfinite(rope_base)) return TG_ERR_INVALID_ARG;
+    if (n_seqs < 0 || n_kept_total < 0 || n_kept_total > INT32_MAX) return TG_ERR_INVALID_ARG;
+    if (n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads != 0) return TG_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return TG_ERR_UNSUPPORTED;
+    const int grp = n_q_heads / n_kv_heads;
+    if (grp != 1 && grp != 2 && grp != 4 && grp != 8) return TG_ERR_UNSUPPORTED;
+    if (!(tau > 0.0f) || !isfinite(tau)) return TG_ERR_INVALID_ARG;
+    if (q_row_stride < (int64_t)n_q_heads * head_dim || q_row_stride % 8 != 0) return TG_ERR_INVALID_ARG;
+    if (kv_row_stride < (int64_t)n_kv_heads * head_dim || kv_row_stride % 8 != 0) return TG_ERR_INVALID_ARG;
+    if (d_out_row_stride < (int64_t)n_q_heads * head_dim || d_out_row_stride % 8 != 0) return TG_ERR_INVALID_ARG;
+    if (max_kept_seqlen < 0 || max_kept_seqlen > n_kept_total || (n_kept_total > 0 && max_kept_seqlen < 1))
+        return TG_ERR_INVALID_ARG;
+    if (!d_gain || !d_tau) return TG_ERR_INVALID_ARG;
+    if (n_seqs == 0 || n_kept_total == 0) {
+        // no causal pair: every gradient is zero
+        return launch_gate_grads_zero(n_q_heads, d_gain, d_tau, (hipStream_t)stream);
+    }
+    if (!q || !v || !key_score || !head_gain || !cu_kept || !out || !lse || !d_out || !d_score)
+        return TG_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(v) || !aligned16(out) || !aligned16(d_out)) return TG_ERR_INVALID_ARG;
+    const size_t cache_need = attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, nullptr,
+                                                    nullptr, nullptr);
+    if (!cache || cache_bytes < cache_need || ((uintptr_t)cache & 255u) != 0) return TG_ERR_WORKSPACE;
+    const size_t need = bwd_workspace_bytes(n_seqs, n_kept_total, max_kept_seqlen, n_q_heads, head_dim);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return TG_ERR_WORKSPACE;
+    const int64_t mp = attn_padded_rows(n_seqs, n_kept_total);
+    // buffer offsets into one head's prepared rows and into d_out stay 32-bit
+    if ((int64_t)(head_dim + 16) * 2 * mp >= ((int64_t)1 << 32) ||
+        d_out_row_stride * 2 * (n_kept_total + 64) >= ((int64_t)1 << 32))
+        return TG_ERR_UNSUPPORTED;
+    size_t off_k, off_vt, off_cs;
+    attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, &off_k, &off_vt, &off_cs);
+    BwdArgs a{};
+    a.q = (const bf16*)q;
+    a.q_stride = q_row_stride;
+    a.v = (const bf16*)v;
+    a.kv_stride = kv_row_stride;
+    a.o = (const bf16*)out;
+    a.lse = lse;
+    a.dout = (const bf16*)d_out;
+    a.do_stride = d_out_row_stride;
+    a.key_score = key_score;
+    a.gain = head_gain;
+    a.tau = tau;
+    a.qk_scale_log2 = (float)(1.4426950408889634 / (sqrt((double)head_dim) * (double)tau));
+    a.cu_kept = cu_kept;
+    a.n_seqs = n_seqs;
+    a.m_tot = n_kept_total;
+    a.max_kept_seqlen = max_kept_seqlen;
+    a.hq = n_q_heads;
+    a.hkv = n_kv_heads;
+    a.d = head_dim;
+    a.rope = rope_base > 0.0;
+    a.ws_k = (const bf16*)((const char*)cache + off_k);
+    a.ws_cs = (const float2*)((const char*)cache + off_cs);
+    a.mp = mp;
+    a.d_score = d_score;
+    a.d_gain = d_gain;
+    a.d_tau = d_tau;
+    a.ws = workspace;
+    return launch_attn_gate_grads(a, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -89,6 +89,37 @@ struct DecodeArgs {
     float* lse;             // [Hq][n_seqs] or null
     void* ws;               // decode partials
 };
+struct BwdArgs {
+    const bf16* q;          // [M] rows of [Hq][D], q_stride elements apart
+    int64_t q_stride;
+    const bf16* v;          // [M] rows of [Hkv][D], kv_stride elements apart
+    int64_t kv_stride;
+    const bf16* o;          // forward output [M][Hq][D]
+    const float* lse;       // forward LSE [Hq][M] (natural log)
+    const bf16* dout;       // [M] rows of [Hq][D], do_stride elements apart
+    int64_t do_stride;
+    const float* key_score; // [M]
+    const float* gain;      // [Hq]
+    float tau;
+    float qk_scale_log2;    // log2(e) / (sqrt(D) * tau)
+    const int* cu_kept;
+    int n_seqs;
+    int64_t m_tot;
+    int max_kept_seqlen;
+    int hq, hkv, d;
+    bool rope;
+    const bf16* ws_k;       // the prepared cache (see AttnArgs)
+    const float2* ws_cs;
+    int64_t mp;
+    float* d_score;         // [M]
+    float* d_gain;          // [Hq]
+    float* d_tau;           // [1]
+    void* ws;
+};
+size_t bwd_workspace_bytes(int n_seqs, int64_t m_tot, int max_kept, int hq, int d);
+int launch_attn_gate_grads(const BwdArgs& a, hipStream_t st);
+int launch_gate_grads_zero(int hq, float* d_gain, float* d_tau, hipStream_t st);
+
 int decode_chunks(int max_kept_seqlen);
 size_t decode_part_o_bytes(int n_seqs, int max_kept_seqlen, int hq, int d);
 size_t decode_workspace_bytes(int n_seqs, int max_kept_seqlen, int hq, int d);

@@ -314,7 +314,8 @@ def keybias_attention(q, k, v, s_kept, gain, tau, pos, cu_kept,
     return out, lse
 
 
-def keybias_attention_gate_grads(q, k, v, s_kept, gain, tau, pos, cu_kept, d_out, rope_base: float = 1e6):
+def keybias_attention_gate_grads(q, k, v, s_kept, gain, tau, pos, cu_kept, d_out, rope_base: float = 1e6,
+                                 scales: bool = False):
     """Gradients of a loss L through token-gated attention with respect to the
     gate-side parameters: the kept keys' scores s_j, the per-head gains g_h and
     the temperature tau, given dL/dO ([ES] "¿Qué es la atención…?": the gain and
@@ -329,6 +330,12 @@ def keybias_attention_gate_grads(q, k, v, s_kept, gain, tau, pos, cu_kept, d_out
         dL/dg_h  = sum_ij s_j dS_hij
         dL/dtau  = sum_hij dS_hij * (-<q~_i, k~_j> / (sqrt(D) tau^2)).
     d_out: [M, Hq, D].  Returns (ds [M], dg [Hq], dtau) in float64.
+
+    scales=True also returns the same three sums taken over absolute values
+    with |dS_ij| replaced by P_ij (|dP_ij| + |Delta_i|): a first-order bound
+    on how far each result moves when every logit moves by a relative amount
+    and every Delta_i by a relative amount (the condition scale a rounded
+    implementation's error is measured against).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -349,6 +356,9 @@ def keybias_attention_gate_grads(q, k, v, s_kept, gain, tau, pos, cu_kept, d_out
     ds = np.zeros(m_tot)
     dg = np.zeros(hq)
     dtau = 0.0
+    ds_mag = np.zeros(m_tot)
+    dg_mag = np.zeros(hq)
+    dtau_mag = 0.0
     for si in range(len(ck) - 1):
         a, b = int(ck[si]), int(ck[si + 1])
         if a == b:
@@ -372,6 +382,14 @@ def keybias_attention_gate_grads(q, k, v, s_kept, gain, tau, pos, cu_kept, d_out
             ds[a:b] += gain[h] * col
             dg[h] += float(s_kept[a:b] @ col)
             dtau += float((dsm * (-qk / float(tau))).sum())
+            if scales:
+                env = pr * (np.abs(dp) + np.abs(delta))
+                ecol = env.sum(axis=0)
+                ds_mag[a:b] += abs(gain[h]) * ecol
+                dg_mag[h] += float(np.abs(s_kept[a:b]) @ ecol)
+                dtau_mag += float((env * np.abs(qk / float(tau))).sum())
+    if scales:
+        return ds, dg, dtau, (ds_mag, dg_mag, dtau_mag)
     return ds, dg, dtau
 
 

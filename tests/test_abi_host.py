@@ -212,6 +212,40 @@ def test_attn_decode_validation(lib):
     assert a(ns=0) == 0                # nothing to do, nothing launched
 
 
+def test_attn_gate_grads_validation(lib):
+    L = lib
+    cache = L.tg_attn_workspace_bytes(1, 100, 8, 128)
+    need = L.tg_attn_gate_grads_workspace_bytes(1, 100, 100, 16, 128)
+    assert need >= 16 * 100 * (128 + 16) * 2 + 3 * 16 * 100 * 4
+    assert L.tg_attn_gate_grads_workspace_bytes(1, 100, 100, 16, 96) == 0
+    a = lambda **kw: L.tg_attn_gate_grads(*[kw.get(k, v) for k, v in [
+        ("q", FAKE), ("qs", 2048), ("v", FAKE), ("kvs", 1024), ("s", FAKE), ("g", FAKE), ("tau", 0.9),
+        ("ck", FAKE), ("ns", 1), ("m", 100), ("mx", 100), ("hq", 16), ("hkv", 8), ("d", 128), ("rb", 1e6),
+        ("out", FAKE), ("lse", FAKE), ("do", FAKE), ("dos", 2048), ("cache", FAKE), ("cb", cache),
+        ("dsc", FAKE), ("dg", FAKE), ("dt", FAKE), ("ws", FAKE), ("wsb", need), ("st", None)]])
+    assert a(tau=0.0) == 1
+    assert a(tau=float("inf")) == 1
+    assert a(rb=float("nan")) == 1
+    assert a(hq=12) == 1               # not a multiple of Hkv
+    assert a(d=96) == 2                # unsupported head_dim
+    assert a(hq=24, qs=3072, dos=3072) == 2   # group size 3
+    assert a(qs=2000) == 1             # stride below Hq * D
+    assert a(kvs=1000) == 1
+    assert a(dos=2040) == 1
+    assert a(dos=2052) == 1            # not a multiple of 8
+    assert a(mx=101) == 1              # longer than the total
+    assert a(mx=0) == 1                # kept keys but no length
+    for name in ("q", "v", "s", "g", "ck", "out", "lse", "do", "dsc", "dg", "dt"):
+        assert a(**{name: None}) == 1, name
+    assert a(q=ctypes.c_void_p(0x1008)) == 1   # not 16-B aligned
+    assert a(do=ctypes.c_void_p(0x1008)) == 1
+    assert a(cb=cache - 1) == 3        # cache smaller than the prepared layout
+    assert a(cache=ctypes.c_void_p(0x1010)) == 3
+    assert a(wsb=need - 1) == 3
+    assert a(ws=ctypes.c_void_p(0x1010)) == 3
+    assert a(m=0, mx=0, dg=None) == 1  # the zero gradients still need somewhere to go
+
+
 def test_random_k_validation(lib):
     L = lib
     need = L.tg_random_k_workspace_bytes(2, 1000, 600)

@@ -486,6 +486,122 @@ def test_decode_position_mask_and_empty():
     _check_decode(c, q_own, pk[rows].astype(np.int32), 1e6, out2, lse2)
 
 
+# ------------------------------------------------------ gate-side gradients ----
+# Bars, against the oracle's condition scales (the same sums over
+# P_ij (|dP_ij| + |Delta_i|) in place of dS_ij): every term of the GPU's sums
+# carries the bf16 rounding of its logit (rotated, scaled q and k, 2^-9
+# relative each) and of the forward's O in Delta, so each term is off by a
+# few 2^-9 of its scale term; d_score sums one column, 1e-2 of its scale; the
+# head and temperature gradients sum ~1e4-1e8 such terms whose roundings do not
+# line up, 1e-3 of theirs (fp32 accumulation: at most ~4e3 * 2^-24 relative
+# over a lane's sum).
+GRAD_TOL_S = 1e-2
+GRAD_TOL_G = 1e-3
+
+
+def _run_grads(c, d_out, rope_base, q=None, v=None, d_out_dev=None):
+    ck = c["ck"]
+    maxlen = int(np.diff(ck).max()) if len(ck) > 1 else 0
+    q = _dev(c["q"]) if q is None else q
+    k = _dev(c["k"])
+    v = _dev(c["v"]) if v is None else v
+    sk, gain, cku = _dev(c["sk"]), _dev(c["gain"]), _i32(ck)
+    hkv = k.shape[1]
+    cache = tg.tg_attn_prepare(k, v.contiguous(), sk, _i32(c["pk"]), cku, rope_base=rope_base)
+    out, lse = tg.tg_attn_forward(q, gain, c["tau"], cku, maxlen, hkv, cache, rope_base=rope_base)
+    dsc, dg, dt = tg.tg_attn_gate_grads(q, v, sk, gain, c["tau"], cku, maxlen, out, lse,
+                                        _dev(d_out) if d_out_dev is None else d_out_dev, cache, rope_base=rope_base)
+    torch.cuda.synchronize()
+    return dsc.cpu().numpy(), dg.cpu().numpy(), float(dt.cpu()[0])
+
+
+def _check_grads(c, d_out, rope_base, got):
+    f = lambda t: t.float().numpy()
+    ds, dg, dtau, (ms, mg, mt) = oracle.keybias_attention_gate_grads(
+        f(c["q"]), f(c["k"]), f(c["v"]), c["sk"], c["gain"], c["tau"], c["pk"], c["ck"], f(d_out),
+        rope_base=rope_base, scales=True)
+    g_s, g_g, g_t = got
+    assert np.isfinite(g_s).all() and np.isfinite(g_g).all() and math.isfinite(g_t)
+    es = np.abs(g_s - ds) / np.maximum(ms, 1e-30)
+    eg = np.abs(g_g - dg) / np.maximum(mg, 1e-30)
+    et = abs(g_t - dtau) / max(mt, 1e-30)
+    print(f"   err/scale: d_score {es.max() if es.size else 0:.3g}  d_gain {eg.max():.3g}  d_tau {et:.3g}"
+          f"   (|d_tau| = {abs(dtau):.4g})", flush=True)
+    assert np.all(np.abs(g_s - ds) <= GRAD_TOL_S * ms + 1e-6)
+    assert np.all(np.abs(g_g - dg) <= GRAD_TOL_G * mg + 1e-6)
+    assert abs(g_t - dtau) <= GRAD_TOL_G * mt + 1e-6
+
+
+@pytest.mark.parametrize("name", ["tiny", "16k", "128k"])
+def test_gate_grads_configs(name):
+    """Every d_score, d_gain and d_tau of the workload against the oracle (128k:
+    8448 kept tokens, 16 q heads, the bench's launch)."""
+    _print_case(f"gate grads {name}")
+    w = workloads.by_name(name)
+    c = _attn_case(w)
+    d_out = w.d_out(int(c["ck"][-1]))
+    got = _run_grads(c, d_out, w.rope_base)
+    _check_grads(c, d_out, w.rope_base, got)
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(64, 4, 4), (64, 8, 2), (128, 16, 8), (128, 8, 1), (128, 16, 2)])
+@pytest.mark.parametrize("rope", [0.0, 1e6])
+def test_gate_grads_shapes_ragged(d, hq, hkv, rope):
+    """Ragged kept lengths: an empty sequence, one key, and the 32/64/128-key
+    block and tile edges of the kernel."""
+    lens = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 300]
+    w = workloads.custom([n + 8 for n in lens], [8 if n else 0 for n in lens], [max(n - 8, 0) for n in lens],
+                         n_q_heads=hq, n_kv_heads=hkv, head_dim=d, seed=d + hq + hkv + 11, tau=0.83)
+    _print_case(f"gate grads shape d={d} hq={hq} hkv={hkv} rope={rope}")
+    c = _attn_case(w)
+    d_out = w.d_out(int(c["ck"][-1]))
+    got = _run_grads(c, d_out, rope)
+    _check_grads(c, d_out, rope, got)
+
+
+def test_gate_grads_strided_rows():
+    """q, v and dL/dO as column slices of wider token rows (a fused projection)."""
+    w = workloads.custom([500, 333], [20, 13], [200, 150], n_q_heads=8, n_kv_heads=2, head_dim=128, seed=51)
+    _print_case("gate grads strided")
+    c = _attn_case(w)
+    m = int(c["ck"][-1])
+    d_out = w.d_out(m)
+    wide_q = torch.zeros(m, 8 * 128 + 64, dtype=torch.bfloat16)
+    wide_q[:, 32:32 + 8 * 128] = c["q"].reshape(m, -1)
+    wide_v = torch.zeros(m, 3 * 2 * 128, dtype=torch.bfloat16)
+    wide_v[:, 2 * 128:4 * 128] = c["v"].reshape(m, -1)
+    wide_do = torch.zeros(m, 8 * 128 + 8, dtype=torch.bfloat16)
+    wide_do[:, 8:] = d_out.reshape(m, -1)
+    q = _dev(wide_q)[:, 32:32 + 8 * 128].unflatten(1, (8, 128))
+    v = _dev(wide_v)[:, 2 * 128:4 * 128].unflatten(1, (2, 128))
+    do = _dev(wide_do)[:, 8:].unflatten(1, (8, 128))
+    got = _run_grads(c, d_out, 1e6, q=q, v=v, d_out_dev=do)
+    _check_grads(c, d_out, 1e6, got)
+
+
+def test_gate_grads_no_tokens_and_determinism():
+    """No kept token: d_gain and d_tau are written as zeros.  Two runs of the same
+    input give the same bits (no atomics)."""
+    _print_case("gate grads empty / repeat")
+    empty = torch.empty(0, 4, 64, dtype=torch.bfloat16, device="cuda")
+    ev = torch.empty(0, 2, 64, dtype=torch.bfloat16, device="cuda")
+    ck = _i32([0, 0])
+    dg = torch.full((4,), float("nan"), device="cuda")
+    dt = torch.full((1,), float("nan"), device="cuda")
+    tg.tg_attn_gate_grads(empty, ev, torch.empty(0, device="cuda"), torch.ones(4, device="cuda"), 0.9, ck, 0,
+                          empty, torch.empty(4, 0, device="cuda"), empty, torch.empty(256, dtype=torch.uint8,
+                                                                                       device="cuda"),
+                          d_gain=dg, d_tau=dt)
+    torch.cuda.synchronize()
+    assert not dg.any().item() and dt.item() == 0.0
+    w = workloads.by_name("tiny")
+    c = _attn_case(w)
+    d_out = w.d_out(int(c["ck"][-1]))
+    a = _run_grads(c, d_out, w.rope_base)
+    b = _run_grads(c, d_out, w.rope_base)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
 # --------------------------------------------------------------- end to end ----
 @pytest.mark.parametrize("name", ["tiny", "16k"])
 def test_gated_layer_end_to_end(name):

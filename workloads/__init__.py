@@ -20,7 +20,8 @@ import numpy as np
 import torch
 
 # component ids of the per-component random streams
-_C_OUTLIER, _C_X, _C_W1, _C_W2, _C_NEEDLE, _C_SCORES, _C_TIES, _C_GAIN, _C_TAU, _C_Q, _C_K, _C_V, _C_LENS = range(13)
+(_C_OUTLIER, _C_X, _C_W1, _C_W2, _C_NEEDLE, _C_SCORES, _C_TIES, _C_GAIN, _C_TAU, _C_Q, _C_K, _C_V, _C_LENS,
+ _C_DOUT) = range(14)
 
 
 def _rng(seed: int, comp: int) -> np.random.Generator:
@@ -177,6 +178,13 @@ class Workload:
         k = to_bf16(_rng(self.seed, _C_K).standard_normal((m, hkv, dd), dtype=np.float32))
         v = to_bf16(_rng(self.seed, _C_V).standard_normal((m, hkv, dd), dtype=np.float32))
         return q, k, v
+
+    def d_out(self, m_tot: int | None = None, seed_offset: int = 0):
+        """dL/dO [M, Hq, D] in bfloat16 (CPU tensor): a stand-in for the gradient
+        that training hands back to the attention output."""
+        m = int(self.cu_kept()[-1]) if m_tot is None else m_tot
+        r = _rng(self.seed + seed_offset, _C_DOUT)
+        return to_bf16(r.standard_normal((m, self.n_q_heads, self.head_dim), dtype=np.float32))
 
 
 def _qwen_layer(**kw):
