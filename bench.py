@@ -176,6 +176,39 @@ def measure_decode(layer: Layer, steps=50, warmup=5):
             "kernels": "attn_decode_split_kernel + attn_decode_combine_kernel (tg_attn_decode)"}
 
 
+def measure_gate_grads(layer: Layer, steps=10, warmup=3):
+    """Gate-side gradients (tg_attn_gate_grads: dL/ds_j, dL/dg_h, dL/dtau) of the
+    layer's attention for a synthetic dL/dO, over the cache and the forward
+    output and LSE the layer left.  Algorithmic work: the two products of every
+    causal pair and q head, q.k and dO.v, 4 D flops per pair (the same count
+    as the forward)."""
+    w = layer.w
+    dev = layer.q.device
+    d_out = w.d_out(layer.m).to(dev)
+    dsc = torch.empty(layer.m, dtype=torch.float32, device=dev)
+    dg = torch.empty(w.n_q_heads, dtype=torch.float32, device=dev)
+    dt = torch.empty(1, dtype=torch.float32, device=dev)
+    wsg = torch.empty(tg.tg_attn_gate_grads_workspace_bytes(w.n_seqs, layer.m, layer.max_kept, w.n_q_heads,
+                                                            w.head_dim), dtype=torch.uint8, device=dev)
+    f = lambda: tg.tg_attn_gate_grads(layer.q, layer.v, layer.sk, layer.gain, layer.tau, layer.ck, layer.max_kept,
+                                      layer.out, layer.lse, d_out, layer.ws, rope_base=w.rope_base, d_score=dsc,
+                                      d_gain=dg, d_tau=dt, workspace=wsg)
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    fl = layer.attn_work()
+    return {"us_per_step": round(us, 1), "flops": fl, "tflops": round(fl / us / 1e6, 1),
+            "frac_bf16_peak": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4),
+            "kernels": "bwd_prep_kernel + bwd_main_kernel + bwd_reduce_kernel (tg_attn_gate_grads)"}
+
+
 def measure_full_prefill(w: workloads.Workload, pruned_layer_ms: float, reps=3):
     """The same attention at K = n_doc (every token kept, no gate/select/gather):
     tg_attn_prepare + tg_attn_forward over all N tokens, beside the pruned layer,
@@ -332,6 +365,7 @@ def main():
     attn_s = r["stage_ms"][Layer.STAGES.index("attn_fwd")] * 1e-3
     achieved = af / attn_s / 1e12
     decode = measure_decode(layer)
+    grads = measure_gate_grads(layer)
     del layer
     torch.cuda.empty_cache()
     full = measure_full_prefill(w, r["wall_ms"])
@@ -373,6 +407,7 @@ def main():
                      "traffic": pmc_traffic()},
         "gated_layer_128k": head,
         "decode_128k": decode,
+        "gate_grads_128k": grads,
         "full_prefill_128k": full,
         "sweep_32k": sweep,
         "cpu_baseline": cpu,

@@ -281,9 +281,9 @@ int tg_attn_decode(const void* q, int64_t q_row_stride, const int32_t* q_pos, co
                    int32_t head_dim, double rope_base, const void* cache, size_t cache_bytes, void* out,
                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes tg_attn_gate_grads needs: the prepared queries (Hq rows of
- * D+16 bf16 per padded kept row) plus four fp32 values per q head and kept
- * token and a few per-block partials. */
+/* Workspace bytes tg_attn_gate_grads needs: the prepared queries and dL/dO
+ * rows (2 Hq rows of D+16 bf16 per padded kept row) plus one fp32 per q head
+ * and kept token and a few per-block partials. */
 size_t tg_attn_gate_grads_workspace_bytes(int32_t n_seqs, int64_t n_kept_total, int32_t max_kept_seqlen,
                                           int32_t n_q_heads, int32_t head_dim);
 

@@ -359,10 +359,8 @@ int tg_attn_gate_grads(const void* q, int64_t q_row_stride, const void* v, int64
     const size_t need = bwd_workspace_bytes(n_seqs, n_kept_total, max_kept_seqlen, n_q_heads, head_dim);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return TG_ERR_WORKSPACE;
     const int64_t mp = attn_padded_rows(n_seqs, n_kept_total);
-    // buffer offsets into one head's prepared rows and into d_out stay 32-bit
-    if ((int64_t)(head_dim + 16) * 2 * mp >= ((int64_t)1 << 32) ||
-        d_out_row_stride * 2 * (n_kept_total + 64) >= ((int64_t)1 << 32))
-        return TG_ERR_UNSUPPORTED;
+    // buffer offsets into one head's prepared rows stay 32-bit
+    if ((int64_t)(head_dim + 16) * 2 * mp >= ((int64_t)1 << 32)) return TG_ERR_UNSUPPORTED;
     size_t off_k, off_vt, off_cs;
     attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, &off_k, &off_vt, &off_cs);
     BwdArgs a{};

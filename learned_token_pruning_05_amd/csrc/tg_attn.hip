@@ -13,7 +13,8 @@
 //       (cos, sin), kept as a per-token table for the queries;
 //     - keys rotated in fp32 and rounded to bf16 into K' rows [Hkv][row][D+16]
 //       whose 16 extra columns carry the key score split in two bf16 halves
-//       (s_hi, s_lo, s_hi, 0...), so the bias rides inside the QK MFMA;
+//       and two ones (s_hi, s_lo, s_hi, 1, 1, 0...), so the bias (and a
+//       per-query constant) rides inside the QK MFMA;
 //     - values transposed through LDS to V^T [Hkv][D][row] (coalesced stores),
 //       the layout the P.V MFMA operand wants, with the middle two quads of
 //       every 16-key group swapped (vt_col) to match the P^T operand's order.
@@ -187,7 +188,9 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
         *(bf16x8*)(dst + p * 8) = x1;
         *(bf16x8*)(dst + HALF + p * 8) = x2;
         if (p == 0) {
-            // bias columns: (s_hi, s_lo, s_hi, 1) against Q' (g_hi, g_hi, g_lo, -m)
+            // bias columns: (s_hi, s_lo, s_hi, 1, 1) against Q' (g_hi, g_hi, g_lo,
+            // -m, 0); a query-side constant split in two bf16 halves can ride
+            // in columns 3 and 4
             bf16x8 extra = bf16x8{};
             if (m >= 0) {
                 bf16 sh, sl;
@@ -196,6 +199,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
                 extra[1] = sl;
                 extra[2] = sh;
                 extra[3] = (bf16)1.0f;
+                extra[4] = (bf16)1.0f;
             }
             *(bf16x8*)(dst + D) = extra;
             *(bf16x8*)(dst + D + 8) = bf16x8{};

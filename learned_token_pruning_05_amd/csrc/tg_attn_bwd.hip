@@ -11,70 +11,76 @@
 // where S = l log2(e) is what the MFMA produces, so ln 2 * S - g_h s_j is the
 // q.k part of the logit.  (Delta_i = sum_j P_ij dP_ij because O_i = sum_j P_ij v_j.)
 //
+// S' = S - LSE2_i and dP' = dP - Delta_i both come out of the MFMAs: the
+// prepared queries carry (g_hi, g_hi, g_lo, -LSE2_hi, -LSE2_lo) against the
+// key cache's (s_hi, s_lo, s_hi, 1, 1), and the prepared dO rows carry
+// (-Delta_hi, -Delta_lo) against a (1, 1) key fragment, so per element the
+// VALU does P = exp2(S'), dS = P dP', two sums.  The temperature sum uses
+// S' instead of S: every row of dS sums to zero (softmax rows sum to one),
+// so subtracting a per-row constant leaves sum dS S unchanged.
+//
 // Kernels:
-//   prep    rotated, scaled queries Q' in the layout of the prepared key cache
-//           (bias columns (g_hi, g_hi, g_lo, 0) against K' (s_hi, s_lo, s_hi, 1)),
-//           plus the log2-domain LSE and Delta of every (q head, kept token);
-//   main    key-outer: a workgroup owns 128 keys (32 per wave) of one q head,
+//   prep    Q' and dO' rows [Hq][padded row][D+16] in the key cache's padded
+//           per-sequence layout (rows without a token are zero): queries
+//           rotated on their positions and scaled by log2(e)/(sqrt(D) tau);
+//   main    key-outer: a workgroup owns 256 keys (32 per wave) of one q head,
 //           keeps their K' and V operand fragments in registers and streams
-//           every query tile at or after its keys (Q' and dO, 64 rows) through
-//           a two-slot LDS ring.  S = Q'.K'^T and dP = dO.V^T run on 32x32x16
-//           bf16 MFMA; the accumulator layout puts one key per lane, so C_hj is
-//           an in-lane sum over the query rows (no atomics, deterministic), and
-//           the workgroup leaves C_hj plus its partial sums of s_j C_hj and of
-//           dS S;
-//   reduce  dL/ds over heads; per head dL/dg and its share of dL/dtau; tau.
+//           every query tile at or after its keys (Q' and dO', 64 rows) through
+//           a four-slot LDS ring, loaded three tiles ahead.  S' = Q'.K'^T and dP' = dO'.V'^T run on
+//           32x32x16 bf16 MFMA; the accumulator layout puts one key per lane,
+//           so C_hj is an in-lane sum over the query rows (no atomics,
+//           deterministic), and the workgroup leaves C_hj plus its partial
+//           sums of s_j C_hj and of dS S';
+//   reduce  one launch: dL/ds over heads, and per head dL/dg and dL/dtau.
 #include <math.h>
+
+#include <type_traits>
 
 #include "tg_common.hpp"
 
 namespace tg {
 namespace {
 
-constexpr int kBwdThreads = 256;
-constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 512;
+constexpr int kBwdWaves = 8;
 constexpr int kBwdKeys = 32 * kBwdWaves;   // keys per main workgroup
+constexpr int kBwdSlots = 4;               // LDS ring slots (tiles loaded 3 ahead)
 constexpr int kBwdQ = 64;                  // query rows per tile
 constexpr int kBwdExtra = 16;              // bias columns, as in K'
 
 template <int D>
 struct BwdLds {
-    // tiles arrive by 16-B LDS-direct loads (64 lanes x 16 B per instruction);
-    // rows are padded by one chunk so that the 16-B operand reads of eight
-    // consecutive rows fall on distinct bank groups (pad slots hold a
-    // duplicate, never read)
+    // Q' and dO' tiles arrive by 16-B LDS-direct loads (64 lanes x 16 B per
+    // instruction); rows are padded by one chunk so that the 16-B operand
+    // reads of eight consecutive rows fall on distinct bank groups (pad slots
+    // hold a duplicate, never read)
     static constexpr int KD = D + kBwdExtra;
-    static constexpr int QCH = KD / 8;            // 16-B chunks per Q' row
-    static constexpr int QROW = QCH + 1;
-    static constexpr int OCH = D / 8;             // 16-B chunks per dO row
-    static constexpr int OROW = OCH + 1;
-    static constexpr int Q_INSTR = kBwdQ * QROW / 64;
-    static constexpr int O_INSTR = kBwdQ * OROW / 64;
-    static_assert(kBwdQ * QROW % 64 == 0 && kBwdQ * OROW % 64 == 0, "tiles must be whole load instructions");
-    static constexpr int QT = kBwdQ * QROW * 8;   // elements per Q' tile
-    static constexpr int OT = kBwdQ * OROW * 8;   // elements per dO tile
-    static constexpr size_t SMEM = (size_t)2 * (QT + OT) * 2 + (size_t)2 * 2 * kBwdQ * 4;   // + LSE2, Delta rows
-    // load instructions one wave issues per tile: its share of the Q' and dO
-    // instructions, plus the LSE2 row (wave 3) or the Delta row (wave 2)
-    __device__ static int per_wave(int w) {
-        return (Q_INSTR - w + kBwdWaves - 1) / kBwdWaves + (O_INSTR - w + kBwdWaves - 1) / kBwdWaves + (w >= 2);
-    }
+    static constexpr int CH = KD / 8;             // 16-B chunks per row
+    static constexpr int ROW = CH + 1;
+    static constexpr int INSTR = kBwdQ * ROW / 64;   // load instructions per tile
+    static_assert(kBwdQ * ROW % 64 == 0, "tiles must be whole load instructions");
+    static constexpr int T = kBwdQ * ROW * 8;     // elements per tile
+    static constexpr size_t SMEM = (size_t)kBwdSlots * 2 * T * 2;   // Q' and dO' per slot
+    // load instructions one wave issues per tile (at most 6: two tiles ahead
+    // stay within the 12 outstanding loads wait_vm_le handles)
+    __device__ static int per_wave(int w) { return 2 * ((INSTR - w + kBwdWaves - 1) / kBwdWaves); }
+    static_assert(2 * 2 * ((INSTR + kBwdWaves - 1) / kBwdWaves) <= 12, "too many loads in flight per wave");
 };
 
 // ---------------------------------------------------------------- prep ----
-// One workgroup per (64 padded rows, q head).  Padded rows follow the key
-// cache's per-sequence layout; rows without a token are zero.  Items (row,
-// rotate-half chunk pair) as in the key pre-pass, lanes over chunk pairs; the
-// (cos, sin) table of the key pre-pass supplies the rotation.  Threads 0..63
-// also compute Delta and LSE2 for their row.
+// One workgroup per (64 padded rows, q head).  Four threads per row copy dO
+// into dO' while computing Delta = <dO, O>, and LSE2 = LSE log2(e); then the
+// Q' items (row, rotate-half chunk pair), lanes over chunk pairs, with the
+// (cos, sin) table of the key pre-pass, and the extra columns.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const bf16* __restrict__ q, int64_t q_stride, const bf16* __restrict__ o, const bf16* __restrict__ dout,
     int64_t do_stride, const float* __restrict__ lse, const float* __restrict__ gain, float qk_scale_log2,
     const float2* __restrict__ ws_cs, int rope, const int* __restrict__ cu_kept, int n_seqs, int64_t m_tot,
-    int hq, int64_t mp, bf16* __restrict__ qc, float* __restrict__ l2, float* __restrict__ delta) {
-    constexpr int HALF = D / 2, KD = D + kBwdExtra, NPAIR = D / 16;
+    int hq, int64_t mp, bf16* __restrict__ qc, bf16* __restrict__ oc) {
+    constexpr int HALF = D / 2, KD = D + kBwdExtra, NPAIR = D / 16, NC8 = D / 8;
     __shared__ int tok[64];
+    __shared__ float rowc[2][64];   // Delta, LSE2
     const int tid = threadIdx.x;
     const int h = blockIdx.y;
     const int64_t p0 = (int64_t)blockIdx.x * 64;
@@ -87,21 +93,38 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
         }
         const int64_t ps = padded_seq_start(cu_kept[lo], lo);
         const int len = cu_kept[lo + 1] - cu_kept[lo];
-        const int m = (r >= ps && r < ps + len) ? cu_kept[lo] + (int)(r - ps) : -1;
-        tok[tid] = m;
+        tok[tid] = (r >= ps && r < ps + len) ? cu_kept[lo] + (int)(r - ps) : -1;
+    }
+    __syncthreads();
+    {
+        // four threads per row; instruction i of the row's threads covers
+        // chunks 4i..4i+3 (64 contiguous bytes): dO is copied into the data
+        // columns of dO' as it is read for Delta
+        const int r = tid >> 2, part = tid & 3;
+        const int m = tok[r];
+        bf16* odst = oc + ((int64_t)h * mp + p0 + r) * KD;
+        float acc = 0.0f;
         if (m >= 0) {
             const bf16* dr = dout + (int64_t)m * do_stride + (int64_t)h * D;
             const bf16* orr = o + ((int64_t)m * hq + h) * D;
-            float acc = 0.0f;
-#pragma unroll 4
-            for (int c = 0; c < D / 8; ++c) {
-                const bf16x8 a = *(const bf16x8*)(dr + c * 8);
-                const bf16x8 b = *(const bf16x8*)(orr + c * 8);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
+            for (int i = 0; i < NC8 / 4; ++i) {
+                const int c = 4 * i + part;
+                const bf16x8 x = *(const bf16x8*)(dr + c * 8);
+                const bf16x8 y = *(const bf16x8*)(orr + c * 8);
+                *(bf16x8*)(odst + c * 8) = x;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
             }
-            delta[(int64_t)h * m_tot + m] = acc;
-            l2[(int64_t)h * m_tot + m] = lse[(int64_t)h * m_tot + m] * kLog2e;
+        } else {
+#pragma unroll
+            for (int i = 0; i < NC8 / 4; ++i) *(bf16x8*)(odst + (4 * i + part) * 8) = bf16x8{};
+        }
+        acc += __shfl_xor(acc, 1, 64);
+        acc += __shfl_xor(acc, 2, 64);
+        if (part == 0) {
+            rowc[0][r] = acc;
+            rowc[1][r] = m >= 0 ? lse[(int64_t)h * m_tot + m] * kLog2e : 0.0f;
         }
     }
     __syncthreads();
@@ -132,43 +155,53 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
                 }
             }
         }
-        bf16* dst = qc + ((int64_t)h * mp + p0 + r) * KD;
+        const int64_t row = (int64_t)h * mp + p0 + r;
+        bf16* dst = qc + row * KD;
         *(bf16x8*)(dst + p * 8) = x1;
         *(bf16x8*)(dst + HALF + p * 8) = x2;
         if (p == 0) {
-            bf16x8 extra = bf16x8{};
+            // Q' (g_hi, g_hi, g_lo, -LSE2_hi, -LSE2_lo), dO' (-Delta_hi, -Delta_lo)
+            bf16x8 qx = bf16x8{}, ox = bf16x8{};
             if (m >= 0) {
                 const float g = gain[h] * kLog2e;
                 const bf16 gh = (bf16)g;
-                extra[0] = gh;
-                extra[1] = gh;
-                extra[2] = (bf16)(g - (float)gh);
+                qx[0] = gh;
+                qx[1] = gh;
+                qx[2] = (bf16)(g - (float)gh);
+                const float l2 = -rowc[1][r];
+                const bf16 lh = (bf16)l2;
+                qx[3] = lh;
+                qx[4] = (bf16)(l2 - (float)lh);
+                const float dl = -rowc[0][r];
+                const bf16 dh = (bf16)dl;
+                ox[0] = dh;
+                ox[1] = (bf16)(dl - (float)dh);
             }
-            *(bf16x8*)(dst + D) = extra;
+            *(bf16x8*)(dst + D) = qx;
             *(bf16x8*)(dst + D + 8) = bf16x8{};
+            bf16* odst = oc + row * KD;
+            *(bf16x8*)(odst + D) = ox;
+            *(bf16x8*)(odst + D + 8) = bf16x8{};
         }
     }
 }
 
 // ---------------------------------------------------------------- main ----
 // Block b: q head b % hq (fastest, so that the workgroups of one head sit on
-// one XCD's L2 and follow each other down the same Q'/dO rows), then the
+// one XCD's L2 and follow each other down the same Q'/dO' rows), then the
 // sequence, then the key tile (tile 0, with the most query rows, first).
 template <int D>
-__global__ __launch_bounds__(kBwdThreads, 2) void bwd_main_kernel(
-    const bf16* __restrict__ qc, const bf16* __restrict__ ws_k, const bf16* __restrict__ v, int64_t kv_stride,
-    const bf16* __restrict__ dout, int64_t do_stride, const float* __restrict__ l2g,
-    const float* __restrict__ deltag, const float* __restrict__ key_score, const int* __restrict__ cu_kept,
-    int n_seqs, int64_t m_tot, int hq, int grp, int64_t mp, int n_kt, float* __restrict__ colsum,
-    float2* __restrict__ part) {
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_main_kernel(
+    const bf16* __restrict__ qc, const bf16* __restrict__ oc, const bf16* __restrict__ ws_k,
+    const bf16* __restrict__ v, int64_t kv_stride, const float* __restrict__ key_score,
+    const int* __restrict__ cu_kept, int n_seqs, int64_t m_tot, int hq, int grp, int64_t mp, int n_kt,
+    float* __restrict__ colsum, float2* __restrict__ part) {
     using L = BwdLds<D>;
     constexpr int KD = L::KD;
-    constexpr int KS = D / 16;   // k-steps of the q.k part; one more for the bias columns
+    constexpr int KS = D / 16;   // k-steps of the data columns; one more for the extra columns
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    bf16* const qs = (bf16*)smem;                       // [2][QT]
-    bf16* const os = qs + 2 * L::QT;                    // [2][OT]
-    float* const ls = (float*)(os + 2 * L::OT);         // [2][64] LSE2
-    float* const dls = ls + 2 * kBwdQ;                  // [2][64] Delta
+    bf16* const qs = (bf16*)smem;                   // [slots][T] Q'
+    bf16* const os = qs + kBwdSlots * L::T;         // [slots][T] dO'
     __shared__ float2 wsum[kBwdWaves];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -193,9 +226,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_main_kernel(
     const int kj = kb0 + il;            // this lane's key
     const bool kvalid = kj < ms;
 
-    // this wave's K' and V fragments as B operands (lane j + 32 (k / 8) holds
-    // B[k..k+7][j]); keys past the sequence end are zero and masked
-    bf16x8 kf[KS + 1], vf[KS];
+    // this wave's K' and V' fragments as B operands (lane j + 32 (k / 8) holds
+    // B[k..k+7][j]); V' is V with the columns (1, 1, 0...) appended; keys past
+    // the sequence end are zero and masked
+    bf16x8 kf[KS + 1], vf[KS + 1];
     {
         const bf16* kr = ws_k + ((int64_t)hk * mp + prow0 + (kvalid ? kj : 0)) * KD + half * 8;
         const bf16* vr = v + (int64_t)(cs0 + (kvalid ? kj : 0)) * kv_stride + (int64_t)hk * D + half * 8;
@@ -203,101 +237,146 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_main_kernel(
         for (int t = 0; t <= KS; ++t) kf[t] = kvalid ? *(const bf16x8*)(kr + t * 16) : bf16x8{};
 #pragma unroll
         for (int t = 0; t < KS; ++t) vf[t] = kvalid ? *(const bf16x8*)(vr + t * 16) : bf16x8{};
+        vf[KS] = bf16x8{};
+        if (kvalid && half == 0) {
+            vf[KS][0] = (bf16)1.0f;
+            vf[KS][1] = (bf16)1.0f;
+        }
     }
 
-    // query tiles from the one holding key0 to the end of the sequence
+    // query tiles from the one holding key0 to the end of the sequence; the
+    // padded layout keeps every tile row inside this head's rows
     const int q_begin = key0 & ~(kBwdQ - 1);
     const int n_qt = (ms - q_begin + kBwdQ - 1) / kBwdQ;
-    // buffer resources over this head's rows from the sequence start: reads
-    // past the end return zero
     const __amdgpu_buffer_rsrc_t qrs =
         make_rsrc(qc + ((int64_t)h * mp + prow0) * KD, (uint32_t)((mp - prow0) * KD * 2));
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(dout + (int64_t)cs0 * do_stride + (int64_t)h * D,
-                                                 (uint32_t)(((m_tot - cs0 - 1) * do_stride + D) * 2));
-    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(l2g + (int64_t)h * m_tot + cs0, (uint32_t)((m_tot - cs0) * 4));
-    const __amdgpu_buffer_rsrc_t drs = make_rsrc(deltag + (int64_t)h * m_tot + cs0, (uint32_t)((m_tot - cs0) * 4));
+    const __amdgpu_buffer_rsrc_t ors =
+        make_rsrc(oc + ((int64_t)h * mp + prow0) * KD, (uint32_t)((mp - prow0) * KD * 2));
     const int n_per_tile = L::per_wave(wave);
     auto load_tile = [&](int t, int slot) {
-        const uint32_t q0 = (uint32_t)(q_begin + t * kBwdQ);
-        for (int i = wave; i < L::Q_INSTR; i += kBwdWaves) {
+        const uint32_t so = (uint32_t)(q_begin + t * kBwdQ) * (KD * 2);
+        for (int i = wave; i < L::INSTR; i += kBwdWaves) {
             const int sl = i * 64 + lane;
-            const int r = sl / L::QROW, c = sl % L::QROW;
-            const uint32_t off = (uint32_t)((r * KD + (c < L::QCH ? c : 0) * 8) * 2);
-            lds_load16_buf(qrs, off, q0 * (KD * 2), qs + slot * L::QT + i * 512);
+            const int r = sl / L::ROW, c = sl % L::ROW;
+            const uint32_t off = (uint32_t)((r * KD + (c < L::CH ? c : 0) * 8) * 2);
+            lds_load16_buf(qrs, off, so, qs + slot * L::T + i * 512);
+            lds_load16_buf(ors, off, so, os + slot * L::T + i * 512);
         }
-        // rows of dO, LSE2 and Delta can run past the last token: their row
-        // offset goes into the per-lane offset, which the bounds check covers
-        for (int i = wave; i < L::O_INSTR; i += kBwdWaves) {
-            const int sl = i * 64 + lane;
-            const int r = sl / L::OROW, c = sl % L::OROW;
-            const uint32_t off = (uint32_t)(((q0 + r) * do_stride + (c < L::OCH ? c : 0) * 8) * 2);
-            lds_load16_buf(ors, off, 0u, os + slot * L::OT + i * 512);
-        }
-        if (wave == 3)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                lrs, (__attribute__((address_space(3))) void*)(ls + slot * kBwdQ), 4, (q0 + lane) * 4, 0, 0, 0);
-        if (wave == 2)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                drs, (__attribute__((address_space(3))) void*)(dls + slot * kBwdQ), 4, (q0 + lane) * 4, 0, 0, 0);
     };
-    load_tile(0, 0);
-    if (n_qt > 1) load_tile(1, 1);
+#pragma unroll
+    for (int t = 0; t < kBwdSlots - 1; ++t)
+        if (t < n_qt) load_tile(t, t);
 
     float csum = 0.0f, asum = 0.0f;
-    for (int t = 0; t < n_qt; ++t) {
-        const int slot = t & 1;
-        // tile t has landed once at most the next tile's loads are outstanding
-        if (t + 1 < n_qt) wait_vm_le(n_per_tile);
-        else __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        const int q0 = q_begin + t * kBwdQ;
-        const bf16* qt = qs + slot * L::QT;
-        const bf16* ot = os + slot * L::OT;
-        const float* lt = ls + slot * kBwdQ;
-        const float* dt = dls + slot * kBwdQ;
-        // one 32-query x 32-key block; masked: causal diagonal or the
-        // sequence's last rows (keys past the end need no test: every query
-        // at or after them is past the end too)
-        auto block = [&](int qb, bool masked) {
-            f32x16 sacc = f32x16{}, pacc = f32x16{};
-            const bf16* qrow = qt + (qb * 32 + il) * (L::QROW * 8) + half * 8;
-            const bf16* orow = ot + (qb * 32 + il) * (L::OROW * 8) + half * 8;
-#pragma unroll
-            for (int k = 0; k <= KS; ++k)
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qrow + k * 16), kf[k], sacc, 0, 0, 0);
-#pragma unroll
-            for (int k = 0; k < KS; ++k)
-                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(orow + k * 16), vf[k], pacc, 0, 0, 0);
-            // accumulator register 4a + e is query row 8a + 4 half + e of the block
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int rb = qb * 32 + 8 * a + 4 * half;
-                const f32x4 lv = *(const f32x4*)(lt + rb);
-                const f32x4 dv = *(const f32x4*)(dt + rb);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * a + e;
-                    const float sv = sacc[r];
-                    float p = __builtin_amdgcn_exp2f(sv - lv[e]);
-                    if (masked) {
-                        const int qi = q0 + rb + e;
-                        p = (qi >= kj && qi < ms) ? p : 0.0f;
-                    }
-                    const float ds = p * (pacc[r] - dv[e]);
-                    csum += ds;
-                    asum = fmaf(ds, sv, asum);
-                }
-            }
+    // Software pipeline over this wave's 32-query blocks.  Block qb of a tile
+    // accumulates into set qb (sA/pA or sB/pB); each step issues the 18 MFMAs
+    // of one block (D = 128) with the element work of the block before it,
+    // whose accumulators are the other set, spread over them.  A block's
+    // element work may thus run after its tile's slot is released: it needs
+    // only registers.  The wave's active blocks are consecutive: the first is
+    // its diagonal block (query rows kb0..kb0+31), the last holds the
+    // sequence's last row.  So inside the loop only the diagonal block needs
+    // a mask: right after its MFMAs its causally hidden logits are set to
+    // -1e30 (exp2 gives 0, and 0 * -1e30 stays finite in the dS S' sum).  The
+    // last block's element work, after the loop, masks rows past the end.
+    // Sets start at zero, so the element work of the step before the first
+    // block adds exactly 0 (P = 1, dP' = 0).
+    f32x16 sA = f32x16{}, pA = f32x16{}, sB = f32x16{}, pB = f32x16{};
+    constexpr int NI = 2 * (KS + 1);   // MFMAs per block
+    constexpr int PF = 4;              // operand reads ahead of their MFMA
+    auto elem = [&](const f32x16& sv, const f32x16& pv, int r, float& cs, float& as) {
+        const float p = __builtin_amdgcn_exp2f(sv[r]);
+        const float ds = p * pv[r];
+        cs += ds;
+        as = fmaf(ds, sv[r], as);
+    };
+    auto step = [&](auto QB, const bf16* qt, const bf16* ot) {
+        constexpr int qb = decltype(QB)::value;
+        f32x16& sc = qb ? sB : sA;
+        f32x16& pc = qb ? pB : pA;
+        f32x16& sp = qb ? sA : sB;
+        f32x16& pp = qb ? pA : pB;
+        float& cs = csum;   // named here so that the generic lambda captures them
+        float& as = asum;
+        const bf16* qrow = qt + (qb * 32 + il) * (L::ROW * 8) + half * 8;
+        const bf16* orow = ot + (qb * 32 + il) * (L::ROW * 8) + half * 8;
+        auto frag = [&](int i) -> bf16x8 {
+            return i <= KS ? *(const bf16x8*)(qrow + i * 16) : *(const bf16x8*)(orow + (i - KS - 1) * 16);
         };
+        bf16x8 ring[PF];
 #pragma unroll
-        for (int qb = 0; qb < kBwdQ / 32; ++qb) {
-            const int qr0 = q0 + qb * 32;                       // first query row of the block
-            if (qr0 + 31 < kb0 || qr0 >= ms) continue;          // every query before this wave's keys, or past the end
-            if (qr0 < kb0 + 31 || qr0 + 31 >= ms) block(qb, true);
-            else block(qb, false);
+        for (int i = 0; i < PF; ++i) ring[i] = frag(i);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            bf16x8 x = ring[i % PF];
+            if (i + PF < NI) ring[i % PF] = frag(i + PF);
+            // the memory clobber keeps the read above from sinking toward its
+            // use; re-defining the MFMA's LDS operand here keeps the MFMA from
+            // rising toward its read
+            __asm__ volatile("" ::: "memory");
+            __asm__ volatile("" : "+v"(x));
+            if (i == 0) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, kf[0], f32x16{}, 0, 0, 0);
+            else if (i <= KS) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, kf[i], sc, 0, 0, 0);
+            else if (i == KS + 1) pc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, vf[0], f32x16{}, 0, 0, 0);
+            else pc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, vf[i - KS - 1], pc, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (r * NI / 16 != i) continue;
+                __asm__ volatile("" : "+v"(sp[r]), "+v"(pp[r]));   // not before this MFMA
+                elem(sp, pp, r, cs, as);
+                __asm__ volatile("" ::"v"(cs), "v"(as));           // and done before the next
+            }
         }
-        __syncthreads();   // every wave is done with this slot
-        if (t + 2 < n_qt) load_tile(t + 2, slot);
+    };
+    // the diagonal block: hide key j from query rows before it
+    auto diag_mask = [&](f32x16& sv) {
+        const int lo = il - 4 * half;   // row k of the block (minus 4 half) sees key il iff k >= lo
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int k = 8 * (r >> 2) + (r & 3);
+            sv[r] = k >= lo ? sv[r] : -1e30f;
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    int last_set = -1, last_qr0 = 0;
+    for (int t = 0; t < n_qt; ++t) {
+        const int slot = t % kBwdSlots;
+        // tile t has landed once at most the later tiles' loads (up to two)
+        // are outstanding; after the barrier every wave's part of it has
+        // landed and every wave is past tile t-1, whose slot takes tile t+3
+        wait_vm_le(min(kBwdSlots - 2, n_qt - 1 - t) * n_per_tile);
+        __syncthreads();
+        if (t + kBwdSlots - 1 < n_qt) load_tile(t + kBwdSlots - 1, (t + kBwdSlots - 1) % kBwdSlots);
+        const int q0 = q_begin + t * kBwdQ;
+        const bf16* qt = qs + slot * L::T;
+        const bf16* ot = os + slot * L::T;
+        if (q0 + 31 >= kb0 && q0 < ms) {
+            step(I0{}, qt, ot);
+            if (q0 == kb0) diag_mask(sA);
+            last_set = 0;
+            last_qr0 = q0;
+        }
+        if (q0 + 63 >= kb0 && q0 + 32 < ms) {
+            step(I1{}, qt, ot);
+            if (q0 + 32 == kb0) diag_mask(sB);
+            last_set = 1;
+            last_qr0 = q0 + 32;
+        }
+    }
+    // element work of the last block: rows past the sequence end are hidden
+    if (last_set >= 0) {
+        const int hi = ms - last_qr0 - 4 * half;
+        const f32x16& sv = last_set ? sB : sA;
+        const f32x16& pv = last_set ? pB : pA;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int k = 8 * (r >> 2) + (r & 3);
+            const float p = k < hi ? __builtin_amdgcn_exp2f(sv[r]) : 0.0f;
+            const float ds = p * pv[r];
+            csum += ds;
+            asum = fmaf(ds, sv[r], asum);
+        }
     }
     // the two lane halves hold the same key over different query rows
     float cs_tot;
@@ -329,49 +408,46 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_main_kernel(
 }
 
 // -------------------------------------------------------------- reduce ----
-// dL/ds_j = sum_h g_h C_hj (every q head sees every key of its sequence)
-__global__ __launch_bounds__(256) void bwd_ds_kernel(const float* __restrict__ colsum, const float* __restrict__ gain,
-                                                     int hq, int64_t m_tot, float* __restrict__ ds) {
-    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (j >= m_tot) return;
-    float t = 0.0f;
-    for (int h = 0; h < hq; ++h) t = fmaf(gain[h], colsum[(int64_t)h * m_tot + j], t);
-    ds[j] = t;
-}
-
-// per head: dL/dg_h = sum of the (s C) partials; T_h = ln 2 * A_h - g_h dL/dg_h
-__global__ __launch_bounds__(256) void bwd_head_kernel(const float2* __restrict__ part, const float* __restrict__ gain,
-                                                       int n_part, float* __restrict__ dg, float* __restrict__ th) {
-    __shared__ float2 red[4];
-    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    float a = 0.0f, c = 0.0f;
-    for (int i = tid; i < n_part; i += 256) {
-        const float2 x = part[(int64_t)h * n_part + i];
-        a += x.x;
-        c += x.y;
+// One launch: blocks 0..n_ds-1 write dL/ds_j = sum_h g_h C_hj (every q head
+// sees every key of its sequence); block n_ds reduces the per-block partials
+// of each head to dL/dg_h and T_h = ln 2 * A_h - g_h dL/dg_h, then dL/dtau =
+// -sum_h T_h / tau.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ colsum,
+                                                         const float2* __restrict__ part,
+                                                         const float* __restrict__ gain, int hq, int64_t m_tot,
+                                                         int n_part, float tau, float* __restrict__ ds,
+                                                         float* __restrict__ dg, float* __restrict__ dtau) {
+    const int tid = threadIdx.x;
+    if (blockIdx.x + 1 < gridDim.x) {
+        const int64_t j = (int64_t)blockIdx.x * 256 + tid;
+        if (j >= m_tot) return;
+        float t = 0.0f;
+        for (int h = 0; h < hq; ++h) t = fmaf(gain[h], colsum[(int64_t)h * m_tot + j], t);
+        ds[j] = t;
+        return;
     }
+    // heads spread over the four waves, partials over the lanes
+    __shared__ float tw[4];
+    const int lane = tid & 63, w = tid >> 6;
+    float tsum = 0.0f;
+    for (int h = w; h < hq; h += 4) {
+        float a = 0.0f, c = 0.0f;
+        for (int i = lane; i < n_part; i += 64) {
+            const float2 x = part[(int64_t)h * n_part + i];
+            a += x.x;
+            c += x.y;
+        }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        a += __shfl_xor(a, o, 64);
-        c += __shfl_xor(c, o, 64);
+        for (int o = 32; o > 0; o >>= 1) {
+            a += __shfl_xor(a, o, 64);
+            c += __shfl_xor(c, o, 64);
+        }
+        if (lane == 0) dg[h] = a;
+        tsum += kLn2 * c - gain[h] * a;
     }
-    if (lane == 0) red[w] = make_float2(a, c);
+    if (lane == 0) tw[w] = tsum;
     __syncthreads();
-    if (tid == 0) {
-        const float dgh = (red[0].x + red[1].x) + (red[2].x + red[3].x);
-        const float ah = (red[0].y + red[1].y) + (red[2].y + red[3].y);
-        dg[h] = dgh;
-        th[h] = kLn2 * ah - gain[h] * dgh;
-    }
-}
-
-__global__ __launch_bounds__(64) void bwd_tau_kernel(const float* __restrict__ th, int hq, float tau,
-                                                     float* __restrict__ dtau) {
-    float t = 0.0f;
-    for (int h = threadIdx.x; h < hq; h += 64) t += th[h];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
-    if (threadIdx.x == 0) dtau[0] = -t / tau;
+    if (tid == 0) dtau[0] = -((tw[0] + tw[1]) + (tw[2] + tw[3])) / tau;
 }
 
 __global__ __launch_bounds__(64) void bwd_zero_kernel(float* __restrict__ dg, int hq, float* __restrict__ dtau) {
@@ -380,7 +456,7 @@ __global__ __launch_bounds__(64) void bwd_zero_kernel(float* __restrict__ dg, in
 }
 
 struct BwdLayout {
-    size_t qc, l2, delta, colsum, part, th, total;
+    size_t qc, oc, colsum, part, total;
 };
 
 BwdLayout bwd_layout(int n_seqs, int64_t m_tot, int max_kept, int hq, int d) {
@@ -390,11 +466,9 @@ BwdLayout bwd_layout(int n_seqs, int64_t m_tot, int max_kept, int hq, int d) {
     BwdLayout L;
     size_t o = 0;
     L.qc = o;     o += al((size_t)hq * mp * (d + kBwdExtra) * 2);
-    L.l2 = o;     o += al((size_t)hq * m_tot * 4);
-    L.delta = o;  o += al((size_t)hq * m_tot * 4);
+    L.oc = o;     o += al((size_t)hq * mp * (d + kBwdExtra) * 2);
     L.colsum = o; o += al((size_t)hq * m_tot * 4);
     L.part = o;   o += al((size_t)hq * n_seqs * (n_kt > 0 ? n_kt : 1) * 8);
-    L.th = o;     o += al((size_t)hq * 4);
     L.total = o;
     return L;
 }
@@ -405,18 +479,16 @@ int launch_bwd_d(const BwdArgs& a, hipStream_t st) {
     const BwdLayout W = bwd_layout(a.n_seqs, a.m_tot, a.max_kept_seqlen, a.hq, D);
     char* w = (char*)a.ws;
     bf16* qc = (bf16*)(w + W.qc);
-    float* l2 = (float*)(w + W.l2);
-    float* delta = (float*)(w + W.delta);
+    bf16* oc = (bf16*)(w + W.oc);
     float* colsum = (float*)(w + W.colsum);
     float2* part = (float2*)(w + W.part);
-    float* th = (float*)(w + W.th);
     const int grp = a.hq / a.hkv;
     const int n_kt = (a.max_kept_seqlen + kBwdKeys - 1) / kBwdKeys;
     const int64_t nblk = (int64_t)n_kt * a.n_seqs * a.hq;
     if (nblk > 0x7fffffff) return TG_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)(a.mp / 64), a.hq), dim3(256), 0, st, a.q, a.q_stride,
                        a.o, a.dout, a.do_stride, a.lse, a.gain, a.qk_scale_log2, a.ws_cs, (int)a.rope, a.cu_kept,
-                       a.n_seqs, a.m_tot, a.hq, a.mp, qc, l2, delta);
+                       a.n_seqs, a.m_tot, a.hq, a.mp, qc, oc);
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute((const void*)bwd_main_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -425,13 +497,12 @@ int launch_bwd_d(const BwdArgs& a, hipStream_t st) {
         attr_set = true;
     }
     hipLaunchKernelGGL(bwd_main_kernel<D>, dim3((unsigned)nblk), dim3(kBwdThreads), L::SMEM, st, (const bf16*)qc,
-                       a.ws_k, a.v, a.kv_stride, a.dout, a.do_stride, (const float*)l2, (const float*)delta,
-                       a.key_score, a.cu_kept, a.n_seqs, a.m_tot, a.hq, grp, a.mp, n_kt, colsum, part);
-    hipLaunchKernelGGL(bwd_ds_kernel, dim3((unsigned)((a.m_tot + 255) / 256)), dim3(256), 0, st, (const float*)colsum,
-                       a.gain, a.hq, a.m_tot, a.d_score);
-    hipLaunchKernelGGL(bwd_head_kernel, dim3((unsigned)a.hq), dim3(256), 0, st, (const float2*)part, a.gain,
-                       a.n_seqs * n_kt, a.d_gain, th);
-    hipLaunchKernelGGL(bwd_tau_kernel, dim3(1), dim3(64), 0, st, (const float*)th, a.hq, a.tau, a.d_tau);
+                       (const bf16*)oc, a.ws_k, a.v, a.kv_stride, a.key_score, a.cu_kept, a.n_seqs, a.m_tot, a.hq,
+                       grp, a.mp, n_kt, colsum, part);
+    const unsigned n_ds = (unsigned)((a.m_tot + 255) / 256);
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(n_ds + 1), dim3(256), 0, st, (const float*)colsum,
+                       (const float2*)part, a.gain, a.hq, a.m_tot, a.n_seqs * n_kt, a.tau, a.d_score, a.d_gain,
+                       a.d_tau);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 

@@ -8,7 +8,7 @@
 // over the kept keys of its sequence with pos_j <= q_pos.
 //
 // The cache is the one tg_attn_prepare writes: rotated K' rows with the
-// bias columns (s_hi, s_lo, s_hi, 1) and V^T with its permuted columns.  One
+// bias columns (s_hi, s_lo, s_hi, 1, 1) and V^T with its permuted columns.  One
 // query per sequence makes this a matrix-vector product, so it is bound by
 // reading the cache (K' (D+16) x 2 B + V^T D x 2 B per key and kv head), not by
 // arithmetic: split over keys.  The split kernel gives each workgroup 64 keys

@@ -216,7 +216,7 @@ def test_attn_gate_grads_validation(lib):
     L = lib
     cache = L.tg_attn_workspace_bytes(1, 100, 8, 128)
     need = L.tg_attn_gate_grads_workspace_bytes(1, 100, 100, 16, 128)
-    assert need >= 16 * 100 * (128 + 16) * 2 + 3 * 16 * 100 * 4
+    assert need >= 2 * 16 * 100 * (128 + 16) * 2 + 16 * 100 * 4
     assert L.tg_attn_gate_grads_workspace_bytes(1, 100, 100, 16, 96) == 0
     a = lambda **kw: L.tg_attn_gate_grads(*[kw.get(k, v) for k, v in [
         ("q", FAKE), ("qs", 2048), ("v", FAKE), ("kvs", 1024), ("s", FAKE), ("g", FAKE), ("tau", 0.9),

@@ -393,8 +393,8 @@ def test_attention_prepare_layout():
     np.testing.assert_array_equal(kp[:, rows, d], np.broadcast_to(hi, (hkv, m)))
     np.testing.assert_array_equal(kp[:, rows, d + 2], np.broadcast_to(hi, (hkv, m)))
     assert np.all(np.abs(kp[:, rows, d] + kp[:, rows, d + 1] - sk[None, :]) <= np.abs(sk) * 2.0 ** -16 + 1e-30)
-    np.testing.assert_array_equal(kp[:, rows, d + 3], 1.0)
-    np.testing.assert_array_equal(kp[:, rows, d + 4:], 0.0)
+    np.testing.assert_array_equal(kp[:, rows, d + 3:d + 5], 1.0)
+    np.testing.assert_array_equal(kp[:, rows, d + 5:], 0.0)
     cols = np.array([_vt_col(int(r)) for r in rows])
     np.testing.assert_array_equal(vt[:, :, cols].transpose(2, 0, 1), vf)
     pad = np.setdiff1d(np.arange(mp), rows)
