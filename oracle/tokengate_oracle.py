@@ -35,7 +35,9 @@ Parity status per function:
                       pruning == masking, tau placement, GQA, varlen, closed forms)
   keybias_attention_gate_grads
                       pinned (central finite differences of the forward, closed
-                      forms: g = 0 gives ds = 0, sum_j ds_j = 0, tau scaling)
+                      forms: g = 0 gives ds = 0, sum_j ds_j = 0, tau scaling);
+                      its condition scales pinned by the triangle inequality
+                      and the one-key closed form
   keybias_decode      pinned (equals the prefill row of a kept token placed at its
                       position, closed forms, no-visible-key case, shift invariance)
 """
