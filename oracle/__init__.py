@@ -13,6 +13,7 @@ from .tokengate_oracle import (  # noqa: F401
     keybias_attention_gate_grads,
     keybias_decode,
     kept_counts,
+    random_budgets,
     random_k_select,
     random_scores,
     rope,

@@ -26,6 +26,8 @@ Parity status per function:
   gate_score          pinned (torch fp64 linear+silu, closed forms, scalar loop)
   topk_select         pinned (brute-force sort, exhaustive tiny cases, invariants)
   splitmix64          pinned (published reference outputs for seed 0)
+  random_budgets      pinned (range, full and empty budgets reached, uniform
+                      frequencies over seeds, determinism)
   random_k_select     pinned (budget and question invariants, determinism, selection
                       frequencies uniform over seeds)
   gather_kept         pinned (definition, invariants)
@@ -185,6 +187,29 @@ def random_scores(seed: int, n: int) -> np.ndarray:
     """Uniform random scores in [0, 1) for n tokens: the top 24 bits of
     SplitMix64 output t (t = global token index), times 2^-24 (exact in fp32)."""
     return ((splitmix64(seed, n) >> np.uint64(40)).astype(np.float64) * 2.0 ** -24).astype(np.float32)
+
+
+def random_budgets(seed, doc_begin, doc_end):
+    """Random-budget sampling for the training schedule ([ES] "¿Qué es la
+    atención…?": each step averages a full-context loss and a loss at a random
+    token budget, so one gate serves every budget).
+
+    Reading (the pages name no distribution): sequence s draws its document
+    budget uniformly from {0, 1, ..., n_doc_s}, where 0 keeps only the question
+    and n_doc_s is the full context.  The draw uses SplitMix64 output s for
+    `seed`: with u = its top 53 bits, K_s = floor(u (n_doc_s + 1) / 2^53),
+    computed exactly in integers.  Returns int32 [S].
+    """
+    db = np.asarray(doc_begin, dtype=np.int64)
+    de = np.asarray(doc_end, dtype=np.int64)
+    if np.any(de < db):
+        raise ValueError("doc_end < doc_begin")
+    z = splitmix64(seed, len(db))
+    out = np.empty(len(db), dtype=np.int32)
+    for i in range(len(db)):
+        u = int(z[i]) >> 11
+        out[i] = (u * (int(de[i] - db[i]) + 1)) >> 53
+    return out
 
 
 def random_k_select(seed, cu_seqlens, doc_begin, doc_end, k_doc):

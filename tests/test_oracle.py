@@ -529,3 +529,31 @@ def test_gate_grad_scales_bound_and_closed_form():
     np.testing.assert_allclose(ms1, (2 * np.abs(dp) * np.abs(g1)[None, :]).sum(1), rtol=1e-12)
     np.testing.assert_allclose(mg1, (2 * np.abs(dp) * np.abs(s1)[:, None]).sum(0), rtol=1e-12)
     np.testing.assert_allclose(mt1, (2 * np.abs(dp) * np.abs(qk)).sum() / (np.sqrt(8) * tau ** 2), rtol=1e-10)
+
+
+# ------------------------------------------------------ random-budget sampling ----
+def test_random_budgets_range_and_uniformity():
+    """Budgets lie in {0..n_doc}; over seeds every value is drawn with frequency
+    1/(n_doc+1) (binomial bound at ~5 sigma), both ends included; an empty
+    document gets 0; the same seed gives the same budgets, another seed others."""
+    db = np.array([0, 5, 0, 3])
+    de = np.array([9, 5, 1, 40003])
+    seeds = 3000
+    cnt = np.zeros(10)
+    ends = [0, 0]
+    for sd in range(seeds):
+        k = oracle.random_budgets(sd, db, de)
+        assert k.dtype == np.int32 and np.all(k >= 0) and np.all(k <= de - db)
+        assert k[1] == 0
+        cnt[k[0]] += 1
+        ends[0] += k[2] == 0
+        ends[1] += k[2] == 1
+    p = 1 / 10
+    assert np.all(np.abs(cnt / seeds - p) <= 5 * np.sqrt(p * (1 - p) / seeds))
+    assert abs(ends[0] / seeds - 0.5) <= 5 * np.sqrt(0.25 / seeds)
+    np.testing.assert_array_equal(oracle.random_budgets(77, db, de), oracle.random_budgets(77, db, de))
+    big = [oracle.random_budgets(sd, db, de)[3] for sd in range(400)]
+    assert len(set(big)) >= 390                         # 40001 values: almost never equal
+    assert abs(np.mean(big) / 40000 - 0.5) <= 5 * np.sqrt(1 / 12 / 400)
+    with pytest.raises(ValueError):
+        oracle.random_budgets(0, [3], [2])
