@@ -124,6 +124,24 @@ int tg_topk_select(const float* scores, int32_t n_seqs, int64_t n_tokens_total, 
                    const int32_t* k_doc, const int32_t* cu_kept, int32_t* kept_idx,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Random-budget sampling, on the host: the training schedule averages a
+ * full-context loss and a loss at a random token budget, so that one gate
+ * serves every budget (spke.com article, section on token-gated attention).
+ * The pages name no distribution; sequence s draws its document budget
+ * uniformly from {0, ..., doc_end[s] - doc_begin[s]} (0 keeps only the
+ * question, the top value the whole context):
+ *     k_doc[s] = floor(u_s (n_doc_s + 1) / 2^53),  u_s = top 53 bits of
+ *     SplitMix64 output s for `seed` (see tg_random_k_select),
+ * in exact integer arithmetic.  Use a seed other than the random-K scores'.
+ *   doc_begin_h, doc_end_h  [host] S int32, 0 <= b <= e
+ *   k_doc_h       [host, out] S int32, ready for tg_kept_counts
+ * Errors: TG_ERR_INVALID_ARG on NULL pointers, negative S or spans.  Never
+ * touches the GPU.
+ */
+int tg_random_budgets(uint64_t seed, int32_t n_seqs, const int32_t* doc_begin_h, const int32_t* doc_end_h,
+                      int32_t* k_doc_h);
+
 /* Workspace bytes tg_random_k_select needs: 4 bytes per token for the random
  * scores plus what tg_topk_select needs. */
 size_t tg_random_k_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen);

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     tg_gather_kept,
     tg_kept_counts,
     tg_keybias_attn_prefill,
+    tg_random_budgets,
     tg_random_k_select,
     tg_topk_select,
     tg_topk_workspace_bytes,

@@ -27,6 +27,7 @@ _P, _I32, _I64, _F, _D, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, 
 SIGNATURES = {
     "tg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tg_kept_counts": (ctypes.c_int, [_I32, _P, _P, _P, _P, _P]),
+    "tg_random_budgets": (ctypes.c_int, [ctypes.c_uint64, _I32, _P, _P, _P]),
     "tg_gate_score": (ctypes.c_int, [_P, _I32, _I64, _I32, _I64, _P, _P, _P, _F, _I32, _P, _P]),
     "tg_topk_workspace_bytes": (_SZ, [_I32, _I64, _I32]),
     "tg_topk_select": (ctypes.c_int, [_P, _I32, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -329,3 +330,16 @@ def tg_attn_gate_grads(q, v, key_score, head_gain, tau: float, cu_kept, max_kept
                                    _ptr(workspace), workspace.numel(), _stream(q))
     _check("tg_attn_gate_grads", st)
     return d_score, d_gain, d_tau
+
+
+def tg_random_budgets(seed: int, doc_begin, doc_end):
+    """Host call: a uniform random document budget per sequence (int32 numpy array)."""
+    db = np.ascontiguousarray(doc_begin, dtype=np.int32)
+    de = np.ascontiguousarray(doc_end, dtype=np.int32)
+    if db.shape != de.shape or db.ndim != 1:
+        raise ValueError("doc_begin and doc_end must be 1-D of one length")
+    out = np.empty(len(db), dtype=np.int32)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    st = load().tg_random_budgets(int(seed) % (1 << 64), len(db), p(db), p(de), p(out))
+    _check("tg_random_budgets", st)
+    return out

@@ -43,6 +43,24 @@ int tg_kept_counts(int32_t n_seqs, const int32_t* cu_seqlens_h, const int32_t* d
     return TG_OK;
 }
 
+int tg_random_budgets(uint64_t seed, int32_t n_seqs, const int32_t* doc_begin_h, const int32_t* doc_end_h,
+                      int32_t* k_doc_h) {
+    if (n_seqs < 0) return TG_ERR_INVALID_ARG;
+    if (n_seqs > 0 && (!doc_begin_h || !doc_end_h || !k_doc_h)) return TG_ERR_INVALID_ARG;
+    for (int32_t s = 0; s < n_seqs; ++s)
+        if (doc_begin_h[s] < 0 || doc_end_h[s] < doc_begin_h[s]) return TG_ERR_INVALID_ARG;
+    for (int32_t s = 0; s < n_seqs; ++s) {
+        // SplitMix64 output s: the finalizer of seed + (s + 1) * golden-ratio increment
+        uint64_t z = seed + (uint64_t)(s + 1) * 0x9E3779B97F4A7C15ull;
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+        z ^= z >> 31;
+        const uint64_t n = (uint64_t)(doc_end_h[s] - doc_begin_h[s]) + 1;
+        k_doc_h[s] = (int32_t)(((unsigned __int128)(z >> 11) * n) >> 53);
+    }
+    return TG_OK;
+}
+
 int tg_gate_score(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d_model,
                   int64_t x_row_stride, const void* w1, const float* b1, const float* w2,
                   float b2, int32_t d_hid, float* scores, void* stream) {

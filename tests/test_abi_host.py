@@ -271,3 +271,22 @@ def test_library_has_no_undefined_internal_symbols(lib):
     out = subprocess.run(["nm", "-D", _lib.LIB_PATH], capture_output=True, text=True).stdout
     undefined = [l for l in out.splitlines() if " U " in l and "_ZN2tg" in l]
     assert not undefined, undefined[:3]
+
+
+def test_random_budgets_host_bit_exact(lib):
+    """tg_random_budgets (host code) against oracle.random_budgets, bit-exact, for
+    seeds up to 2^64 - 1 and spans up to 2^31 - 2; and its validation."""
+    import oracle
+    from learned_token_pruning_05_amd import _lib
+    db = np.array([0, 5, 0, 3, 0, 100, 7], dtype=np.int32)
+    de = np.array([9, 5, 1, 40003, 2 ** 31 - 2, 130916, 8], dtype=np.int32)
+    for seed in (0, 1, 12345, 2 ** 63, 2 ** 64 - 1):
+        np.testing.assert_array_equal(_lib.tg_random_budgets(seed, db, de), oracle.random_budgets(seed, db, de))
+    assert lib.tg_random_budgets(1, -1, None, None, None) == 1
+    bad = np.array([5], dtype=np.int32)
+    good = np.array([4], dtype=np.int32)
+    out = np.zeros(1, dtype=np.int32)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert lib.tg_random_budgets(1, 1, p(bad), p(good), p(out)) == 1   # end before begin
+    assert lib.tg_random_budgets(1, 1, p(good), p(bad), None) == 1
+    assert lib.tg_random_budgets(1, 0, None, None, None) == 0

@@ -210,6 +210,25 @@ def test_random_k_bit_exact(name, seed):
     np.testing.assert_array_equal(kept.cpu().numpy(), kept_ref)
 
 
+@pytest.mark.parametrize("seed", [3, 2 ** 64 - 2])
+def test_random_budget_random_k_chain(seed):
+    """The random training mode end to end: budgets from tg_random_budgets (host),
+    kept counts, then random-K selection on the GPU, against the oracle chain,
+    bit-exact, on the packed varlen shape."""
+    _print_case(f"random budgets + random-K varlen seed={seed}")
+    w = workloads.by_name("varlen")
+    kd = tg.tg_random_budgets(seed ^ 0x5A5A, w.doc_begin, w.doc_end)
+    kd_ref = oracle.random_budgets(seed ^ 0x5A5A, w.doc_begin, w.doc_end)
+    np.testing.assert_array_equal(kd, kd_ref)
+    kept_ref, ck = oracle.random_k_select(seed, w.cu_seqlens, w.doc_begin, w.doc_end, kd_ref)
+    ck_gpu = tg.tg_kept_counts(w.cu_seqlens, w.doc_begin, w.doc_end, kd)
+    np.testing.assert_array_equal(ck_gpu, ck)
+    kept = tg.tg_random_k_select(seed, _i32(w.cu_seqlens), _i32(w.doc_begin), _i32(w.doc_end), _i32(kd),
+                                 _i32(ck), w.n_tokens, int(ck[-1]), int(max(w.seqlens)))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kept.cpu().numpy(), kept_ref)
+
+
 @pytest.mark.parametrize("name", ["tiny", "16k", "128k", "varlen"])
 def test_gather_bit_exact(name):
     _print_case(f"gather {name}")
