@@ -104,6 +104,41 @@ class Layer:
                            rope_base=self.w.rope_base, out=self.out, lse=self.lse)
         rec(5)
 
+    def step_fused(self):
+        """The same layer through tg_gated_select (gate -> top-K -> gather in one call)."""
+        tg.tg_gated_select(self.x, self.w1, None, self.w2, self.b2, self.cu, self.db, self.de, self.kd, self.ck,
+                           self.m, self.max_seq, scores=self.scores, kept_idx=self.kept, x_kept=self.xk,
+                           scores_kept=self.sk, pos_kept=self.pk, workspace=self.ws_topk)
+        tg.tg_attn_prepare(self.k, self.v, self.sk, self.pk, self.ck, rope_base=self.w.rope_base,
+                           workspace=self.ws)
+        tg.tg_attn_forward(self.q, self.gain, self.tau, self.ck, self.max_kept, self.w.n_kv_heads, self.ws,
+                           rope_base=self.w.rope_base, out=self.out, lse=self.lse)
+
+    def measure_graph(self, steps):
+        """The layer captured once into a HIP graph (the front half through
+        tg_gated_select), then `steps` replays back to back between two
+        synchronisations: one host launch per layer."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step_fused()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.step_fused()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        del graph
+        return {"ms_per_gated_layer": round(ms, 4), "launches_per_layer": 1,
+                "calls": "tg_gated_select + tg_attn_prepare + tg_attn_forward, captured into one HIP graph"}
+
     def measure(self, steps, warmup):
         """Headline: `steps` back-to-back layers bracketed by synchronisations, no
         events between stages.  Breakdown: a second pass with an event between
@@ -364,6 +399,7 @@ def main():
     af = layer.attn_work()
     attn_s = r["stage_ms"][Layer.STAGES.index("attn_fwd")] * 1e-3
     achieved = af / attn_s / 1e12
+    graph = layer.measure_graph(args.steps)
     decode = measure_decode(layer)
     grads = measure_gate_grads(layer)
     del layer
@@ -406,6 +442,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": pmc_traffic()},
         "gated_layer_128k": head,
+        "graph_128k": graph,
         "decode_128k": decode,
         "gate_grads_128k": grads,
         "full_prefill_128k": full,

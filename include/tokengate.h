@@ -182,6 +182,33 @@ int tg_gather_kept(const void* x, int32_t x_dtype, int32_t d_model, int64_t x_ro
                    int32_t n_seqs, const int32_t* cu_seqlens, const int32_t* cu_kept,
                    void* x_kept, float* scores_kept, int32_t* pos_kept, void* stream);
 
+/*
+ * The front half of the gated layer in one call: tg_gate_score, then
+ * tg_topk_select on those scores, then tg_gather_kept (spke.com article,
+ * gate-module and pruned-forward phases), launched back to back on `stream`
+ * after all three argument sets are validated (nothing is launched if any
+ * check fails).  The call does no host synchronisation, no allocation and no
+ * memset, so a caller can capture it (and the attention after it) into one
+ * HIP graph and replay the whole layer as a single launch.
+ *   x, x_dtype, n_tokens_total, d_model, x_row_stride, w1, b1, w2, b2, d_hid:
+ *                 as for tg_gate_score
+ *   n_seqs, max_seqlen, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept:
+ *                 as for tg_topk_select
+ *   n_kept_total  cu_kept[S] (host value, as for tg_gather_kept)
+ *   scores        [device, out] n_tokens_total fp32
+ *   kept_idx      [device, out] n_kept_total int32
+ *   x_kept, scores_kept, pos_kept   [device, out] as for tg_gather_kept
+ *   workspace     [device] >= tg_topk_workspace_bytes(...) bytes, 256-B aligned
+ * Requirements and errors: those of the three calls.
+ */
+int tg_gated_select(const void* x, int32_t x_dtype, int64_t n_tokens_total, int32_t d_model,
+                    int64_t x_row_stride, const void* w1, const float* b1, const float* w2, float b2,
+                    int32_t d_hid, int32_t n_seqs, int32_t max_seqlen, const int32_t* cu_seqlens,
+                    const int32_t* doc_begin, const int32_t* doc_end, const int32_t* k_doc,
+                    const int32_t* cu_kept, int64_t n_kept_total, float* scores, int32_t* kept_idx,
+                    void* x_kept, float* scores_kept, int32_t* pos_kept, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /* Workspace bytes tg_keybias_attn_prefill (and tg_attn_prepare / tg_attn_forward)
  * need for these sizes. */
 size_t tg_attn_workspace_bytes(int32_t n_seqs, int64_t n_kept_total, int32_t n_kv_heads,

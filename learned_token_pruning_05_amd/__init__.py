@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     tg_attn_prepare,
     tg_attn_workspace_bytes,
     tg_gate_score,
+    tg_gated_select,
     tg_gather_kept,
     tg_kept_counts,
     tg_keybias_attn_prefill,

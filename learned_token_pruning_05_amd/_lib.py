@@ -32,6 +32,8 @@ SIGNATURES = {
     "tg_topk_workspace_bytes": (_SZ, [_I32, _I64, _I32]),
     "tg_topk_select": (ctypes.c_int, [_P, _I32, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tg_gather_kept": (ctypes.c_int, [_P, _I32, _I32, _I64, _P, _P, _I64, _I32, _P, _P, _P, _P, _P, _P]),
+    "tg_gated_select": (ctypes.c_int, [_P, _I32, _I64, _I32, _I64, _P, _P, _P, _F, _I32, _I32, _I32, _P, _P, _P, _P,
+                                       _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tg_attn_workspace_bytes": (_SZ, [_I32, _I64, _I32, _I32]),
     "tg_keybias_attn_prefill": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P, _F, _P, _P, _I32, _I64,
                                                _I32, _I32, _I32, _I32, _D, _P, _P, _P, _SZ, _P]),
@@ -185,6 +187,37 @@ def tg_gather_kept(x, scores, kept_idx, cu_seqlens, cu_kept, x_kept=None, scores
                                _ptr(scores_kept), _ptr(pos_kept), _stream(x))
     _check("tg_gather_kept", st)
     return x_kept, scores_kept, pos_kept
+
+
+def tg_gated_select(x, w1, b1, w2, b2: float, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, n_kept_total: int,
+                    max_seqlen: int, scores=None, kept_idx=None, x_kept=None, scores_kept=None, pos_kept=None,
+                    workspace=None):
+    """gate -> top-K -> gather in one call.  Returns (scores, kept_idx, x_kept, scores_kept, pos_kept)."""
+    n, d_model, stride = _rows(x)
+    d_hid = w1.shape[0]
+    n_seqs = cu_seqlens.shape[0] - 1
+    m = int(n_kept_total)
+    dev = x.device
+    if scores is None:
+        scores = torch.empty(n, dtype=torch.float32, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty(m, dtype=torch.int32, device=dev)
+    if x_kept is None:
+        x_kept = torch.empty((m, d_model), dtype=x.dtype, device=dev)
+    if scores_kept is None:
+        scores_kept = torch.empty(m, dtype=torch.float32, device=dev)
+    if pos_kept is None:
+        pos_kept = torch.empty(m, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(1, tg_topk_workspace_bytes(n_seqs, n, max_seqlen)), dtype=torch.uint8,
+                                device=dev)
+    st = load().tg_gated_select(_ptr(x), _dtype_code(x), n, d_model, stride, _ptr(w1), _ptr(b1), _ptr(w2),
+                                float(b2), d_hid, n_seqs, int(max_seqlen), _ptr(cu_seqlens), _ptr(doc_begin),
+                                _ptr(doc_end), _ptr(k_doc), _ptr(cu_kept), m, _ptr(scores), _ptr(kept_idx),
+                                _ptr(x_kept), _ptr(scores_kept), _ptr(pos_kept), _ptr(workspace),
+                                workspace.numel(), _stream(x))
+    _check("tg_gated_select", st)
+    return scores, kept_idx, x_kept, scores_kept, pos_kept
 
 
 def tg_attn_workspace_bytes(n_seqs, n_kept_total, n_kv_heads, head_dim) -> int:

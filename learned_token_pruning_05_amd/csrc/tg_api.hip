@@ -9,6 +9,65 @@ namespace {
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Checks of the front-half calls: TG_OK (launch), -1 (valid, nothing to do) or
+// the error status.  No HIP call.
+int gate_check(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d_model, int64_t x_row_stride,
+               const void* w1, const float* w2, float b2, int32_t d_hid, const float* scores) {
+    if (n_tokens < 0 || d_model <= 0 || d_hid <= 0 || !isfinite(b2)) return TG_ERR_INVALID_ARG;
+    if (x_dtype != TG_F32 && x_dtype != TG_BF16) return TG_ERR_INVALID_ARG;
+    if (d_model % 8 != 0 || x_row_stride < d_model || x_row_stride % 8 != 0) return TG_ERR_INVALID_ARG;
+    if (n_tokens == 0) return -1;
+    if (!x || !w1 || !w2 || !scores || !aligned16(x) || !aligned16(w1)) return TG_ERR_INVALID_ARG;
+    if (x_dtype == TG_BF16) {
+        if (d_model % 64 != 0) return TG_ERR_UNSUPPORTED;
+        if (d_hid != 64 && d_hid != 128 && d_hid != 192 && d_hid != 256) return TG_ERR_UNSUPPORTED;
+        if (x_row_stride >= (1 << 23)) return TG_ERR_UNSUPPORTED;   // per-workgroup offsets are 32-bit
+    } else if (d_hid > 1024 || d_model > 2048) {
+        return TG_ERR_UNSUPPORTED;
+    }
+    return TG_OK;
+}
+
+int gate_launch(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d_model, int64_t x_row_stride,
+                const void* w1, const float* b1, const float* w2, float b2, int32_t d_hid, float* scores,
+                void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    if (x_dtype == TG_BF16)
+        return launch_gate_bf16((const bf16*)x, n_tokens, d_model, x_row_stride, (const bf16*)w1, b1, w2, b2,
+                                d_hid, scores, st);
+    return launch_gate_f32((const float*)x, n_tokens, d_model, x_row_stride, (const float*)w1, b1, w2, b2, d_hid,
+                           scores, st);
+}
+
+int topk_check(const float* scores, int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen,
+               const int32_t* cu_seqlens, const int32_t* doc_begin, const int32_t* doc_end, const int32_t* k_doc,
+               const int32_t* cu_kept, const int32_t* kept_idx, const void* workspace, size_t workspace_bytes) {
+    if (n_seqs < 0 || n_tokens_total < 0 || n_tokens_total > INT32_MAX || max_seqlen < 0 ||
+        max_seqlen > n_tokens_total)
+        return TG_ERR_INVALID_ARG;
+    if (max_seqlen > topk_max_seqlen()) return TG_ERR_UNSUPPORTED;
+    if (n_seqs == 0 || n_tokens_total == 0) return -1;
+    if (!cu_seqlens || !doc_begin || !doc_end || !k_doc || !cu_kept || !kept_idx || !scores)
+        return TG_ERR_INVALID_ARG;
+    const size_t need = topk_workspace_bytes(n_seqs, n_tokens_total, max_seqlen);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return TG_ERR_WORKSPACE;
+    return TG_OK;
+}
+
+int gather_check(const void* x, int32_t x_dtype, int32_t d_model, int64_t x_row_stride, const float* scores,
+                 const int32_t* kept_idx, int64_t n_kept_total, int32_t n_seqs, const int32_t* cu_seqlens,
+                 const int32_t* cu_kept, const void* x_kept, const float* scores_kept, const int32_t* pos_kept) {
+
+    if (n_kept_total < 0 || n_seqs < 0 || d_model <= 0) return TG_ERR_INVALID_ARG;
+    if (x_dtype != TG_F32 && x_dtype != TG_BF16) return TG_ERR_INVALID_ARG;
+    if (d_model % 8 != 0 || x_row_stride < d_model || x_row_stride % 8 != 0) return TG_ERR_INVALID_ARG;
+    if (n_kept_total == 0) return -1;
+    if (!x || !kept_idx || !x_kept || !aligned16(x) || !aligned16(x_kept)) return TG_ERR_INVALID_ARG;
+    if (scores_kept && !scores) return TG_ERR_INVALID_ARG;
+    if (pos_kept && (n_seqs < 1 || !cu_seqlens || !cu_kept)) return TG_ERR_INVALID_ARG;
+    return TG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -64,22 +123,10 @@ int tg_random_budgets(uint64_t seed, int32_t n_seqs, const int32_t* doc_begin_h,
 int tg_gate_score(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d_model,
                   int64_t x_row_stride, const void* w1, const float* b1, const float* w2,
                   float b2, int32_t d_hid, float* scores, void* stream) {
-    if (n_tokens < 0 || d_model <= 0 || d_hid <= 0 || !isfinite(b2)) return TG_ERR_INVALID_ARG;
-    if (x_dtype != TG_F32 && x_dtype != TG_BF16) return TG_ERR_INVALID_ARG;
-    if (d_model % 8 != 0 || x_row_stride < d_model || x_row_stride % 8 != 0) return TG_ERR_INVALID_ARG;
-    if (n_tokens == 0) return TG_OK;
-    if (!x || !w1 || !w2 || !scores || !aligned16(x) || !aligned16(w1)) return TG_ERR_INVALID_ARG;
-    hipStream_t st = (hipStream_t)stream;
-    if (x_dtype == TG_BF16) {
-        if (d_model % 64 != 0) return TG_ERR_UNSUPPORTED;
-        if (d_hid != 64 && d_hid != 128 && d_hid != 192 && d_hid != 256) return TG_ERR_UNSUPPORTED;
-        if (x_row_stride >= (1 << 23)) return TG_ERR_UNSUPPORTED;   // per-workgroup offsets are 32-bit
-        return launch_gate_bf16((const bf16*)x, n_tokens, d_model, x_row_stride, (const bf16*)w1, b1,
-                                w2, b2, d_hid, scores, st);
-    }
-    if (d_hid > 1024 || d_model > 2048) return TG_ERR_UNSUPPORTED;
-    return launch_gate_f32((const float*)x, n_tokens, d_model, x_row_stride, (const float*)w1, b1, w2,
-                           b2, d_hid, scores, st);
+    const int st = gate_check(x, x_dtype, n_tokens, d_model, x_row_stride, w1, w2, b2, d_hid, scores);
+    if (st == -1) return TG_OK;
+    if (st != TG_OK) return st;
+    return gate_launch(x, x_dtype, n_tokens, d_model, x_row_stride, w1, b1, w2, b2, d_hid, scores, stream);
 }
 
 size_t tg_topk_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen) {
@@ -91,16 +138,10 @@ int tg_topk_select(const float* scores, int32_t n_seqs, int64_t n_tokens_total, 
                    const int32_t* cu_seqlens, const int32_t* doc_begin, const int32_t* doc_end,
                    const int32_t* k_doc, const int32_t* cu_kept, int32_t* kept_idx,
                    void* workspace, size_t workspace_bytes, void* stream) {
-    if (n_seqs < 0 || n_tokens_total < 0 || n_tokens_total > INT32_MAX || max_seqlen < 0 ||
-        max_seqlen > n_tokens_total)
-        return TG_ERR_INVALID_ARG;
-    if (max_seqlen > topk_max_seqlen()) return TG_ERR_UNSUPPORTED;
-    if (n_seqs == 0 || n_tokens_total == 0) return TG_OK;
-    if (!cu_seqlens || !doc_begin || !doc_end || !k_doc || !cu_kept || !kept_idx || !scores)
-        return TG_ERR_INVALID_ARG;
-    const size_t need = topk_workspace_bytes(n_seqs, n_tokens_total, max_seqlen);
-    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
-        return TG_ERR_WORKSPACE;
+    const int st = topk_check(scores, n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end, k_doc,
+                              cu_kept, kept_idx, workspace, workspace_bytes);
+    if (st == -1) return TG_OK;
+    if (st != TG_OK) return st;
     return launch_topk(scores, n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end,
                        k_doc, cu_kept, kept_idx, workspace, (hipStream_t)stream);
 }
@@ -130,16 +171,47 @@ int tg_gather_kept(const void* x, int32_t x_dtype, int32_t d_model, int64_t x_ro
                    const float* scores, const int32_t* kept_idx, int64_t n_kept_total,
                    int32_t n_seqs, const int32_t* cu_seqlens, const int32_t* cu_kept,
                    void* x_kept, float* scores_kept, int32_t* pos_kept, void* stream) {
-    if (n_kept_total < 0 || n_seqs < 0 || d_model <= 0) return TG_ERR_INVALID_ARG;
-    if (x_dtype != TG_F32 && x_dtype != TG_BF16) return TG_ERR_INVALID_ARG;
-    if (d_model % 8 != 0 || x_row_stride < d_model || x_row_stride % 8 != 0) return TG_ERR_INVALID_ARG;
-    if (n_kept_total == 0) return TG_OK;
-    if (!x || !kept_idx || !x_kept || !aligned16(x) || !aligned16(x_kept)) return TG_ERR_INVALID_ARG;
-    if (scores_kept && !scores) return TG_ERR_INVALID_ARG;
-    if (pos_kept && (n_seqs < 1 || !cu_seqlens || !cu_kept)) return TG_ERR_INVALID_ARG;
+    const int st = gather_check(x, x_dtype, d_model, x_row_stride, scores, kept_idx, n_kept_total, n_seqs,
+                                cu_seqlens, cu_kept, x_kept, scores_kept, pos_kept);
+    if (st == -1) return TG_OK;
+    if (st != TG_OK) return st;
     const int esize = x_dtype == TG_BF16 ? 2 : 4;
     return launch_gather(x, esize, d_model, x_row_stride, scores, kept_idx, n_kept_total, n_seqs,
                          cu_seqlens, cu_kept, x_kept, scores_kept, pos_kept, (hipStream_t)stream);
+}
+
+int tg_gated_select(const void* x, int32_t x_dtype, int64_t n_tokens_total, int32_t d_model,
+                    int64_t x_row_stride, const void* w1, const float* b1, const float* w2, float b2,
+                    int32_t d_hid, int32_t n_seqs, int32_t max_seqlen, const int32_t* cu_seqlens,
+                    const int32_t* doc_begin, const int32_t* doc_end, const int32_t* k_doc,
+                    const int32_t* cu_kept, int64_t n_kept_total, float* scores, int32_t* kept_idx,
+                    void* x_kept, float* scores_kept, int32_t* pos_kept, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    // every stage is validated before the first launch
+    const int sg = gate_check(x, x_dtype, n_tokens_total, d_model, x_row_stride, w1, w2, b2, d_hid, scores);
+    if (sg != TG_OK && sg != -1) return sg;
+    const int stk = topk_check(scores, n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end,
+                               k_doc, cu_kept, kept_idx, workspace, workspace_bytes);
+    if (stk != TG_OK && stk != -1) return stk;
+    const int sga = gather_check(x, x_dtype, d_model, x_row_stride, scores, kept_idx, n_kept_total, n_seqs,
+                                 cu_seqlens, cu_kept, x_kept, scores_kept, pos_kept);
+    if (sga != TG_OK && sga != -1) return sga;
+    if (sg == TG_OK) {
+        const int st = gate_launch(x, x_dtype, n_tokens_total, d_model, x_row_stride, w1, b1, w2, b2, d_hid,
+                                   scores, stream);
+        if (st != TG_OK) return st;
+    }
+    if (stk == TG_OK) {
+        const int st = launch_topk(scores, n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end,
+                                   k_doc, cu_kept, kept_idx, workspace, (hipStream_t)stream);
+        if (st != TG_OK) return st;
+    }
+    if (sga == TG_OK) {
+        const int esize = x_dtype == TG_BF16 ? 2 : 4;
+        return launch_gather(x, esize, d_model, x_row_stride, scores, kept_idx, n_kept_total, n_seqs, cu_seqlens,
+                             cu_kept, x_kept, scores_kept, pos_kept, (hipStream_t)stream);
+    }
+    return TG_OK;
 }
 
 size_t tg_attn_workspace_bytes(int32_t n_seqs, int64_t n_kept_total, int32_t n_kv_heads,

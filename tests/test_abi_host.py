@@ -290,3 +290,25 @@ def test_random_budgets_host_bit_exact(lib):
     assert lib.tg_random_budgets(1, 1, p(bad), p(good), p(out)) == 1   # end before begin
     assert lib.tg_random_budgets(1, 1, p(good), p(bad), None) == 1
     assert lib.tg_random_budgets(1, 0, None, None, None) == 0
+
+
+def test_gated_select_validation(lib):
+    """The fused front-half call validates all three stages before launching: an
+    error in any stage's arguments returns that stage's status."""
+    L = lib
+    need = L.tg_topk_workspace_bytes(1, 4096, 4096)
+    a = lambda **kw: L.tg_gated_select(*[kw.get(k, v) for k, v in [
+        ("x", FAKE), ("dt", 1), ("n", 4096), ("d", 2048), ("xs", 2048), ("w1", FAKE), ("b1", None), ("w2", FAKE),
+        ("b2", 0.0), ("dh", 256), ("ns", 1), ("mx", 4096), ("cu", FAKE), ("db", FAKE), ("de", FAKE), ("kd", FAKE),
+        ("ck", FAKE), ("m", 1000), ("sc", FAKE), ("ki", FAKE), ("xk", FAKE), ("sk", FAKE), ("pk", FAKE),
+        ("ws", FAKE), ("wsb", need), ("st", None)]])
+    assert a(d=100) == 1                  # gate: d_model not a multiple of 8
+    assert a(dh=100) == 2                 # gate: unsupported hidden width
+    assert a(b2=float("nan")) == 1
+    assert a(mx=4097) == 1                # top-K: longer than the total
+    assert a(kd=None) == 1
+    assert a(wsb=need - 1) == 3           # top-K workspace
+    assert a(xk=None) == 1                # gather output
+    assert a(xk=ctypes.c_void_p(0x1008)) == 1
+    assert a(m=-1) == 1
+    assert a(n=0, mx=0, m=0) == 0         # nothing to do, nothing launched

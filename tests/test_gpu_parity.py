@@ -621,6 +621,89 @@ def test_gate_grads_no_tokens_and_determinism():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
 
 
+# -------------------------------------------------- front half in one call ----
+@pytest.mark.parametrize("name", ["tiny", "16k", "varlen"])
+def test_gated_select_matches_separate_calls(name):
+    """tg_gated_select (gate -> top-K -> gather in one call) gives the same bits as
+    the three calls made one by one."""
+    _print_case(f"gated select {name}")
+    w = workloads.by_name(name)
+    g = _gate_inputs(name)
+    x, w1, w2 = _dev(g["x"]), _dev(g["w1"]), _dev(g["w2"])
+    ck = tg.tg_kept_counts(w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+    m, mx = int(ck[-1]), int(max(w.seqlens))
+    meta = [_i32(a) for a in (w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr, ck)]
+    s1 = tg.tg_gate_score(x, w1, None, w2, g["b2"])
+    k1 = tg.tg_topk_select(s1, *meta, m, mx)
+    xk1, sk1, pk1 = tg.tg_gather_kept(x, s1, k1, meta[0], meta[4])
+    s2, k2, xk2, sk2, pk2 = tg.tg_gated_select(x, w1, None, w2, g["b2"], *meta, m, mx)
+    torch.cuda.synchronize()
+    for a, b in ((s1, s2), (k1, k2), (xk1, xk2), (sk1, sk2), (pk1, pk2)):
+        assert torch.equal(a, b)
+
+
+def test_gated_layer_graph_replay():
+    """The whole gated layer (tg_gated_select, tg_attn_prepare, tg_attn_forward)
+    captured into one HIP graph and replayed: before each of four replays a
+    different input is copied into the captured buffers, eager work and a
+    synchronisation run between replays, and every replay's outputs equal an
+    eager run on the same input (bit for bit)."""
+    _print_case("gated layer graph replay 16k")
+    w = workloads.by_name("16k")
+    g = _gate_inputs("16k")
+    dev = torch.device("cuda:0")
+    x = _dev(g["x"])
+    w1, w2 = _dev(g["w1"]), _dev(g["w2"])
+    ck = tg.tg_kept_counts(w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+    m, mx, mk = int(ck[-1]), int(max(w.seqlens)), int(np.diff(ck).max())
+    meta = [_i32(a) for a in (w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr, ck)]
+    q, k, v = (t.to(dev) for t in w.qkv(m))
+    gain, tau = w.attn_params()
+    gain = torch.from_numpy(gain).to(dev)
+    n = w.n_tokens
+
+    def buffers():
+        return dict(scores=torch.empty(n, device=dev), kept=torch.empty(m, dtype=torch.int32, device=dev),
+                    xk=torch.empty(m, w.d_model, dtype=x.dtype, device=dev), sk=torch.empty(m, device=dev),
+                    pk=torch.empty(m, dtype=torch.int32, device=dev),
+                    ws_t=torch.empty(tg.tg_topk_workspace_bytes(w.n_seqs, n, mx), dtype=torch.uint8, device=dev),
+                    ws_a=torch.empty(tg.tg_attn_workspace_bytes(w.n_seqs, m, w.n_kv_heads, w.head_dim),
+                                     dtype=torch.uint8, device=dev),
+                    out=torch.empty(m, w.n_q_heads, w.head_dim, dtype=torch.bfloat16, device=dev),
+                    lse=torch.empty(w.n_q_heads, m, device=dev))
+
+    def layer(xin, b):
+        tg.tg_gated_select(xin, w1, None, w2, g["b2"], *meta, m, mx, scores=b["scores"], kept_idx=b["kept"],
+                           x_kept=b["xk"], scores_kept=b["sk"], pos_kept=b["pk"], workspace=b["ws_t"])
+        tg.tg_attn_prepare(k, v, b["sk"], b["pk"], meta[4], rope_base=w.rope_base, workspace=b["ws_a"])
+        tg.tg_attn_forward(q, gain, tau, meta[4], mk, w.n_kv_heads, b["ws_a"], rope_base=w.rope_base,
+                           out=b["out"], lse=b["lse"])
+
+    static_x = x.clone()
+    gb = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer(static_x, gb)          # first calls set kernel attributes outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer(static_x, gb)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    for rep in range(4):
+        xr = x if rep == 0 else (x.float() + 0.5 * torch.randn(x.shape, generator=gen).to(dev)).to(x.dtype)
+        static_x.copy_(xr)
+        graph.replay()
+        torch.cuda.synchronize()
+        eb = buffers()
+        layer(xr, eb)                # eager run between replays, on fresh buffers
+        torch.cuda.synchronize()
+        for key in ("scores", "kept", "xk", "sk", "pk", "out", "lse"):
+            assert torch.equal(gb[key], eb[key]), f"replay {rep}: {key} differs from the eager run"
+
+
 # --------------------------------------------------------------- end to end ----
 @pytest.mark.parametrize("name", ["tiny", "16k"])
 def test_gated_layer_end_to_end(name):
