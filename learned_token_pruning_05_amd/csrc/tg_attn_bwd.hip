@@ -68,7 +68,7 @@ struct BwdLds {
 };
 
 // ---------------------------------------------------------------- prep ----
-// One workgroup per (64 padded rows, q head).  Four threads per row copy dO
+// One workgroup per (q head, 64 padded rows).  Four threads per row copy dO
 // into dO' while computing Delta = <dO, O>, and LSE2 = LSE log2(e); then the
 // Q' items (row, rotate-half chunk pair), lanes over chunk pairs, with the
 // (cos, sin) table of the key pre-pass, and the extra columns.
@@ -82,8 +82,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     __shared__ int tok[64];
     __shared__ float rowc[2][64];   // Delta, LSE2
     const int tid = threadIdx.x;
-    const int h = blockIdx.y;
-    const int64_t p0 = (int64_t)blockIdx.x * 64;
+    // head fastest: the heads of a row block run side by side and share the
+    // (cos, sin) rows and the O / dO row segments through the caches
+    const int h = blockIdx.x;
+    const int64_t p0 = (int64_t)blockIdx.y * 64;
     if (tid < 64) {
         const int64_t r = p0 + tid;
         int lo = 0, hi = n_seqs;
@@ -486,7 +488,7 @@ int launch_bwd_d(const BwdArgs& a, hipStream_t st) {
     const int n_kt = (a.max_kept_seqlen + kBwdKeys - 1) / kBwdKeys;
     const int64_t nblk = (int64_t)n_kt * a.n_seqs * a.hq;
     if (nblk > 0x7fffffff) return TG_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)(a.mp / 64), a.hq), dim3(256), 0, st, a.q, a.q_stride,
+    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(a.hq, (unsigned)(a.mp / 64)), dim3(256), 0, st, a.q, a.q_stride,
                        a.o, a.dout, a.do_stride, a.lse, a.gain, a.qk_scale_log2, a.ws_cs, (int)a.rope, a.cu_kept,
                        a.n_seqs, a.m_tot, a.hq, a.mp, qc, oc);
     static bool attr_set = false;
