@@ -125,17 +125,16 @@ size_t decode_part_o_bytes(int n_seqs, int max_kept_seqlen, int hq, int d);
 size_t decode_workspace_bytes(int n_seqs, int max_kept_seqlen, int hq, int d);
 int launch_attn_decode(const DecodeArgs& a, hipStream_t st);
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane l writes LDS bytes [ldst + 16 l, ldst + 16 l + 16); ldst must be the
-// same for the whole wave.
 // Buffer resource over `bytes` bytes from `base` (raw, untyped 32-bit
-// elements): reads beyond it return zero instead of faulting.
+// elements): reads at per-lane offsets beyond it return zero instead of
+// faulting.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// 16 B per lane from rsrc at byte offset voff + soff (soff wave-uniform) into
-// LDS at ldst + 16 * lane (ldst wave-uniform).
+// Direct global -> LDS copy (buffer_load_dwordx4 ... lds): 16 B per lane from
+// rsrc at byte offset voff + soff (soff wave-uniform) into LDS bytes
+// [ldst + 16 lane, ldst + 16 lane + 16) (ldst wave-uniform).
 __device__ __forceinline__ void lds_load16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* ldst) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)ldst, 16, (int)voff,
                                               (int)soff, 0, 0);
@@ -162,10 +161,6 @@ __device__ __forceinline__ void wait_vm_le(int n) {
         case 12: __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); break;
         default: __builtin_amdgcn_s_waitcnt(0); break;
     }
-}
-
-__device__ __forceinline__ void lds_load16(const void* gsrc, void* ldst) {
-    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)ldst, 16, 0, 0);
 }
 
 // Upper-bound search: the sequence s with cu[s] <= m < cu[s+1] (cu non-decreasing,
