@@ -161,8 +161,27 @@ class Layer:
             self.step(evs[i])
         torch.cuda.synchronize()
         st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(n)] for e in evs])   # ms
-        return dict(wall_ms=wall, gpu_ms=gpu, stage_ms=st.mean(axis=0), stage_p10=np.percentile(st, 10, axis=0),
-                    stage_p90=np.percentile(st, 90, axis=0))
+        return dict(wall_ms=wall, gpu_ms=gpu, stage_ms=st.mean(axis=0), stage_med=np.median(st, axis=0),
+                    stage_p10=np.percentile(st, 10, axis=0), stage_p90=np.percentile(st, 90, axis=0))
+
+    def measure_cold(self, steps):
+        """Per-stage times with cold caches: before every layer (outside the
+        events) a 512 MiB buffer is written, which evicts the 256 MB Infinity
+        Cache and the L2s, so the gate, top-K and gather read their inputs
+        from HBM.  Median and p10/p90 per stage."""
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=self.x.device)
+        n = len(self.STAGES)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+        for i in range(steps):
+            scratch.fill_(i & 255)
+            self.step(evs[i])
+        torch.cuda.synchronize()
+        del scratch
+        st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(n)] for e in evs]) * 1e3   # us
+        return {"stage_us_median": {k: round(float(v), 2) for k, v in zip(self.STAGES, np.median(st, axis=0))},
+                "stage_us_p10_p90": {k: [round(float(a), 1), round(float(b), 1)] for k, a, b in
+                                     zip(self.STAGES, np.percentile(st, 10, axis=0), np.percentile(st, 90, axis=0))},
+                "steps": steps}
 
     # algorithmic work per launch
     def gate_work(self):
@@ -333,10 +352,61 @@ def cpu_baseline(w: workloads.Workload):
     oracle.keybias_attention(q, k, v, sk, gain, tau, pk, ck, rope_base=w.rope_base)
     attn_ms = (time.perf_counter() - t) * 1e3
     total = gate_ms + topk_ms + gather_ms + attn_ms
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(total, 3), "unit": "ms/gated layer", "cores": int(threads), "kind": "oracle",
+            "cpu_model": model, "os_cpu_count": os.cpu_count(),
             "sample": f"{w.name}: the whole gated layer ({n} tokens, {m} kept, all heads), no extrapolation; "
                       f"per stage ms: gate {gate_ms:.0f}, topk {topk_ms:.0f}, gather {gather_ms:.0f}, "
                       f"attn {attn_ms:.0f}"}
+
+
+def machine_context():
+    """Context for the peaks: a plain device copy's GB/s and a plain bf16 GEMM's
+    TFLOP/s (vendor library) on this GPU, and the clocks rocm-smi reports."""
+    dev = torch.device("cuda:0")
+    x = torch.ones(256 << 20, dtype=torch.bfloat16, device=dev)   # 512 MiB
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * x.numel() * 2 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    del x, y
+    n = 8192
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2.0 * n ** 3 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    clocks = None
+    try:
+        import subprocess
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
+        clocks = [ln.strip() for ln in out.splitlines() if "sclk" in ln.lower() or "mclk" in ln.lower()] or None
+    except Exception:
+        clocks = None
+    return {"copy_gbs": round(copy_gbs, 1), "copy_frac_hbm": round(copy_gbs / PEAK_HBM_GBS, 4),
+            "bf16_gemm_8192_tflops": round(gemm_tflops, 1),
+            "bf16_gemm_frac_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+            "rocm_smi_clocks_idle": clocks}
 
 
 def summarize(layer: Layer, r):
@@ -349,6 +419,7 @@ def summarize(layer: Layer, r):
         "ms_per_gated_layer": round(r["wall_ms"], 4),
         "gpu_ms_per_gated_layer": round(r["gpu_ms"], 4),
         "stage_us": {k: round(v * 1e6, 2) for k, v in stage_s.items()},
+        "stage_us_median": {k: round(float(v) * 1e3, 2) for k, v in zip(Layer.STAGES, r["stage_med"])},
         "stage_us_p10_p90": {k: [round(a * 1e3, 1), round(b * 1e3, 1)]
                              for k, a, b in zip(Layer.STAGES, r["stage_p10"], r["stage_p90"])},
         "attn_fwd_tflops": round(af / stage_s["attn_fwd"] / 1e12, 2),
@@ -396,6 +467,7 @@ def main():
     af = layer.attn_work()
     attn_s = r["stage_ms"][Layer.STAGES.index("attn_fwd")] * 1e-3
     achieved = af / attn_s / 1e12
+    cold = layer.measure_cold(args.steps)
     graph = layer.measure_graph(args.steps)
     decode = measure_decode(layer)
     grads = measure_gate_grads(layer)
@@ -410,9 +482,11 @@ def main():
             ls = Layer(ws)
             rs = ls.measure(max(5, args.steps // 2), 2)
             sweep[ws.name] = summarize(ls, rs)
+            sweep[ws.name]["cold_cache_stage_us_median"] = ls.measure_cold(max(5, args.steps // 2))["stage_us_median"]
             del ls
             torch.cuda.empty_cache()
 
+    context = machine_context()
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(w)
@@ -439,11 +513,13 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": pmc_traffic()},
         "gated_layer_128k": head,
+        "cold_cache_128k": cold,
         "graph_128k": graph,
         "decode_128k": decode,
         "gate_grads_128k": grads,
         "full_prefill_128k": full,
         "sweep_32k": sweep,
+        "machine_context": context,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
