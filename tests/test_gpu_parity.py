@@ -551,10 +551,11 @@ def _check_grads(c, d_out, rope_base, got):
     assert abs(g_t - dtau) <= GRAD_TOL_G * mt + 1e-6
 
 
-@pytest.mark.parametrize("name", ["tiny", "16k", "128k"])
+@pytest.mark.parametrize("name", ["tiny", "16k", "128k", "varlen"])
 def test_gate_grads_configs(name):
     """Every d_score, d_gain and d_tau of the workload against the oracle (128k:
-    8448 kept tokens, 16 q heads, the bench's launch)."""
+    8448 kept tokens, 16 q heads, the bench's launch; varlen: 8 packed
+    sequences)."""
     _print_case(f"gate grads {name}")
     w = workloads.by_name(name)
     c = _attn_case(w)
