@@ -367,7 +367,7 @@ def cpu_baseline(w: workloads.Workload):
 
 def machine_context():
     """Context for the peaks: a plain device copy's GB/s and a plain bf16 GEMM's
-    TFLOP/s (vendor library) on this GPU, and the clocks rocm-smi reports."""
+    TFLOP/s (vendor library) on this GPU, and the driver's current clock levels."""
     dev = torch.device("cuda:0")
     x = torch.ones(256 << 20, dtype=torch.bfloat16, device=dev)   # 512 MiB
     y = torch.empty_like(x)
@@ -396,17 +396,27 @@ def machine_context():
     gemm_tflops = 2.0 * n ** 3 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
     del a, b
     torch.cuda.empty_cache()
-    clocks = None
-    try:
-        import subprocess
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
-        clocks = [ln.strip() for ln in out.splitlines() if "sclk" in ln.lower() or "mclk" in ln.lower()] or None
-    except Exception:
-        clocks = None
     return {"copy_gbs": round(copy_gbs, 1), "copy_frac_hbm": round(copy_gbs / PEAK_HBM_GBS, 4),
             "bf16_gemm_8192_tflops": round(gemm_tflops, 1),
             "bf16_gemm_frac_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-            "rocm_smi_clocks_idle": clocks}
+            "dpm_clock_levels": dpm_clock_levels()}
+
+
+def dpm_clock_levels():
+    """The current shader and memory clock levels the amdgpu driver lists in sysfs
+    for this device (the entry marked '*'), read from files rather than through a
+    child process, so that a profiler's preload never reaches another program."""
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        d = f"/sys/bus/pci/devices/{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
+        out = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            with open(os.path.join(d, name)) as f:
+                cur = [ln.strip() for ln in f if ln.strip().endswith("*")]
+            out[name[-4:]] = cur[0] if cur else None
+        return out
+    except Exception:
+        return None
 
 
 def summarize(layer: Layer, r):
