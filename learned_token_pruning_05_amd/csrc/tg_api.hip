@@ -367,6 +367,7 @@ int tg_attn_decode(const void* q, int64_t q_row_stride, const int32_t* q_pos, co
     if (q_row_stride < (int64_t)n_q_heads * head_dim) return TG_ERR_INVALID_ARG;
     if (max_kept_seqlen < 0 || max_kept_seqlen > n_kept_total || (n_kept_total > 0 && max_kept_seqlen < 1))
         return TG_ERR_INVALID_ARG;
+    if (n_seqs == 0 && n_kept_total > 0) return TG_ERR_INVALID_ARG;   // kept keys but no sequence
     if (n_seqs == 0) return TG_OK;
     if (!q || !q_pos || !head_gain || !cu_kept || !out || (n_kept_total > 0 && !pos)) return TG_ERR_INVALID_ARG;
     const size_t cache_need = attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, nullptr,
@@ -436,6 +437,7 @@ int tg_attn_gate_grads(const void* q, int64_t q_row_stride, const void* v, int64
     if (max_kept_seqlen < 0 || max_kept_seqlen > n_kept_total || (n_kept_total > 0 && max_kept_seqlen < 1))
         return TG_ERR_INVALID_ARG;
     if (!d_gain || !d_tau) return TG_ERR_INVALID_ARG;
+    if (n_seqs == 0 && n_kept_total > 0) return TG_ERR_INVALID_ARG;   // kept tokens but no sequence
     if (n_seqs == 0 || n_kept_total == 0) {
         // no causal pair: every gradient is zero
         return launch_gate_grads_zero(n_q_heads, d_gain, d_tau, (hipStream_t)stream);

@@ -209,7 +209,8 @@ def test_attn_decode_validation(lib):
     assert a(cache=ctypes.c_void_p(0x1010)) == 3
     assert a(wsb=need - 1) == 3
     assert a(ws=ctypes.c_void_p(0x1010)) == 3
-    assert a(ns=0) == 0                # nothing to do, nothing launched
+    assert a(ns=0) == 1                # kept keys but no sequence
+    assert a(ns=0, m=0, mx=0) == 0     # nothing to do, nothing launched
 
 
 def test_attn_gate_grads_validation(lib):
@@ -244,6 +245,7 @@ def test_attn_gate_grads_validation(lib):
     assert a(wsb=need - 1) == 3
     assert a(ws=ctypes.c_void_p(0x1010)) == 3
     assert a(m=0, mx=0, dg=None) == 1  # the zero gradients still need somewhere to go
+    assert a(ns=0) == 1                # kept tokens but no sequence
 
 
 def test_random_k_validation(lib):
