@@ -49,8 +49,10 @@ struct DecLds {
     static constexpr int V_INSTR = D * VROW / 64;
     static constexpr int KT = kDecKeys * KROW * 8;          // tile sizes in elements
     static constexpr int VT = D * VROW * 8;
+    // ring slots: one when a workgroup streams a single tile, else two
+    __host__ __device__ static int slots(int nsub) { return nsub > 1 ? 2 : 1; }
     static size_t smem(int grp, int nsub) {
-        return (size_t)(2 * KT + 2 * VT) * 2 + (size_t)grp * D * 4 + (size_t)grp * kDecKeys * 4 +
+        return (size_t)(slots(nsub) * KT + slots(nsub) * VT) * 2 + (size_t)grp * D * 4 + (size_t)grp * kDecKeys * 4 +
                (size_t)nsub * kDecKeys * 4 + (size_t)4 * grp * 4;
     }
     static_assert(kDecKeys * KROW % 64 == 0 && D * VROW % 64 == 0, "tiles must be whole load instructions");
@@ -70,8 +72,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void attn_decode_split_kernel(
     // dynamic LDS, sized for this launch's grp and nsub (two workgroups fit a CU)
     extern __shared__ __attribute__((aligned(16))) char dsm[];
     bf16* const ks = (bf16*)dsm;                       // [2][KT] K' ring
-    bf16* const vs = ks + 2 * KT;                      // [2][VT] V^T ring
-    float* const qs = (float*)(vs + 2 * VT);           // [grp][D] rotated, scaled queries
+    bf16* const vs = ks + L::slots(nsub) * KT;         // [slots][VT] V^T ring
+    float* const qs = (float*)(vs + L::slots(nsub) * VT);   // [grp][D] rotated, scaled queries
     float* const ts = qs + grp * D;                    // [grp][64] logits, then probabilities
     int* const pk = (int*)(ts + grp * kDecKeys);       // [nsub][64] key positions
     float* const gs = (float*)(pk + nsub * kDecKeys);  // [grp] g log2 e
@@ -235,18 +237,20 @@ __global__ __launch_bounds__(kDecThreads, 2) void attn_decode_split_kernel(
     }
 }
 
-// One workgroup per (sequence, q head) merges the partials of the sequence's
-// chunks: the chunk maxima reduce to one m, then batches of 256 chunk weights
-// 2^(m_c - m) go to LDS and 256 / D lanes per channel sum the weighted
-// partial outputs of interleaved chunks (independent loads, all in flight),
-// reduced through LDS at the end.  No visible key: O = 0, LSE = -inf.
-template <int D>
-__global__ __launch_bounds__(kDecThreads) void attn_decode_combine_kernel(
+// One workgroup of NT threads per (sequence, q head) merges the partials of
+// the sequence's chunks: the chunk maxima reduce to one m, then batches of NT
+// chunk weights 2^(m_c - m) go to LDS and NT / D lanes per channel sum the
+// weighted partial outputs of interleaved chunks (eight independent loads in
+// flight per lane), reduced through LDS at the end.  Many chunks per sequence
+// take NT = 1024, so fewer round trips per lane.  No visible key: O = 0,
+// LSE = -inf.
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void attn_decode_combine_kernel(
     const int* __restrict__ cu_kept, int hq, int chunk_keys, int n_chunks, const float* __restrict__ part_o,
     const float2* __restrict__ part_ml, bf16* __restrict__ out, float* __restrict__ lse) {
-    constexpr int SUB = kDecThreads / D;   // lanes per channel
-    __shared__ float wsh[kDecThreads];
-    __shared__ float red[kDecThreads];
+    constexpr int SUB = NT / D;   // lanes per channel
+    __shared__ float wsh[NT];
+    __shared__ float red[NT];
     const int s = blockIdx.x / hq, h = blockIdx.x % hq, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int ms = cu_kept[s + 1] - cu_kept[s];
@@ -264,17 +268,17 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_combine_kernel(
         __syncthreads();
         float r = red[0];
 #pragma unroll
-        for (int i = 1; i < kDecWaves; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+        for (int i = 1; i < NT / 64; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
         __syncthreads();
         return r;
     };
 
     float m = -INFINITY;
-    for (int c = tid; c < nc; c += kDecThreads) m = fmaxf(m, ml[(int64_t)c * hq].x);
+    for (int c = tid; c < nc; c += NT) m = fmaxf(m, ml[(int64_t)c * hq].x);
     m = block_reduce(m, true);
     float l = 0.0f, o = 0.0f;
     const int d = tid % D, sub = tid / D;
-    for (int c0 = 0; c0 < nc; c0 += kDecThreads) {
+    for (int c0 = 0; c0 < nc; c0 += NT) {
         const int c = c0 + tid;
         float wc = 0.0f;
         if (c < nc && m != -INFINITY) {
@@ -286,8 +290,8 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_combine_kernel(
         }
         wsh[tid] = wc;
         __syncthreads();
-        const int nb = min(kDecThreads, nc - c0);
-#pragma unroll 4
+        const int nb = min(NT, nc - c0);
+#pragma unroll 8
         for (int j = sub; j < nb; j += SUB) o += wsh[j] * po[((int64_t)(c0 + j) * hq) * D + d];
         __syncthreads();
     }
@@ -308,10 +312,12 @@ template <int D>
 int launch_decode_d(const DecodeArgs& a, hipStream_t st) {
     using L = DecLds<D>;
     const int grp = a.hq / a.hkv;
-    // 64-key tiles per split workgroup: enough workgroups for two per CU
-    // (256 CUs), then longer streams per workgroup
+    // 64-key tiles per split workgroup.  Up to 1536 (tile, kv head, sequence)
+    // jobs each workgroup takes one tile through a one-slot ring (~38 KB of LDS,
+    // four workgroups per CU, every tile's loads in flight at once); more jobs
+    // give 2-4 tiles per workgroup through a two-slot ring, two per CU.
     const int64_t jobs = (int64_t)decode_chunks(a.max_kept_seqlen) * a.hkv * a.n_seqs;
-    const int nsub = (int)std::min<int64_t>(kDecMaxSub, std::max<int64_t>(1, (jobs + 511) / 512));
+    const int nsub = jobs <= 1536 ? 1 : (int)std::min<int64_t>(kDecMaxSub, (jobs + 511) / 512);
     const int chunk_keys = nsub * kDecKeys;
     const int n_chunks = a.max_kept_seqlen > 0 ? (a.max_kept_seqlen + chunk_keys - 1) / chunk_keys : 1;
     float* part_o = (float*)a.ws;
@@ -333,9 +339,14 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t st) {
                            a.qk_scale_log2, a.pos, a.cu_kept, a.hq, grp, a.mp, a.ws_k, a.ws_vt, fr, (int)a.rope,
                            nsub, n_chunks, part_o, part_ml);
     }
-    hipLaunchKernelGGL(attn_decode_combine_kernel<D>, dim3((unsigned)(a.n_seqs * a.hq)), dim3(kDecThreads), 0, st,
-                       a.cu_kept, a.hq, chunk_keys, n_chunks, (const float*)part_o, (const float2*)part_ml, a.out,
-                       a.lse);
+    if (n_chunks >= 128)
+        hipLaunchKernelGGL((attn_decode_combine_kernel<D, 1024>), dim3((unsigned)(a.n_seqs * a.hq)), dim3(1024), 0,
+                           st, a.cu_kept, a.hq, chunk_keys, n_chunks, (const float*)part_o,
+                           (const float2*)part_ml, a.out, a.lse);
+    else
+        hipLaunchKernelGGL((attn_decode_combine_kernel<D, kDecThreads>), dim3((unsigned)(a.n_seqs * a.hq)),
+                           dim3(kDecThreads), 0, st, a.cu_kept, a.hq, chunk_keys, n_chunks,
+                           (const float*)part_o, (const float2*)part_ml, a.out, a.lse);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 
