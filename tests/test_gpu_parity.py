@@ -485,6 +485,19 @@ def test_decode_shapes_ragged(d, hq, hkv, rope):
     _check_decode(c, q_new, q_pos, rope, out, lse)
 
 
+def test_decode_many_partials_ragged():
+    """Sequences long enough for 128+ one-tile partials each (the wide merge), with
+    an empty and a one-key sequence in the same batch."""
+    lens = [0, 1, 8200, 9000]
+    w = workloads.custom([n + 8 for n in lens], [8 if n else 0 for n in lens], [max(n - 8, 0) for n in lens],
+                         n_q_heads=8, n_kv_heads=2, head_dim=128, seed=77, tau=0.87)
+    _print_case("decode many partials")
+    c = _attn_case(w)
+    q_new, q_pos = _new_queries(c, 29, offset=3)
+    out, lse = _run_decode(c, q_new, q_pos, 1e6)
+    _check_decode(c, q_new, q_pos, 1e6, out, lse)
+
+
 def test_decode_position_mask_and_empty():
     """A query inside a sequence sees only the keys at or before its position; one
     before every key gets O = 0, LSE = -inf; decode at a kept token's own
