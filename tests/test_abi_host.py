@@ -105,6 +105,7 @@ def test_topk_validation(lib):
     assert t(s=None) == 1
     assert t(mx=11) == 1                         # longer than the whole batch
     assert t(n=2 ** 23, mx=2 ** 23) == 2          # beyond the 4 Mi grid limit
+    assert t(n=2 ** 22 + 1, mx=2 ** 22 + 1) == 2  # one token past it
     need = L.tg_topk_workspace_bytes(1, 10, 10)
     assert need > 0
     assert t(ws=None, wsb=need) == 3

@@ -168,6 +168,20 @@ def test_topk_edge_values_and_budgets(k_frac):
         np.testing.assert_array_equal(got, want, err_msg=tag)
 
 
+def test_topk_max_seqlen_bit_exact():
+    """One sequence of exactly the longest supported length (4 Mi tokens: every
+    per-chunk table of the select kernel full), scores on a coarse grid so that
+    ties cross the threshold, a 10% budget and a 256-token question."""
+    n = 1 << 22
+    r = np.random.default_rng(11)
+    s = (np.round(r.standard_normal(n) * 64) / 64).astype(np.float32)
+    nd = n - 256
+    _print_case(f"topk max seqlen n={n}")
+    got, _ = _topk_gpu(s, [0, n], [0], [nd], [nd // 10])
+    want, _ = oracle.topk_select(s, [0, n], [0], [nd], [nd // 10])
+    np.testing.assert_array_equal(got, want)
+
+
 def test_topk_ragged_varlen_and_spans():
     r = np.random.default_rng(7)
     lens = [1, 0, 2, 63, 64, 65, 4095, 4096, 4097, 9000, 1, 17]
