@@ -42,7 +42,7 @@ extern "C" {
 enum {
     TG_OK = 0,
     TG_ERR_INVALID_ARG = 1,  /* bad scalar, NULL required pointer, misaligned pointer */
-    TG_ERR_UNSUPPORTED = 2,  /* a shape or dtype this build has no kernel for */
+    TG_ERR_UNSUPPORTED = 2,  /* a shape or dtype the library has no kernel for */
     TG_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
     TG_ERR_HIP = 4           /* a HIP launch failed */
 };
