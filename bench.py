@@ -326,7 +326,7 @@ def pmc_traffic():
 
 def cpu_baseline(w: workloads.Workload):
     """The fp64 oracle, as it stands, over one whole gated layer of the same
-    workload (about 10 s on the machine's host threads, so no extrapolation)."""
+    workload (about 10 s on the host's CPU threads, so no extrapolation)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -367,7 +367,7 @@ def cpu_baseline(w: workloads.Workload):
 
 def machine_context():
     """Context for the peaks: a plain device copy's GB/s and a plain bf16 GEMM's
-    TFLOP/s (vendor library) on this GPU, and the driver's current clock levels."""
+    TFLOP/s (vendor library) on this GPU, and the amdgpu kernel driver's current clock levels."""
     dev = torch.device("cuda:0")
     x = torch.ones(256 << 20, dtype=torch.bfloat16, device=dev)   # 512 MiB
     y = torch.empty_like(x)
