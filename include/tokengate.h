@@ -27,7 +27,9 @@
  *    TG_ERR_HIP.  Device-resident metadata (cu_seqlens, spans, budgets,
  *    cu_kept, positions) is trusted: inconsistent values are undefined
  *    behaviour.
- *  - Calls are reentrant and thread-safe; the library has no global state.
+ *  - Calls are reentrant and thread-safe.  The only global state is, per
+ *    kernel, an atomic mask of the devices on which its dynamic LDS limit has
+ *    been raised (once per device, at that kernel's first call there).
  */
 #ifndef TOKENGATE_H
 #define TOKENGATE_H

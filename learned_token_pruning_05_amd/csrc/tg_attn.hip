@@ -608,13 +608,8 @@ int launch_fwd(const AttnArgs& a, hipStream_t st) {
     // buffer offsets into one head's K' rows ((D+16)*2 B each) stay 32-bit
     if (nblk > 0x7fffffff || (int64_t)(D + kExtra) * 2 * a.mp >= ((int64_t)1 << 32)) return TG_ERR_UNSUPPORTED;
     const size_t shm = (size_t)AttnLds<D>::SMEM;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void*)attn_fwd_kernel<D, HW, NW>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) != hipSuccess)
-            return TG_ERR_HIP;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (const int e = set_dyn_lds_once((const void*)attn_fwd_kernel<D, HW, NW>, (int)shm, lds_set)) return e;
     hipLaunchKernelGGL((attn_fwd_kernel<D, HW, NW>), dim3((unsigned)nblk), dim3(NW * 64), shm, st, a.q,
                        a.q_stride, a.ws_k, a.ws_vt, a.ws_cs, (int)a.rope, a.gain, a.qk_scale_log2,
                        a.cu_kept, a.n_seqs, a.m_tot, a.mp, a.hq, grp, n_qtiles, n_hblk, a.out, a.lse);

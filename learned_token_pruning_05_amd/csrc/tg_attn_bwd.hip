@@ -488,16 +488,11 @@ int launch_bwd_d(const BwdArgs& a, hipStream_t st) {
     const int n_kt = (a.max_kept_seqlen + kBwdKeys - 1) / kBwdKeys;
     const int64_t nblk = (int64_t)n_kt * a.n_seqs * a.hq;
     if (nblk > 0x7fffffff) return TG_ERR_UNSUPPORTED;
+    static std::atomic<uint64_t> lds_set{0};   // before the first launch of the call
+    if (const int e = set_dyn_lds_once((const void*)bwd_main_kernel<D>, (int)L::SMEM, lds_set)) return e;
     hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(a.hq, (unsigned)(a.mp / 64)), dim3(256), 0, st, a.q, a.q_stride,
                        a.o, a.dout, a.do_stride, a.lse, a.gain, a.qk_scale_log2, a.ws_cs, (int)a.rope, a.cu_kept,
                        a.n_seqs, a.m_tot, a.hq, a.mp, qc, oc);
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void*)bwd_main_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)L::SMEM) != hipSuccess)
-            return TG_ERR_HIP;
-        attr_set = true;
-    }
     hipLaunchKernelGGL(bwd_main_kernel<D>, dim3((unsigned)nblk), dim3(kBwdThreads), L::SMEM, st, (const bf16*)qc,
                        (const bf16*)oc, a.ws_k, a.v, a.kv_stride, a.key_score, a.cu_kept, a.n_seqs, a.m_tot, a.hq,
                        grp, a.mp, n_kt, colsum, part);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "tokengate.h"
 
 namespace tg {
@@ -124,6 +126,20 @@ int decode_chunks(int max_kept_seqlen);
 size_t decode_part_o_bytes(int n_seqs, int max_kept_seqlen, int hq, int d);
 size_t decode_workspace_bytes(int n_seqs, int max_kept_seqlen, int hq, int d);
 int launch_attn_decode(const DecodeArgs& a, hipStream_t st);
+
+// Raises `fn`'s dynamic LDS limit to `bytes` on the current device, once per
+// device: `done` records the devices already set (devices past 63 are set on
+// every call).  Concurrent first calls may both set the same value, which is
+// harmless; the mask itself is atomic.
+inline int set_dyn_lds_once(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TG_ERR_HIP;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return TG_OK;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess) return TG_ERR_HIP;
+    if (bit) done.fetch_or(bit, std::memory_order_release);
+    return TG_OK;
+}
 
 // Buffer resource over `bytes` bytes from `base` (raw, untyped 32-bit
 // elements): reads at per-lane offsets beyond it return zero instead of

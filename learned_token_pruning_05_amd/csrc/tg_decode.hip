@@ -327,13 +327,8 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t st) {
         fr.rev[f] = a.rope && f < D / 2 ? exp2(-(2.0 * f / D) * a.rope_log2_base) / 6.283185307179586 : 0.0;
     if (a.m_tot > 0) {
         const size_t shm = L::smem(kDecMaxGrp, kDecMaxSub);   // the attribute covers every launch
-        static bool attr_set = false;
-        if (!attr_set) {
-            if (hipFuncSetAttribute((const void*)attn_decode_split_kernel<D>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) != hipSuccess)
-                return TG_ERR_HIP;
-            attr_set = true;
-        }
+        static std::atomic<uint64_t> lds_set{0};
+        if (const int e = set_dyn_lds_once((const void*)attn_decode_split_kernel<D>, (int)shm, lds_set)) return e;
         hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3((unsigned)n_chunks, a.hkv, a.n_seqs),
                            dim3(kDecThreads), L::smem(grp, nsub), st, a.q, a.q_stride, a.q_pos, a.gain,
                            a.qk_scale_log2, a.pos, a.cu_kept, a.hq, grp, a.mp, a.ws_k, a.ws_vt, fr, (int)a.rope,

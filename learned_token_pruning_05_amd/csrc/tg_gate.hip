@@ -254,13 +254,8 @@ int launch_gate_tile(const bf16* x, int64_t n, int d_model, int64_t x_stride, co
     constexpr size_t slab = (size_t)(BM + NH) * kLdk * 2;
     constexpr size_t red = (size_t)BM * 65 * 4;
     constexpr size_t shm = kStages * slab > red ? kStages * slab : red;
-    static bool attr_set = false;   // idempotent; racing first calls set the same value
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void*)gate_bf16_kernel<CB, BM>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) != hipSuccess)
-            return TG_ERR_HIP;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (const int e = set_dyn_lds_once((const void*)gate_bf16_kernel<CB, BM>, (int)shm, lds_set)) return e;
     const dim3 grid((unsigned)((n + BM - 1) / BM));
     hipLaunchKernelGGL((gate_bf16_kernel<CB, BM>), grid, dim3(BM * 2), shm, st, x, n, d_model, x_stride, w1,
                        b1, w2, b2, scores);
