@@ -363,6 +363,26 @@ def test_attention_bias_shift_invariance_gpu():
     np.testing.assert_allclose(l2 - l1, (c["gain"] * 0.75)[:, None] * np.ones_like(l1), atol=4e-3)
 
 
+def test_attention_offset_rescale_path():
+    """The forward's running offset comes from the first key tile.  With the first
+    64 kept keys' scores at -90 and the next 64 at -45, every later row's logits
+    jump past that offset by 45 g log2(e), which exceeds the 2^62 row-sum limit
+    for the heads with g > 0.96 (five of eight here, two jumps per row), so those
+    rows take the rescale path twice; all rows are checked against the oracle."""
+    w = workloads.custom([1400], [100], [1300], n_q_heads=8, n_kv_heads=2, head_dim=128, seed=17, tau=0.9)
+    _print_case("attn offset rescale")
+    c = _attn_case(w)
+    sk = c["sk"].copy()
+    sk[:64] = -90.0
+    sk[64:128] = -45.0
+    c = dict(c, sk=sk.astype(np.float32))
+    out, lse = _run_attn(c, 1e6)
+    _check_attn(c, out, lse, 1e6, np.arange(int(c["ck"][-1])))
+    # the gradients recompute P from that forward's LSE (down to -176 here)
+    d_out = w.d_out(int(c["ck"][-1]))
+    _check_grads(c, d_out, 1e6, _run_grads(c, d_out, 1e6))
+
+
 def test_attention_prepare_forward_split():
     """tg_attn_prepare + tg_attn_forward give exactly the one-shot result, and one
     prepared kept-only cache serves a second query set."""
