@@ -299,15 +299,15 @@ def _run_attn(c, rope_base, q=None, k=None, v=None):
     return out.float().cpu().numpy(), lse.cpu().numpy()
 
 
-def _check_attn(c, out, lse, rope_base, rows):
+def _check_attn(c, out, lse, rope_base, rows, tol=ATTN_TOL):
     f = lambda t: t.float().numpy()
     ref_o, ref_l = oracle.keybias_attention(f(c["q"]), f(c["k"]), f(c["v"]), c["sk"], c["gain"], c["tau"],
                                             c["pk"], c["ck"], rope_base=rope_base, rows=rows)
     assert np.isfinite(out).all()
     eo = np.abs(out[rows] - ref_o[rows]).max()
     el = np.abs(lse[:, rows] - ref_l[:, rows]).max()
-    print(f"   max|dO|={eo:.3g} max|dLSE|={el:.3g} rows={len(rows)}", flush=True)
-    assert eo <= ATTN_TOL and el <= ATTN_TOL
+    print(f"   max|dO|={eo:.3g} max|dLSE|={el:.3g} rows={len(rows)} (bar {tol:.3g})", flush=True)
+    assert eo <= tol and el <= tol
 
 
 ATTN_CASES = ["tiny", "16k", "32k@5%", "32k@10%", "32k@25%", "32k@50%", "32k@100%", "128k", "varlen"]
@@ -381,6 +381,27 @@ def test_attention_offset_rescale_path():
     # the gradients recompute P from that forward's LSE (down to -176 here)
     d_out = w.d_out(int(c["ck"][-1]))
     _check_grads(c, d_out, 1e6, _run_grads(c, d_out, 1e6))
+
+
+@pytest.mark.parametrize("tau", [0.3, 4.0])
+def test_attention_temperature_extremes(tau):
+    """A sharp (tau = 0.3) and a flat (tau = 4) temperature: the forward on every
+    row and the gate gradients, d_tau included, against the oracle.
+
+    The kernels round the rotated, scaled q and k to bf16 (2^-9 relative each),
+    so a logit's error is proportional to the logit scale 1 / (sqrt(D) tau), and
+    in a sharp softmax it moves the output by about dP (v_top - v_next).  The
+    bars therefore scale as 1 / tau below the configs' tau range (0.8 - 0.9):
+    factor max(1, 0.9 / tau), 3x at tau = 0.3."""
+    w = workloads.custom([700, 500], [40, 20], [400, 250], n_q_heads=8, n_kv_heads=4, head_dim=128, seed=23,
+                         tau=tau)
+    _print_case(f"attn tau={tau}")
+    c = _attn_case(w)
+    k = max(1.0, 0.9 / tau)
+    out, lse = _run_attn(c, 1e6)
+    _check_attn(c, out, lse, 1e6, np.arange(int(c["ck"][-1])), tol=ATTN_TOL * k)
+    d_out = w.d_out(int(c["ck"][-1]))
+    _check_grads(c, d_out, 1e6, _run_grads(c, d_out, 1e6), scale=k)
 
 
 def test_attention_prepare_forward_split():
@@ -581,7 +602,7 @@ def _run_grads(c, d_out, rope_base, q=None, v=None, d_out_dev=None):
     return dsc.cpu().numpy(), dg.cpu().numpy(), float(dt.cpu()[0])
 
 
-def _check_grads(c, d_out, rope_base, got):
+def _check_grads(c, d_out, rope_base, got, scale=1.0):
     f = lambda t: t.float().numpy()
     ds, dg, dtau, (ms, mg, mt) = oracle.keybias_attention_gate_grads(
         f(c["q"]), f(c["k"]), f(c["v"]), c["sk"], c["gain"], c["tau"], c["pk"], c["ck"], f(d_out),
@@ -593,9 +614,9 @@ def _check_grads(c, d_out, rope_base, got):
     et = abs(g_t - dtau) / max(mt, 1e-30)
     print(f"   err/scale: d_score {es.max() if es.size else 0:.3g}  d_gain {eg.max():.3g}  d_tau {et:.3g}"
           f"   (|d_tau| = {abs(dtau):.4g})", flush=True)
-    assert np.all(np.abs(g_s - ds) <= GRAD_TOL_S * ms + 1e-6)
-    assert np.all(np.abs(g_g - dg) <= GRAD_TOL_G * mg + 1e-6)
-    assert abs(g_t - dtau) <= GRAD_TOL_G * mt + 1e-6
+    assert np.all(np.abs(g_s - ds) <= scale * GRAD_TOL_S * ms + 1e-6)
+    assert np.all(np.abs(g_g - dg) <= scale * GRAD_TOL_G * mg + 1e-6)
+    assert abs(g_t - dtau) <= scale * GRAD_TOL_G * mt + 1e-6
 
 
 @pytest.mark.parametrize("name", ["tiny", "16k", "128k", "varlen"])
