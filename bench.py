@@ -263,6 +263,31 @@ def measure_gate_grads(layer: Layer, steps=10, warmup=3):
             "kernels": "bwd_prep_kernel + bwd_main_kernel + bwd_reduce_kernel (tg_attn_gate_grads)"}
 
 
+def measure_random_k(layer: Layer, steps=50, warmup=5):
+    """The random-K selector mode (tg_random_k_select: SplitMix64 scores for every
+    token, then the top-K passes) on the layer's sequence layout, a new seed per
+    call.  Bytes as the top-K's: the scores written and read, the kept indices."""
+    w = layer.w
+    dev = layer.x.device
+    n = w.n_tokens
+    kept = torch.empty(layer.m, dtype=torch.int32, device=dev)
+    wsr = torch.empty(tg.tg_random_k_workspace_bytes(w.n_seqs, n, layer.max_seq), dtype=torch.uint8, device=dev)
+    f = lambda seed: tg.tg_random_k_select(seed, layer.cu, layer.db, layer.de, layer.kd, layer.ck, n, layer.m,
+                                           layer.max_seq, kept_idx=kept, workspace=wsr)
+    for i in range(warmup):
+        f(1000 + i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        f(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    return {"us_per_call": round(us, 2), "tokens": n, "kept": layer.m,
+            "kernels": "random_scores_kernel + the five top-K kernels (tg_random_k_select)"}
+
+
 def measure_full_prefill(w: workloads.Workload, pruned_layer_ms: float, reps=3):
     """The same attention at K = n_doc (every token kept, no gate/select/gather):
     tg_attn_prepare + tg_attn_forward over all N tokens, beside the pruned layer,
@@ -481,6 +506,7 @@ def main():
     graph = layer.measure_graph(args.steps)
     decode = measure_decode(layer)
     grads = measure_gate_grads(layer)
+    random_k = measure_random_k(layer)
     del layer
     torch.cuda.empty_cache()
     full = measure_full_prefill(w, r["wall_ms"])
@@ -527,6 +553,7 @@ def main():
         "graph_128k": graph,
         "decode_128k": decode,
         "gate_grads_128k": grads,
+        "random_k_128k": random_k,
         "full_prefill_128k": full,
         "sweep_32k": sweep,
         "machine_context": context,

@@ -153,6 +153,10 @@ def tg_topk_select(scores, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, n_kep
     return kept_idx
 
 
+def tg_random_k_workspace_bytes(n_seqs, n_tokens_total, max_seqlen) -> int:
+    return load().tg_random_k_workspace_bytes(n_seqs, n_tokens_total, max_seqlen)
+
+
 def tg_random_k_select(seed: int, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, n_tokens: int, n_kept_total: int,
                        max_seqlen: int, kept_idx=None, workspace=None):
     """Random-K selector mode: as tg_topk_select over seeded SplitMix64 scores."""
@@ -162,7 +166,7 @@ def tg_random_k_select(seed: int, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept
         kept_idx = torch.empty(n_kept_total, dtype=torch.int32, device=dev)
     lib = load()
     if workspace is None:
-        need = lib.tg_random_k_workspace_bytes(n_seqs, n_tokens, max_seqlen)
+        need = tg_random_k_workspace_bytes(n_seqs, n_tokens, max_seqlen)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     st = lib.tg_random_k_select(int(seed) % (1 << 64), n_seqs, n_tokens, max_seqlen, _ptr(cu_seqlens),
                                 _ptr(doc_begin), _ptr(doc_end), _ptr(k_doc), _ptr(cu_kept), _ptr(kept_idx),

@@ -326,10 +326,21 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
         const uint32_t bmask = pass == 0 ? 2047u : 1023u;
         for (int i = tid; i < kBins; i += kSelThreads) h[i] = 0u;
         __syncthreads();
-        for (uint32_t i0 = 0; i0 < nc; i0 += kSelThreads) {
-            const uint32_t i = i0 + tid;
-            const uint32_t key = i < nc ? get(i).x : 0u;
-            hist_add(h, (key >> shift) & bmask, i < nc && (key & pmask) == prefix);
+        // eight candidates per thread per round, their loads issued together
+        // (from the workspace they are global reads)
+        constexpr int U = 8;
+        for (uint32_t i0 = 0; i0 < nc; i0 += kSelThreads * U) {
+            uint32_t key[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = i0 + u * kSelThreads + tid;
+                key[u] = i < nc ? get(i).x : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = i0 + u * kSelThreads + tid;
+                hist_add(h, (key[u] >> shift) & bmask, i < nc && (key[u] & pmask) == prefix);
+            }
         }
         __syncthreads();
         uint32_t bk, ab;
@@ -347,11 +358,20 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
         const uint32_t o = coff[c], n_c = coff[c + 1] - o;
         const uint2* src = cg + (int64_t)c * kWriteChunk;
         uint32_t na = 0, nb = 0;
-        for (uint32_t i0 = 0; i0 < n_c; i0 += 64) {
-            const uint32_t i = i0 + lane;
-            const uint32_t key = i < n_c ? (in_lds ? cand[o + i].x : src[i].x) : 0u;
-            na += (uint32_t)__popcll(__ballot(i < n_c && key > T));
-            nb += (uint32_t)__popcll(__ballot(i < n_c && key == T));
+        constexpr int V = 4;   // four slices of 64 per round, loads together
+        for (uint32_t i0 = 0; i0 < n_c; i0 += 64 * V) {
+            uint32_t key[V];
+#pragma unroll
+            for (int u = 0; u < V; ++u) {
+                const uint32_t i = i0 + u * 64 + lane;
+                key[u] = i < n_c ? (in_lds ? cand[o + i].x : src[i].x) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < V; ++u) {
+                const uint32_t i = i0 + u * 64 + lane;
+                na += (uint32_t)__popcll(__ballot(i < n_c && key[u] > T));
+                nb += (uint32_t)__popcll(__ballot(i < n_c && key[u] == T));
+            }
         }
         if (lane == 0) {
             ca[c] += na;
