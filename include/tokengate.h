@@ -154,9 +154,10 @@ size_t tg_random_k_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32
  * "Техническая реализация").  Same budget, same always-kept question and same
  * output as tg_topk_select, but the K_eff document tokens of each sequence
  * are a seeded uniform random subset: tg_topk_select applied to the scores
- * r_t = top 24 bits of SplitMix64 output t for `seed`, times 2^-24, where t
- * is the global token index (SplitMix64: Steele, Lea and Flood, OOPSLA 2014;
- * output t = finalizer of seed + (t+1) * 0x9E3779B97F4A7C15).  Equal draws
+ * r_t = the positive normal fp32 with bit pattern 2^23 + d_t, where d_t is the
+ * top 30 bits of SplitMix64 output t for `seed` and t the global token index
+ * (SplitMix64: Steele, Lea and Flood, OOPSLA 2014; output t = finalizer of
+ * seed + (t+1) * 0x9E3779B97F4A7C15).  r_t orders exactly like d_t; equal draws
  * keep the lower index.  Arguments, requirements and errors as for
  * tg_topk_select, without `scores`; workspace >= tg_random_k_workspace_bytes.
  */

@@ -512,7 +512,9 @@ TopkLayout topk_layout(int n_seqs, int64_t n_tokens, int max_seqlen) {
 // Random-K selector mode: uniform scores in [0, 1) from SplitMix64 (Steele,
 // Lea and Flood 2014): output t of the generator seeded with `seed` is the
 // finalizer of seed + (t+1) * 0x9E3779B97F4A7C15, so each token's draw is
-// independent of the others; the top 24 bits times 2^-24 are exact in fp32.
+// independent of the others.  The score is the top 30 bits d of the draw as the
+// positive normal fp32 with bit pattern 2^23 + d: it orders exactly like d, and
+// d's top bits spread the scores over the selector's radix buckets.
 __global__ __launch_bounds__(256) void random_scores_kernel(uint64_t seed, int64_t n, float* __restrict__ out) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= n) return;
@@ -520,7 +522,7 @@ __global__ __launch_bounds__(256) void random_scores_kernel(uint64_t seed, int64
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
     z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
     z ^= z >> 31;
-    out[t] = (float)(uint32_t)(z >> 40) * 0x1p-24f;
+    out[t] = __uint_as_float((uint32_t)(z >> 34) + 0x00800000u);
 }
 
 }  // namespace

@@ -184,9 +184,13 @@ def splitmix64(seed: int, n: int) -> np.ndarray:
 
 
 def random_scores(seed: int, n: int) -> np.ndarray:
-    """Uniform random scores in [0, 1) for n tokens: the top 24 bits of
-    SplitMix64 output t (t = global token index), times 2^-24 (exact in fp32)."""
-    return ((splitmix64(seed, n) >> np.uint64(40)).astype(np.float64) * 2.0 ** -24).astype(np.float32)
+    """Random scores for n tokens, one independent uniform 30-bit draw each: the
+    top 30 bits d_t of SplitMix64 output t (t = global token index), encoded as
+    the positive normal fp32 whose bit pattern is 2^23 + d_t.  Positive floats
+    order like their bit patterns, so the scores order exactly like the draws;
+    only that order matters to the selector."""
+    d = (splitmix64(seed, n) >> np.uint64(34)).astype(np.uint32)
+    return (d + np.uint32(1 << 23)).view(np.float32)
 
 
 def random_budgets(seed, doc_begin, doc_end):
@@ -219,7 +223,7 @@ def random_k_select(seed, cu_seqlens, doc_begin, doc_end, k_doc):
     Reading: the same budget and the same always-kept question as the learned
     selector, but the K_eff document tokens of each sequence are a seeded
     uniform random subset: the selector of topk_select applied to
-    random_scores(seed, N_tot) instead of the gate's scores (24-bit scores, so
+    random_scores(seed, N_tot) instead of the gate's scores (30-bit draws, so
     equal draws are possible and keep the lower index, as for gate scores).
     Returns (kept_idx, cu_kept) as topk_select does.
     """

@@ -417,12 +417,18 @@ def test_splitmix64_reference_outputs():
         assert int(oracle.splitmix64((12345 + i * g) % 2 ** 64, 1)[0]) == int(a[i])
 
 
-def test_random_scores_exact_24_bit_grid():
-    s = oracle.random_scores(7, 1000)
-    assert s.dtype == np.float32 and np.all((s >= 0) & (s < 1))
-    np.testing.assert_array_equal(s.astype(np.float64) * 2 ** 24, np.floor(s.astype(np.float64) * 2 ** 24))
-    raw = oracle.splitmix64(7, 1000)
-    np.testing.assert_array_equal((s.astype(np.float64) * 2 ** 24).astype(np.uint64), raw >> np.uint64(40))
+def test_random_scores_encode_30_bit_draws_in_order():
+    """Each score is a positive normal float whose bit pattern is 2^23 plus the
+    top 30 bits of the pinned SplitMix64 output, so the scores sort exactly
+    like those draws (checked on values, not on the encoding)."""
+    s = oracle.random_scores(7, 5000)
+    raw = oracle.splitmix64(7, 5000) >> np.uint64(34)
+    assert s.dtype == np.float32 and np.all(np.isfinite(s))
+    assert np.all(s >= np.float32(2.0 ** -126)) and np.all(s < np.float32(4.0))
+    np.testing.assert_array_equal(s.view(np.uint32).astype(np.uint64) - (1 << 23), raw)
+    np.testing.assert_array_equal(np.argsort(s.astype(np.float64), kind="stable"), np.argsort(raw, kind="stable"))
+    # the draws' top bits spread over the selector's 2048 top-11-bit buckets
+    assert len(np.unique(s.view(np.uint32) >> 21)) > 400
 
 
 def test_random_k_budget_question_and_determinism():
