@@ -404,6 +404,28 @@ def test_attention_temperature_extremes(tau):
     _check_grads(c, d_out, 1e6, _run_grads(c, d_out, 1e6), scale=k)
 
 
+def test_many_short_sequences():
+    """300 packed sequences of 0-40 tokens (many empty or one-token ones): the
+    selector bit-exact, then attention on every kept row and one decode query per
+    sequence against the oracle."""
+    r = np.random.default_rng(29)
+    lens = r.integers(0, 41, 300)
+    q = np.minimum(lens, r.integers(0, 9, 300))
+    kd = r.integers(0, 30, 300)
+    w = workloads.custom(list(lens), list(q), list(kd), n_q_heads=8, n_kv_heads=2, head_dim=64, seed=31, tau=0.85)
+    _print_case("many short sequences")
+    s = w.topk_scores()
+    got, _ = _topk_gpu(s, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+    want, _ = oracle.topk_select(s, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+    np.testing.assert_array_equal(got, want)
+    c = _attn_case(w)
+    out, lse = _run_attn(c, 1e6)
+    _check_attn(c, out, lse, 1e6, np.arange(int(c["ck"][-1])))
+    q_new, q_pos = _new_queries(c, 37)
+    o2, l2 = _run_decode(c, q_new, q_pos, 1e6)
+    _check_decode(c, q_new, q_pos, 1e6, o2, l2)
+
+
 def test_attention_prepare_forward_split():
     """tg_attn_prepare + tg_attn_forward give exactly the one-shot result, and one
     prepared kept-only cache serves a second query set."""
