@@ -406,8 +406,8 @@ def test_attention_temperature_extremes(tau):
 
 def test_many_short_sequences():
     """300 packed sequences of 0-40 tokens (many empty or one-token ones): the
-    selector bit-exact, then attention on every kept row and one decode query per
-    sequence against the oracle."""
+    selector bit-exact, then attention on every kept row, one decode query per
+    sequence and the gate gradients against the oracle."""
     r = np.random.default_rng(29)
     lens = r.integers(0, 41, 300)
     q = np.minimum(lens, r.integers(0, 9, 300))
@@ -424,6 +424,8 @@ def test_many_short_sequences():
     q_new, q_pos = _new_queries(c, 37)
     o2, l2 = _run_decode(c, q_new, q_pos, 1e6)
     _check_decode(c, q_new, q_pos, 1e6, o2, l2)
+    d_out = w.d_out(int(c["ck"][-1]))
+    _check_grads(c, d_out, 1e6, _run_grads(c, d_out, 1e6))
 
 
 def test_attention_prepare_forward_split():
