@@ -428,6 +428,28 @@ def test_many_short_sequences():
     _check_grads(c, d_out, 1e6, _run_grads(c, d_out, 1e6))
 
 
+def test_full_prefill_131072_sampled():
+    """The full-prefill comparator that the benchmark times: all 131072 tokens of
+    the 128k workload kept (one sequence, 16 q / 8 kv heads, D = 128), on the
+    benchmark's own inputs (the same generator, seed and draw order), checked
+    on 18 rows that the oracle computes one by one (the first and last rows and
+    three in between)."""
+    w = workloads.long128k()
+    n = w.n_tokens
+    _print_case(f"full prefill n={n}")
+    g = torch.Generator(device="cpu").manual_seed(4)
+    q = torch.randn(n, w.n_q_heads, w.head_dim, generator=g).to(torch.bfloat16)
+    k = torch.randn(n, w.n_kv_heads, w.head_dim, generator=g).to(torch.bfloat16)
+    v = torch.randn(n, w.n_kv_heads, w.head_dim, generator=g).to(torch.bfloat16)
+    sk = torch.randn(n, generator=g)
+    gain, tau = w.attn_params()
+    c = dict(q=q, k=k, v=v, sk=sk.numpy(), pk=np.arange(n, dtype=np.int32), ck=np.array([0, n], dtype=np.int32),
+             gain=gain, tau=tau)
+    out, lse = _run_attn(c, w.rope_base)
+    rows = np.array(list(range(8)) + [70000, 100000, 131071 - 8] + list(range(n - 7, n)))
+    _check_attn(c, out, lse, w.rope_base, rows)
+
+
 def test_attention_prepare_forward_split():
     """tg_attn_prepare + tg_attn_forward give exactly the one-shot result, and one
     prepared kept-only cache serves a second query set."""
