@@ -315,3 +315,15 @@ def test_gated_select_validation(lib):
     assert a(xk=ctypes.c_void_p(0x1008)) == 1
     assert a(m=-1) == 1
     assert a(n=0, mx=0, m=0) == 0         # nothing to do, nothing launched
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and says so,
+    before touching a GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
