@@ -110,6 +110,37 @@ def _i32_host(a):
     return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
 
 
+def _req(t, name, dtype=None, dim=None, numel=None, dense=True, device=None, optional=False):
+    """Check a tensor argument before its pointer reaches a kernel: a torch
+    tensor on a GPU device (the same one as `device` if given), of the given
+    dtype(s) and rank, dense when the kernels read it as one flat array.
+    Raises TypeError / ValueError; a wrong tensor never becomes a bad device
+    address inside a kernel."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if dtype is not None:
+        dts = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in dts:
+            raise TypeError(f"{name} must be {' or '.join(str(d) for d in dts)}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions, got shape {tuple(t.shape)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, not {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other tensors on {device}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    if dense and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_I32T, _F32T, _BF16T, _U8T = torch.int32, torch.float32, torch.bfloat16, torch.uint8
+
+
 # ------------------------------------------------------------------ entries --
 def tg_kept_counts(cu_seqlens, doc_begin, doc_end, k_doc) -> np.ndarray:
     """Host-side kept counts -> cu_kept (int32 numpy, S+1)."""
@@ -121,9 +152,26 @@ def tg_kept_counts(cu_seqlens, doc_begin, doc_end, k_doc) -> np.ndarray:
     return out
 
 
-def tg_gate_score(x, w1, b1, w2, b2: float, scores=None):
+def _check_gate(x, w1, b1, w2, scores):
+    _req(x, "x", (_BF16T, _F32T), dim=2, dense=False)
     n, d_model, stride = _rows(x)
+    _req(w1, "w1", x.dtype, dim=2, device=x.device)
+    if w1.shape[1] != d_model:
+        raise ValueError(f"w1 must be [d_hid, {d_model}], got {tuple(w1.shape)}")
     d_hid = w1.shape[0]
+    _req(b1, "b1", _F32T, dim=1, numel=d_hid, device=x.device, optional=True)
+    _req(w2, "w2", _F32T, dim=1, numel=d_hid, device=x.device)
+    _req(scores, "scores", _F32T, dim=1, numel=n, device=x.device, optional=True)
+    return n, d_model, stride, d_hid
+
+
+def _check_meta(dev, n_seqs, **meta):
+    for name, t in meta.items():
+        _req(t, name, _I32T, dim=1, numel=n_seqs + (1 if name.startswith("cu_") else 0), device=dev)
+
+
+def tg_gate_score(x, w1, b1, w2, b2: float, scores=None):
+    n, d_model, stride, d_hid = _check_gate(x, w1, b1, w2, scores)
     if scores is None:
         scores = torch.empty(n, dtype=torch.float32, device=x.device)
     st = load().tg_gate_score(_ptr(x), _dtype_code(x), n, d_model, stride, _ptr(w1), _ptr(b1), _ptr(w2),
@@ -139,7 +187,12 @@ def tg_topk_workspace_bytes(n_seqs, n_tokens_total, max_seqlen) -> int:
 def tg_topk_select(scores, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, n_kept_total: int,
                    max_seqlen: int, kept_idx=None, workspace=None):
     """Device metadata tensors (int32); n_kept_total = cu_kept[-1] known on the host."""
+    _req(scores, "scores", _F32T, dim=1)
+    _req(cu_seqlens, "cu_seqlens", _I32T, dim=1, device=scores.device)
     n_seqs = cu_seqlens.shape[0] - 1
+    _check_meta(scores.device, n_seqs, doc_begin=doc_begin, doc_end=doc_end, k_doc=k_doc, cu_kept=cu_kept)
+    _req(kept_idx, "kept_idx", _I32T, dim=1, numel=int(n_kept_total), device=scores.device, optional=True)
+    _req(workspace, "workspace", _U8T, device=scores.device, optional=True)
     if kept_idx is None:
         kept_idx = torch.empty(n_kept_total, dtype=torch.int32, device=scores.device)
     lib = load()
@@ -160,8 +213,12 @@ def tg_random_k_workspace_bytes(n_seqs, n_tokens_total, max_seqlen) -> int:
 def tg_random_k_select(seed: int, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, n_tokens: int, n_kept_total: int,
                        max_seqlen: int, kept_idx=None, workspace=None):
     """Random-K selector mode: as tg_topk_select over seeded SplitMix64 scores."""
+    _req(cu_seqlens, "cu_seqlens", _I32T, dim=1)
     n_seqs = cu_seqlens.shape[0] - 1
     dev = cu_seqlens.device
+    _check_meta(dev, n_seqs, doc_begin=doc_begin, doc_end=doc_end, k_doc=k_doc, cu_kept=cu_kept)
+    _req(kept_idx, "kept_idx", _I32T, dim=1, numel=int(n_kept_total), device=dev, optional=True)
+    _req(workspace, "workspace", _U8T, device=dev, optional=True)
     if kept_idx is None:
         kept_idx = torch.empty(n_kept_total, dtype=torch.int32, device=dev)
     lib = load()
@@ -177,9 +234,17 @@ def tg_random_k_select(seed: int, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept
 
 def tg_gather_kept(x, scores, kept_idx, cu_seqlens, cu_kept, x_kept=None, scores_kept=None,
                    pos_kept=None):
+    _req(x, "x", (_BF16T, _F32T), dim=2, dense=False)
     n, d_model, stride = _rows(x)
-    m = kept_idx.shape[0]
     dev = x.device
+    _req(kept_idx, "kept_idx", _I32T, dim=1, device=dev)
+    m = kept_idx.shape[0]
+    _req(scores, "scores", _F32T, dim=1, numel=n, device=dev, optional=True)
+    _req(cu_seqlens, "cu_seqlens", _I32T, dim=1, device=dev)
+    _req(cu_kept, "cu_kept", _I32T, dim=1, numel=cu_seqlens.shape[0], device=dev)
+    _req(x_kept, "x_kept", x.dtype, dim=2, numel=m * d_model, device=dev, optional=True)
+    _req(scores_kept, "scores_kept", _F32T, dim=1, numel=m, device=dev, optional=True)
+    _req(pos_kept, "pos_kept", _I32T, dim=1, numel=m, device=dev, optional=True)
     if x_kept is None:
         x_kept = torch.empty((m, d_model), dtype=x.dtype, device=dev)
     if scores_kept is None and scores is not None:
@@ -197,11 +262,17 @@ def tg_gated_select(x, w1, b1, w2, b2: float, cu_seqlens, doc_begin, doc_end, k_
                     max_seqlen: int, scores=None, kept_idx=None, x_kept=None, scores_kept=None, pos_kept=None,
                     workspace=None):
     """gate -> top-K -> gather in one call.  Returns (scores, kept_idx, x_kept, scores_kept, pos_kept)."""
-    n, d_model, stride = _rows(x)
-    d_hid = w1.shape[0]
-    n_seqs = cu_seqlens.shape[0] - 1
-    m = int(n_kept_total)
+    n, d_model, stride, d_hid = _check_gate(x, w1, b1, w2, scores)
     dev = x.device
+    _req(cu_seqlens, "cu_seqlens", _I32T, dim=1, device=dev)
+    n_seqs = cu_seqlens.shape[0] - 1
+    _check_meta(dev, n_seqs, doc_begin=doc_begin, doc_end=doc_end, k_doc=k_doc, cu_kept=cu_kept)
+    m = int(n_kept_total)
+    _req(kept_idx, "kept_idx", _I32T, dim=1, numel=m, device=dev, optional=True)
+    _req(x_kept, "x_kept", x.dtype, dim=2, numel=m * d_model, device=dev, optional=True)
+    _req(scores_kept, "scores_kept", _F32T, dim=1, numel=m, device=dev, optional=True)
+    _req(pos_kept, "pos_kept", _I32T, dim=1, numel=m, device=dev, optional=True)
+    _req(workspace, "workspace", _U8T, device=dev, optional=True)
     if scores is None:
         scores = torch.empty(n, dtype=torch.float32, device=dev)
     if kept_idx is None:
@@ -229,19 +300,33 @@ def tg_attn_workspace_bytes(n_seqs, n_kept_total, n_kv_heads, head_dim) -> int:
 
 
 def _check_kv(k, v):
+    _req(k, "k", _BF16T, dim=3, dense=False)
+    _req(v, "v", _BF16T, dim=3, dense=False, device=k.device)
+    if v.shape != k.shape:
+        raise ValueError(f"k and v must have one shape, got {tuple(k.shape)} and {tuple(v.shape)}")
     if k.stride(2) != 1 or k.stride(1) != k.shape[2] or v.stride() != k.stride():
         raise ValueError("heads must be contiguous within a token row; k and v must share strides")
 
 
-def _check_q(q):
+def _check_q(q, name="q"):
+    _req(q, name, _BF16T, dim=3, dense=False)
     if q.stride(2) != 1 or q.stride(1) != q.shape[2]:
         raise ValueError("heads must be contiguous within a token row")
+
+
+def _check_attn_meta(dev, m, hq, key_score=None, head_gain=None, pos=None, cu_kept=None):
+    _req(key_score, "key_score", _F32T, dim=1, numel=m, device=dev, optional=key_score is None)
+    _req(head_gain, "head_gain", _F32T, dim=1, numel=hq, device=dev, optional=hq is None)
+    _req(pos, "pos", _I32T, dim=1, numel=m, device=dev, optional=pos is None)
+    _req(cu_kept, "cu_kept", _I32T, dim=1, device=dev)
 
 
 def tg_attn_prepare(k, v, key_score, pos, cu_kept, rope_base: float = 1e6, workspace=None):
     """Kept-only key/value cache for tg_attn_forward; returns the workspace."""
     _check_kv(k, v)
     m, hkv, d = k.shape
+    _check_attn_meta(k.device, m, None, key_score=key_score, pos=pos, cu_kept=cu_kept)
+    _req(workspace, "workspace", _U8T, device=k.device, optional=True)
     n_seqs = cu_kept.shape[0] - 1
     need = tg_attn_workspace_bytes(n_seqs, m, hkv, d)
     if workspace is None:
@@ -258,6 +343,10 @@ def tg_attn_forward(q, head_gain, tau: float, cu_kept, max_kept_seqlen: int, n_k
     _check_q(q)
     m, hq, d = q.shape
     dev = q.device
+    _check_attn_meta(dev, m, hq, head_gain=head_gain, cu_kept=cu_kept)
+    _req(workspace, "workspace", _U8T, device=dev)
+    _req(out, "out", _BF16T, numel=m * hq * d, device=dev, optional=True)
+    _req(lse, "lse", _F32T, numel=m * hq, device=dev, optional=True)
     if out is None:
         out = torch.empty((m, hq, d), dtype=torch.bfloat16, device=dev)
     if lse is None and want_lse:
@@ -278,8 +367,14 @@ def tg_keybias_attn_prefill(q, k, v, key_score, head_gain, tau: float, pos, cu_k
     _check_kv(k, v)
     m, hq, d = q.shape
     hkv = k.shape[1]
-    n_seqs = cu_kept.shape[0] - 1
     dev = q.device
+    if k.device != dev or k.shape[0] != m or k.shape[2] != d:
+        raise ValueError("q, k and v must share the device, the token count and head_dim")
+    _check_attn_meta(dev, m, hq, key_score=key_score, head_gain=head_gain, pos=pos, cu_kept=cu_kept)
+    _req(workspace, "workspace", _U8T, device=dev, optional=True)
+    _req(out, "out", _BF16T, numel=m * hq * d, device=dev, optional=True)
+    _req(lse, "lse", _F32T, numel=m * hq, device=dev, optional=True)
+    n_seqs = cu_kept.shape[0] - 1
     if out is None:
         out = torch.empty((m, hq, d), dtype=torch.bfloat16, device=dev)
     if lse is None and want_lse:
@@ -307,11 +402,17 @@ def tg_attn_decode(q, q_pos, head_gain, tau: float, pos, cu_kept, max_kept_seqle
     pos, cu_kept: the kept positions and offsets the cache was prepared with.
     Returns (out [S, Hq, D] bf16, lse [Hq, S] fp32 or None).
     """
-    if q.dim() != 3 or q.dtype != torch.bfloat16 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
-        raise ValueError("q must be bf16 [S, Hq, D] with contiguous heads")
+    _check_q(q)
     n_seqs, hq, d = q.shape
-    m = int(pos.shape[0])
     dev = q.device
+    _req(pos, "pos", _I32T, dim=1, device=dev)
+    m = int(pos.shape[0])
+    _req(q_pos, "q_pos", _I32T, dim=1, numel=n_seqs, device=dev)
+    _check_attn_meta(dev, m, hq, head_gain=head_gain, cu_kept=cu_kept)
+    _req(cache, "cache", _U8T, device=dev)
+    _req(out, "out", _BF16T, numel=n_seqs * hq * d, device=dev, optional=True)
+    _req(lse, "lse", _F32T, numel=n_seqs * hq, device=dev, optional=True)
+    _req(workspace, "workspace", _U8T, device=dev, optional=True)
     if out is None:
         out = torch.empty((n_seqs, hq, d), dtype=torch.bfloat16, device=dev)
     if lse is None and want_lse:
@@ -342,15 +443,24 @@ def tg_attn_gate_grads(q, v, key_score, head_gain, tau: float, cu_kept, max_kept
     Returns (d_score [M], d_gain [Hq], d_tau [1]) fp32.
     """
     _check_q(q)
-    _check_q(d_out)
+    _check_q(d_out, "d_out")
+    _req(v, "v", _BF16T, dim=3, dense=False, device=q.device)
     if v.stride(2) != 1 or v.stride(1) != v.shape[2]:
         raise ValueError("heads must be contiguous within a token row")
-    if not out.is_contiguous():
-        raise ValueError("out must be dense [M, Hq, D]")
     m, hq, d = q.shape
     hkv = v.shape[1]
-    n_seqs = cu_kept.shape[0] - 1
     dev = q.device
+    if d_out.shape != q.shape or d_out.device != dev or v.shape[0] != m or v.shape[2] != d:
+        raise ValueError("q, v and d_out must share the device, the token count and head_dim")
+    _req(out, "out", _BF16T, dim=3, numel=m * hq * d, device=dev)
+    _req(lse, "lse", _F32T, numel=m * hq, device=dev)
+    _check_attn_meta(dev, m, hq, key_score=key_score, head_gain=head_gain, cu_kept=cu_kept)
+    _req(cache, "cache", _U8T, device=dev)
+    _req(d_score, "d_score", _F32T, dim=1, numel=m, device=dev, optional=True)
+    _req(d_gain, "d_gain", _F32T, dim=1, numel=hq, device=dev, optional=True)
+    _req(d_tau, "d_tau", _F32T, dim=1, numel=1, device=dev, optional=True)
+    _req(workspace, "workspace", _U8T, device=dev, optional=True)
+    n_seqs = cu_kept.shape[0] - 1
     if d_score is None:
         d_score = torch.empty(m, dtype=torch.float32, device=dev)
     if d_gain is None:

@@ -7,17 +7,20 @@
 //     P = softmax_j(l),  dP_ij = <dO_i, v_j>,  Delta_i = <dO_i, O_i>,
 //     dS_ij = P_ij (dP_ij - Delta_i)                          (= dL/dl_ij)
 //     dL/ds_j = sum_h g_h C_hj,   dL/dg_h = sum_j s_j C_hj,   C_hj = sum_i dS_hij
-//     dL/dtau = -(1/tau) sum_h (ln 2 * A_h - g_h dL/dg_h),    A_h = sum_ij dS_hij S_hij
-// where S = l log2(e) is what the MFMA produces, so ln 2 * S - g_h s_j is the
-// q.k part of the logit.  (Delta_i = sum_j P_ij dP_ij because O_i = sum_j P_ij v_j.)
+//     dL/dtau = -(ln 2 / tau) sum_h A_h,    A_h = sum_ij dS_hij Z_hij
+// where Z = <q~_i, k~_j> log2(e) / (sqrt(D) tau) is the q.k part of the logit
+// in the log2 units the MFMAs work in.  (Delta_i = sum_j P_ij dP_ij because
+// O_i = sum_j P_ij v_j.)
 //
-// S' = S - LSE2_i and dP' = dP - Delta_i both come out of the MFMAs: the
-// prepared queries carry (g_hi, g_hi, g_lo, -LSE2_hi, -LSE2_lo) against the
-// key cache's (s_hi, s_lo, s_hi, 1, 1), and the prepared dO rows carry
-// (-Delta_hi, -Delta_lo) against a (1, 1) key fragment, so per element the
-// VALU does P = exp2(S'), dS = P dP', two sums.  The temperature sum uses
-// S' instead of S: every row of dS sums to zero (softmax rows sum to one),
-// so subtracting a per-row constant leaves sum dS S unchanged.
+// Z comes out of the data k-steps of the q.k MFMA chain; its last k-step
+// (the extra columns) continues from Z into S' = Z + g_h s_j log2(e) - LSE2_i,
+// and dP' = dP - Delta_i comes out of the dO.V MFMAs: the prepared queries
+// carry (g_hi, g_hi, g_lo, -LSE2_hi, -LSE2_lo) against the key cache's
+// (s_hi, s_lo, s_hi, 1, 1), and the prepared dO rows carry (-Delta_hi,
+// -Delta_lo) against a (1, 1) key fragment, so per element the VALU does
+// P = exp2(S'), dS = P dP', two sums.  The temperature sum takes Z itself, not
+// S': with the stored bf16 O the rows of dS do not sum exactly to zero, and a
+// per-row constant such as LSE2_i would then leak into the sum.
 //
 // Kernels:
 //   prep    Q' and dO' rows [Hq][padded row][D+16] in the key cache's padded
@@ -30,7 +33,7 @@
 //           32x32x16 bf16 MFMA; the accumulator layout puts one key per lane,
 //           so C_hj is an in-lane sum over the query rows (no atomics,
 //           deterministic), and the workgroup leaves C_hj plus its partial
-//           sums of s_j C_hj and of dS S';
+//           sums of s_j C_hj and of dS Z;
 //   reduce  one launch: dL/ds over heads, and per head dL/dg and dL/dtau.
 #include <math.h>
 
@@ -279,25 +282,27 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_main_kernel(
     // its diagonal block (query rows kb0..kb0+31), the last holds the
     // sequence's last row.  So inside the loop only the diagonal block needs
     // a mask: right after its MFMAs its causally hidden logits are set to
-    // -1e30 (exp2 gives 0, and 0 * -1e30 stays finite in the dS S' sum).  The
+    // -1e30 (exp2 gives 0, so dS = 0 there).  The
     // last block's element work, after the loop, masks rows past the end.
     // Sets start at zero, so the element work of the step before the first
     // block adds exactly 0 (P = 1, dP' = 0).
-    f32x16 sA = f32x16{}, pA = f32x16{}, sB = f32x16{}, pB = f32x16{};
+    f32x16 sA = f32x16{}, pA = f32x16{}, zA = f32x16{}, sB = f32x16{}, pB = f32x16{}, zB = f32x16{};
     constexpr int NI = 2 * (KS + 1);   // MFMAs per block
     constexpr int PF = 4;              // operand reads ahead of their MFMA
-    auto elem = [&](const f32x16& sv, const f32x16& pv, int r, float& cs, float& as) {
+    auto elem = [&](const f32x16& sv, const f32x16& pv, const f32x16& zv, int r, float& cs, float& as) {
         const float p = __builtin_amdgcn_exp2f(sv[r]);
         const float ds = p * pv[r];
         cs += ds;
-        as = fmaf(ds, sv[r], as);
+        as = fmaf(ds, zv[r], as);
     };
     auto step = [&](auto QB, const bf16* qt, const bf16* ot) {
         constexpr int qb = decltype(QB)::value;
         f32x16& sc = qb ? sB : sA;
         f32x16& pc = qb ? pB : pA;
+        f32x16& zc = qb ? zB : zA;
         f32x16& sp = qb ? sA : sB;
         f32x16& pp = qb ? pA : pB;
+        f32x16& zp = qb ? zA : zB;
         float& cs = csum;   // named here so that the generic lambda captures them
         float& as = asum;
         const bf16* qrow = qt + (qb * 32 + il) * (L::ROW * 8) + half * 8;
@@ -317,15 +322,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_main_kernel(
             // rising toward its read
             __asm__ volatile("" ::: "memory");
             __asm__ volatile("" : "+v"(x));
-            if (i == 0) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, kf[0], f32x16{}, 0, 0, 0);
-            else if (i <= KS) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, kf[i], sc, 0, 0, 0);
+            if (i == 0) zc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, kf[0], f32x16{}, 0, 0, 0);
+            else if (i < KS) zc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, kf[i], zc, 0, 0, 0);
+            else if (i == KS) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, kf[KS], zc, 0, 0, 0);
             else if (i == KS + 1) pc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, vf[0], f32x16{}, 0, 0, 0);
             else pc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, vf[i - KS - 1], pc, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 if (r * NI / 16 != i) continue;
-                __asm__ volatile("" : "+v"(sp[r]), "+v"(pp[r]));   // not before this MFMA
-                elem(sp, pp, r, cs, as);
+                __asm__ volatile("" : "+v"(sp[r]), "+v"(pp[r]), "+v"(zp[r]));   // not before this MFMA
+                elem(sp, pp, zp, r, cs, as);
                 __asm__ volatile("" ::"v"(cs), "v"(as));           // and done before the next
             }
         }
@@ -371,13 +377,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_main_kernel(
         const int hi = ms - last_qr0 - 4 * half;
         const f32x16& sv = last_set ? sB : sA;
         const f32x16& pv = last_set ? pB : pA;
+        const f32x16& zv = last_set ? zB : zA;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int k = 8 * (r >> 2) + (r & 3);
             const float p = k < hi ? __builtin_amdgcn_exp2f(sv[r]) : 0.0f;
             const float ds = p * pv[r];
             csum += ds;
-            asum = fmaf(ds, sv[r], asum);
+            asum = fmaf(ds, zv[r], asum);
         }
     }
     // the two lane halves hold the same key over different query rows
@@ -412,8 +419,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_main_kernel(
 // -------------------------------------------------------------- reduce ----
 // One launch: blocks 0..n_ds-1 write dL/ds_j = sum_h g_h C_hj (every q head
 // sees every key of its sequence); block n_ds reduces the per-block partials
-// of each head to dL/dg_h and T_h = ln 2 * A_h - g_h dL/dg_h, then dL/dtau =
-// -sum_h T_h / tau.
+// of each head to dL/dg_h and A_h, then dL/dtau = -(ln 2 / tau) sum_h A_h.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ colsum,
                                                          const float2* __restrict__ part,
                                                          const float* __restrict__ gain, int hq, int64_t m_tot,
@@ -445,7 +451,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
             c += __shfl_xor(c, o, 64);
         }
         if (lane == 0) dg[h] = a;
-        tsum += kLn2 * c - gain[h] * a;
+        tsum += kLn2 * c;
     }
     if (lane == 0) tw[w] = tsum;
     __syncthreads();

@@ -11,6 +11,7 @@ from .tokengate_oracle import (  # noqa: F401
     gather_kept,
     keybias_attention,
     keybias_attention_gate_grads,
+    keybias_attention_gate_grads_at,
     keybias_decode,
     kept_counts,
     random_budgets,

@@ -40,6 +40,11 @@ Parity status per function:
                       forms: g = 0 gives ds = 0, sum_j ds_j = 0, tau scaling);
                       its condition scales pinned by the triangle inequality
                       and the one-key closed form
+  keybias_attention_gate_grads_at
+                      pinned (equals keybias_attention_gate_grads at the exact
+                      forward outputs; a constant added to a head's lse scales
+                      that head's terms by exp(-c); one-key closed form with an
+                      arbitrary stored output)
   keybias_decode      pinned (equals the prefill row of a kept token placed at its
                       position, closed forms, no-visible-key case, shift invariance)
 """
@@ -421,6 +426,96 @@ def keybias_attention_gate_grads(q, k, v, s_kept, gain, tau, pos, cu_kept, d_out
                 dtau_mag += float((env * np.abs(qk / float(tau))).sum())
     if scales:
         return ds, dg, dtau, (ds_mag, dg_mag, dtau_mag)
+    return ds, dg, dtau
+
+
+def keybias_attention_gate_grads_at(q, k, v, s_kept, gain, tau, pos, cu_kept, d_out, out, lse,
+                                    rope_base: float = 1e6, scales: bool = False):
+    """The same three gradients as keybias_attention_gate_grads, evaluated at a
+    stored forward (out, lse) instead of one recomputed exactly.
+
+    A backward pass that receives the forward's outputs (as FlashAttention-style
+    backward passes do) takes the probabilities from the stored log-sum-exp and
+    Delta from the stored output:
+        P_ij = exp(l_ij - lse_i)  (0 where pos_j > pos_i),
+        Delta_i = <dO_i, out_i>,   dS_ij = P_ij (<dO_i, v_j> - Delta_i),
+    and then, exactly as in keybias_attention_gate_grads,
+        dL/ds_j = sum_h g_h sum_i dS_hij,   dL/dg_h = sum_ij s_j dS_hij,
+        dL/dtau = sum_hij dS_hij * (-<q~_i, k~_j> / (sqrt(D) tau^2)).
+    With (out, lse) the exact forward outputs this is the same function (softmax
+    rows sum to one, and out_i = sum_j P_ij v_j gives Delta_i = sum_j P_ij dP_ij).
+    out: [M, Hq, D]; lse: [Hq, M] (natural log).
+
+    scales=True also returns two sets of condition sums over the terms
+    e_ij = P_ij (|dP_ij| + |Delta_i|) times |g_h|, |s_j| or |<q~, k~>| / (sqrt(D) tau^2):
+    their plain sums (as keybias_attention_gate_grads gives), and their
+    quadrature sums, the scale of independent relative errors: for dL/ds_j the
+    root of the sum of squared terms of its column; for dL/dg_h and dL/dtau the
+    root of the sum over query rows of the squared row sums (an error shared by
+    the terms of one row, such as one in Delta_i, adds up along the row and in
+    quadrature across rows).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    s_kept = np.asarray(s_kept, dtype=np.float64)
+    gain = np.asarray(gain, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    ck = np.asarray(cu_kept, dtype=np.int64)
+    m_tot, hq, d = q.shape
+    hkv = k.shape[1]
+    if hq % hkv != 0:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    if not (tau > 0 and math.isfinite(tau)):
+        raise ValueError("tau must be positive and finite")
+    grp = hq // hkv
+    scale = 1.0 / (math.sqrt(d) * float(tau))
+    ds = np.zeros(m_tot)
+    dg = np.zeros(hq)
+    dtau = 0.0
+    ds_mag = np.zeros(m_tot)
+    dg_mag = np.zeros(hq)
+    dtau_mag = 0.0
+    ds_q2 = np.zeros(m_tot)
+    dg_q2 = np.zeros(hq)
+    dtau_q2 = 0.0
+    for si in range(len(ck) - 1):
+        a, b = int(ck[si]), int(ck[si + 1])
+        if a == b:
+            continue
+        p = pos[a:b]
+        qr = rope(q[a:b], p, rope_base)
+        kr = rope(k[a:b], p, rope_base)
+        vs = v[a:b]
+        mask = p[None, :] > p[:, None]
+        for h in range(hq):
+            hk = h // grp
+            qk = (qr[:, h, :] @ kr[:, hk, :].T) * scale
+            logit = qk + gain[h] * s_kept[a:b][None, :]
+            pr = np.exp(logit - lse[h, a:b][:, None])
+            pr[mask] = 0.0
+            dp = d_out[a:b, h, :] @ vs[:, hk, :].T
+            delta = np.sum(d_out[a:b, h, :] * out[a:b, h, :], axis=1)[:, None]
+            dsm = pr * (dp - delta)
+            col = dsm.sum(axis=0)
+            ds[a:b] += gain[h] * col
+            dg[h] += float(s_kept[a:b] @ col)
+            dtau += float((dsm * (-qk / float(tau))).sum())
+            if scales:
+                env = pr * (np.abs(dp) + np.abs(delta))
+                ecol = env.sum(axis=0)
+                ds_mag[a:b] += abs(gain[h]) * ecol
+                dg_mag[h] += float(np.abs(s_kept[a:b]) @ ecol)
+                et = env * np.abs(qk / float(tau))
+                dtau_mag += float(et.sum())
+                ds_q2[a:b] += gain[h] ** 2 * (env ** 2).sum(axis=0)
+                dg_q2[h] += float(((env @ np.abs(s_kept[a:b])) ** 2).sum())
+                dtau_q2 += float((et.sum(axis=1) ** 2).sum())
+    if scales:
+        return ds, dg, dtau, (ds_mag, dg_mag, dtau_mag), (np.sqrt(ds_q2), np.sqrt(dg_q2), math.sqrt(dtau_q2))
     return ds, dg, dtau
 
 

@@ -327,3 +327,51 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120, cwd=root)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def test_binding_rejects_bad_tensors(lib):
+    """The Python binding checks device, dtype, rank and size of every tensor
+    argument before the C call, so a host tensor, a wrong dtype or a short
+    buffer raises instead of reaching a kernel as a bad pointer.  (CPU tensors
+    only: every call here is refused before any GPU work.)"""
+    import torch
+    from learned_token_pruning_05_amd import _lib as tg
+    x = torch.zeros(8, 64, dtype=torch.bfloat16)
+    w1 = torch.zeros(64, 64, dtype=torch.bfloat16)
+    w2 = torch.zeros(64)
+    with pytest.raises(ValueError, match="GPU device"):
+        tg.tg_gate_score(x, w1, None, w2, 0.0)
+    with pytest.raises(TypeError, match="must be a torch tensor"):
+        tg.tg_gate_score(np.zeros((8, 64), np.float32), w1, None, w2, 0.0)
+    i32 = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU device"):
+        tg.tg_topk_select(torch.zeros(8), i32, i32[:1], i32[:1], i32[:1], i32, 2, 8)
+    q = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU device"):
+        tg.tg_keybias_attn_prefill(q, q, q, torch.zeros(4), torch.ones(2), 0.9, torch.zeros(4, dtype=torch.int32),
+                                   i32, 4)
+    with pytest.raises(TypeError):
+        tg.tg_attn_prepare(q.float(), q.float(), torch.zeros(4), torch.zeros(4, dtype=torch.int32), i32)
+    with pytest.raises(ValueError, match="GPU device"):
+        tg.tg_attn_gate_grads(q, q, torch.zeros(4), torch.ones(2), 0.9, i32, 4, q, torch.zeros(2, 4), q,
+                              torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="GPU device"):
+        tg.tg_gather_kept(x, None, torch.zeros(2, dtype=torch.int32), i32, i32)
+
+
+
+def test_binding_check_rules():
+    """_req, the binding's per-tensor check: dtype and rank are checked first,
+    then the device, then size and contiguity (host tensors; no GPU needed)."""
+    import torch
+    from learned_token_pruning_05_amd import _lib as tg
+    t = torch.zeros(4, 8)
+    with pytest.raises(TypeError, match="torch.int32"):
+        tg._req(t, "t", torch.int32)
+    with pytest.raises(ValueError, match="dimensions"):
+        tg._req(t, "t", torch.float32, dim=1)
+    with pytest.raises(ValueError, match="GPU device"):
+        tg._req(t, "t", torch.float32, dim=2)
+    tg._req(None, "t", optional=True)
+    with pytest.raises(ValueError, match="required"):
+        tg._req(None, "t")

@@ -537,6 +537,48 @@ def test_gate_grad_scales_bound_and_closed_form():
     np.testing.assert_allclose(mt1, (2 * np.abs(dp) * np.abs(qk)).sum() / (np.sqrt(8) * tau ** 2), rtol=1e-10)
 
 
+def test_gate_grads_at_stored_forward_reduces_and_scales():
+    """At the exact forward outputs the stored-forward backward is the
+    finite-difference-pinned gradient; a constant c added to one head's lse
+    scales every term of that head by exp(-c) (P = exp(l - lse)), and the other
+    heads' terms are untouched."""
+    q, k, v, s, g, pos, ck, d_out = _grad_case(55, [11, 1, 6], 4, 2, 8)
+    tau = 0.87
+    for base in (0.0, 1e6):
+        out, lse = oracle.keybias_attention(q, k, v, s, g, tau, pos, ck, rope_base=base)
+        ref = oracle.keybias_attention_gate_grads(q, k, v, s, g, tau, pos, ck, d_out, rope_base=base)
+        got = oracle.keybias_attention_gate_grads_at(q, k, v, s, g, tau, pos, ck, d_out, out, lse, rope_base=base)
+        np.testing.assert_allclose(got[0], ref[0], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(got[1], ref[1], rtol=1e-9, atol=1e-12)
+        assert abs(got[2] - ref[2]) <= 1e-9 * max(1.0, abs(ref[2]))
+    out, lse = oracle.keybias_attention(q, k, v, s, g, tau, pos, ck)
+    base_dg = oracle.keybias_attention_gate_grads_at(q, k, v, s, g, tau, pos, ck, d_out, out, lse)[1]
+    lse2 = lse.copy()
+    lse2[2] += 0.7
+    dg2 = oracle.keybias_attention_gate_grads_at(q, k, v, s, g, tau, pos, ck, d_out, out, lse2)[1]
+    np.testing.assert_allclose(dg2[2], base_dg[2] * math.exp(-0.7), rtol=1e-12)
+    np.testing.assert_allclose(np.delete(dg2, 2), np.delete(base_dg, 2), rtol=1e-12)
+
+
+def test_gate_grads_at_one_key_closed_form():
+    """One key per sequence with lse = its own logit (P = 1) and an arbitrary
+    stored output u: dS = <dO, v - u>, so dL/ds = sum_h g_h dS_h,
+    dL/dg_h = sum_j s_j dS_hj and dL/dtau = -sum dS <q, k> / (sqrt(D) tau^2)
+    (rotation at one shared position keeps the inner product)."""
+    q, k, v, s, g, _, _, d_out = _grad_case(56, [1, 1, 1], 4, 2, 8)
+    pos = np.array([7, 0, 250])
+    ck = np.arange(4)
+    tau = 0.93
+    u = np.random.default_rng(57).standard_normal(q.shape)
+    qk = np.stack([[q[j, h] @ k[j, h // 2] for h in range(4)] for j in range(3)]) / (np.sqrt(8) * tau)
+    lse = (qk + g[None, :] * s[:, None]).T                                     # [head, key]
+    dsm = np.stack([[d_out[j, h] @ (v[j, h // 2] - u[j, h]) for h in range(4)] for j in range(3)])
+    ds, dg, dt = oracle.keybias_attention_gate_grads_at(q, k, v, s, g, tau, pos, ck, d_out, u, lse)
+    np.testing.assert_allclose(ds, (dsm * g[None, :]).sum(1), rtol=1e-12)
+    np.testing.assert_allclose(dg, (dsm * s[:, None]).sum(0), rtol=1e-12)
+    assert abs(dt - float(-(dsm * qk).sum() / tau)) <= 1e-12 * max(1.0, abs(dt))
+
+
 # ------------------------------------------------------ random-budget sampling ----
 def test_random_budgets_range_and_uniformity():
     """Budgets lie in {0..n_doc}; over seeds every value is drawn with frequency
