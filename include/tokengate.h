@@ -94,8 +94,9 @@ int tg_gate_score(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d_mo
                   int64_t x_row_stride, const void* w1, const float* b1, const float* w2,
                   float b2, int32_t d_hid, float* scores, void* stream);
 
-/* Workspace bytes tg_topk_select needs: per-sequence state and histogram,
- * per-chunk counts, and 8 bytes per token for threshold candidates. */
+/* Workspace bytes tg_topk_select needs: per-sequence counters and state,
+ * per-chunk histogram rows and counts, and 8 bytes per token for threshold
+ * candidates. */
 size_t tg_topk_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen);
 
 /*
@@ -115,7 +116,9 @@ size_t tg_topk_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32_t m
  *   max_seqlen    host upper bound of every n_s (sizes the grid); at most 4 Mi
  *                 tokens and at most n_tokens_total
  *   workspace     [device] >= tg_topk_workspace_bytes(...) bytes, 256-byte
- *                 aligned, contents need not be initialised
+ *                 aligned, contents need not be initialised (the call's first
+ *                 kernel zeroes the counters it needs).  Calls that share a
+ *                 workspace must not overlap.
  * Errors: TG_ERR_INVALID_ARG on NULL pointers or bad sizes, TG_ERR_UNSUPPORTED
  * for max_seqlen above 4 Mi, TG_ERR_WORKSPACE for a missing or short workspace.
  * n_s > max_seqlen is undefined behaviour (outputs incomplete, never out of
@@ -144,8 +147,8 @@ int tg_topk_select(const float* scores, int32_t n_seqs, int64_t n_tokens_total, 
 int tg_random_budgets(uint64_t seed, int32_t n_seqs, const int32_t* doc_begin_h, const int32_t* doc_end_h,
                       int32_t* k_doc_h);
 
-/* Workspace bytes tg_random_k_select needs: 4 bytes per token for the random
- * scores plus what tg_topk_select needs. */
+/* Workspace bytes tg_random_k_select needs: what tg_topk_select needs plus 4
+ * bytes per token for the random scores. */
 size_t tg_random_k_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen);
 
 /*
@@ -188,11 +191,13 @@ int tg_gather_kept(const void* x, int32_t x_dtype, int32_t d_model, int64_t x_ro
 /*
  * The front half of the gated layer in one call: tg_gate_score, then
  * tg_topk_select on those scores, then tg_gather_kept (spke.com article,
- * gate-module and pruned-forward phases), launched back to back on `stream`
- * after all three argument sets are validated (nothing is launched if any
- * check fails).  The call does no host synchronisation, no allocation and no
- * memset, so a caller can capture it (and the attention after it) into one
- * HIP graph and replay the whole layer as a single launch.
+ * gate-module and pruned-forward phases), after all three argument sets are
+ * validated (nothing is launched if any check fails): six kernels back to
+ * back on `stream` (gate; counter clear, histogram, filter, write of the
+ * selection; row copy).  Results are bit-identical to the three calls made
+ * one by one.  The call does no host synchronisation, no
+ * allocation and no memset, so a caller can capture it (and the attention
+ * after it) into one HIP graph and replay the whole layer as a single launch.
  *   x, x_dtype, n_tokens_total, d_model, x_row_stride, w1, b1, w2, b2, d_hid:
  *                 as for tg_gate_score
  *   n_seqs, max_seqlen, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept:

@@ -210,6 +210,35 @@ def test_topk_deterministic_repeat():
     np.testing.assert_array_equal(a, b)
 
 
+def test_topk_reused_workspace():
+    """One workspace, filled with garbage once, serves a run of calls on
+    different workloads (sequence counts and lengths change the workspace
+    layout; plain and random-K selectors alternate): every call zeroes the
+    counters it needs, so each one is bit-exact against the oracle."""
+    _print_case("topk reused workspace")
+    names = ["varlen", "tiny", "16k", "32k@5%", "varlen", "16k"]
+    ws_bytes = max(max(tg.tg_topk_workspace_bytes(workloads.by_name(n).n_seqs, workloads.by_name(n).n_tokens,
+                                                  int(max(workloads.by_name(n).seqlens))),
+                       tg.tg_random_k_workspace_bytes(workloads.by_name(n).n_seqs, workloads.by_name(n).n_tokens,
+                                                      int(max(workloads.by_name(n).seqlens))))
+                   for n in set(names))
+    ws = torch.full((ws_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    for rep, name in enumerate(names):
+        w = workloads.by_name(name)
+        s = w.topk_scores()
+        ck = tg.tg_kept_counts(w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+        meta = [_i32(a) for a in (w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr, ck)]
+        mx = int(max(w.seqlens))
+        kept = tg.tg_topk_select(_dev(s), *meta, int(ck[-1]), mx, workspace=ws)
+        seed = 1000 + rep
+        kept_r = tg.tg_random_k_select(seed, *meta, w.n_tokens, int(ck[-1]), mx, workspace=ws)
+        torch.cuda.synchronize()
+        ref, _ = oracle.topk_select(s, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+        np.testing.assert_array_equal(kept.cpu().numpy(), ref, err_msg=f"call {rep} ({name})")
+        ref_r, _ = oracle.random_k_select(seed, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+        np.testing.assert_array_equal(kept_r.cpu().numpy(), ref_r, err_msg=f"random-K call {rep} ({name})")
+
+
 # ----------------------------------------------------------------- gather ----
 @pytest.mark.parametrize("name,seed", [("tiny", 0), ("16k", 1), ("128k", 2), ("varlen", 3), ("32k@25%", 2 ** 64 - 1)])
 def test_random_k_bit_exact(name, seed):
