@@ -130,6 +130,28 @@ int tg_topk_select(const float* scores, int32_t n_seqs, int64_t n_tokens_total, 
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * tg_topk_select for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as tg_topk_select, without the
+ * workspace: the selector's scratch is a library-owned device array of
+ * tg_topk_noalloc_max_bytes() = 6 MiB per GPU, allocated with the library's
+ * code object on each device it runs on and held until the process ends.  The
+ * call itself allocates nothing.
+ *   Limit: tg_topk_workspace_bytes(n_seqs, n_tokens_total, max_seqlen) <= 6 MiB
+ *   (for example 64 sequences of 512 Ki tokens in total); larger calls return
+ *   TG_ERR_UNSUPPORTED before any GPU work.
+ *   The first call on each device resolves the array's device address; make
+ *   it before capturing the call into a graph.  Every call on one GPU uses the
+ *   same array (each call first zeroes the counters it needs): calls that
+ *   overlap on one GPU, from several streams or threads, race and give wrong
+ *   results, so serialise them.
+ */
+size_t tg_topk_noalloc_max_bytes(void);
+int tg_topk_select_noalloc(const float* scores, int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen,
+                           const int32_t* cu_seqlens, const int32_t* doc_begin, const int32_t* doc_end,
+                           const int32_t* k_doc, const int32_t* cu_kept, int32_t* kept_idx, void* stream);
+
+/*
  * Random-budget sampling, on the host: the training schedule averages a
  * full-context loss and a loss at a random token budget, so that one gate
  * serves every budget (spke.com article, section on token-gated attention).

@@ -40,6 +40,8 @@ SIGNATURES = {
     "tg_attn_prepare": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _D, _P, _SZ, _P]),
     "tg_attn_forward": (ctypes.c_int, [_P, _I64, _P, _F, _P, _I32, _I64, _I32, _I32, _I32, _I32, _D, _P, _P,
                                        _P, _SZ, _P]),
+    "tg_topk_noalloc_max_bytes": (_SZ, []),
+    "tg_topk_select_noalloc": (ctypes.c_int, [_P, _I32, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]),
     "tg_random_k_workspace_bytes": (_SZ, [_I32, _I64, _I32]),
     "tg_random_k_select": (ctypes.c_int, [ctypes.c_uint64, _I32, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tg_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
@@ -203,6 +205,24 @@ def tg_topk_select(scores, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, n_kep
                             _ptr(doc_end), _ptr(k_doc), _ptr(cu_kept), _ptr(kept_idx), _ptr(workspace),
                             workspace.numel(), _stream(scores))
     _check("tg_topk_select", st)
+    return kept_idx
+
+
+def tg_topk_select_noalloc(scores, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, n_kept_total: int,
+                           max_seqlen: int, kept_idx=None):
+    """tg_topk_select with the library's own scratch array (no workspace; the C
+    call allocates nothing).  kept_idx is allocated here only if not given."""
+    _req(scores, "scores", _F32T, dim=1)
+    _req(cu_seqlens, "cu_seqlens", _I32T, dim=1, device=scores.device)
+    n_seqs = cu_seqlens.shape[0] - 1
+    _check_meta(scores.device, n_seqs, doc_begin=doc_begin, doc_end=doc_end, k_doc=k_doc, cu_kept=cu_kept)
+    _req(kept_idx, "kept_idx", _I32T, dim=1, numel=int(n_kept_total), device=scores.device, optional=True)
+    if kept_idx is None:
+        kept_idx = torch.empty(n_kept_total, dtype=torch.int32, device=scores.device)
+    st = load().tg_topk_select_noalloc(_ptr(scores), n_seqs, scores.shape[0], max_seqlen, _ptr(cu_seqlens),
+                                       _ptr(doc_begin), _ptr(doc_end), _ptr(k_doc), _ptr(cu_kept), _ptr(kept_idx),
+                                       _stream(scores))
+    _check("tg_topk_select_noalloc", st)
     return kept_idx
 
 

@@ -5,6 +5,17 @@
 
 using namespace tg;
 
+// Scratch of tg_topk_select_noalloc: one array per GPU, allocated with the
+// code object when the library loads on that device and held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (on the
+// host that name is only a stand-in for the device variable); it resolves the
+// array's device address once per device with hipGetSymbolAddress and passes
+// that.
+constexpr size_t kScratchBytes = 6u << 20;
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+static std::atomic<void*> g_scratch_ptr[kScratchDevices];
+
 namespace {
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -65,6 +76,22 @@ int gather_check(const void* x, int32_t x_dtype, int32_t d_model, int64_t x_row_
     if (!x || !kept_idx || !x_kept || !aligned16(x) || !aligned16(x_kept)) return TG_ERR_INVALID_ARG;
     if (scores_kept && !scores) return TG_ERR_INVALID_ARG;
     if (pos_kept && (n_seqs < 1 || !cu_seqlens || !cu_kept)) return TG_ERR_INVALID_ARG;
+    return TG_OK;
+}
+
+// Device address of the current device's `scratch` array (resolved on the
+// device's first call, then cached; threads that race here store the same
+// address).
+int scratch_ptr(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TG_ERR_HIP;
+    if (dev < 0 || dev >= kScratchDevices) return TG_ERR_UNSUPPORTED;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TG_ERR_HIP;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
     return TG_OK;
 }
 
@@ -144,6 +171,25 @@ int tg_topk_select(const float* scores, int32_t n_seqs, int64_t n_tokens_total, 
     if (st != TG_OK) return st;
     return launch_topk(scores, n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end,
                        k_doc, cu_kept, kept_idx, workspace, (hipStream_t)stream);
+}
+
+size_t tg_topk_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int tg_topk_select_noalloc(const float* scores, int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen,
+                           const int32_t* cu_seqlens, const int32_t* doc_begin, const int32_t* doc_end,
+                           const int32_t* k_doc, const int32_t* cu_kept, int32_t* kept_idx, void* stream) {
+    if (n_seqs < 0 || n_tokens_total < 0 || n_tokens_total > INT32_MAX || max_seqlen < 0 ||
+        max_seqlen > n_tokens_total)
+        return TG_ERR_INVALID_ARG;
+    if (max_seqlen > topk_max_seqlen()) return TG_ERR_UNSUPPORTED;
+    if (topk_workspace_bytes(n_seqs, n_tokens_total, max_seqlen) > kScratchBytes) return TG_ERR_UNSUPPORTED;
+    if (n_seqs == 0 || n_tokens_total == 0) return TG_OK;
+    if (!cu_seqlens || !doc_begin || !doc_end || !k_doc || !cu_kept || !kept_idx || !scores)
+        return TG_ERR_INVALID_ARG;
+    void* ws = nullptr;
+    if (const int e = scratch_ptr(&ws)) return e;
+    return launch_topk(scores, n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept,
+                       kept_idx, ws, (hipStream_t)stream);
 }
 
 size_t tg_random_k_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen) {
