@@ -191,6 +191,9 @@ class Layer:
         return 2.0 * n * d * dh, float(n * d * e + dh * d * e + 4 * n)
 
     def topk_gather_bytes(self):
+        """Algorithmic bytes of top-K + gather: the scores read, the kept indices
+        written, and per kept row its residual read and written plus index,
+        score and position."""
         n, m, d = self.w.n_tokens, self.m, self.w.d_model
         e = self.x.element_size()
         return float(4 * n + 4 * m + m * (2 * d * e + 12) + 4 * m)
@@ -285,7 +288,7 @@ def measure_random_k(layer: Layer, steps=50, warmup=5):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / steps * 1e3
     return {"us_per_call": round(us, 2), "tokens": n, "kept": layer.m,
-            "kernels": "random_scores_kernel + the five top-K kernels (tg_random_k_select)"}
+            "kernels": "random_scores_kernel + the four top-K kernels (tg_random_k_select)"}
 
 
 def measure_full_prefill(w: workloads.Workload, pruned_layer_ms: float, reps=3):
@@ -511,6 +514,17 @@ def main():
     torch.cuda.empty_cache()
     full = measure_full_prefill(w, r["wall_ms"])
 
+    # the other two configurations' layers: 16k (one sequence) and varlen (8 packed sequences)
+    others = {}
+    for wo in (workloads.qwen16k(), workloads.varlen()):
+        lo = Layer(wo)
+        ro = lo.measure(args.steps, args.warmup)
+        others[wo.name] = summarize(lo, ro)
+        others[wo.name]["cold_cache_stage_us_median"] = lo.measure_cold(args.steps)["stage_us_median"]
+        others[wo.name]["decode"] = measure_decode(lo)
+        del lo
+        torch.cuda.empty_cache()
+
     sweep = {}
     if not args.no_sweep:
         for pct in workloads.BUDGET_PCTS:
@@ -524,8 +538,11 @@ def main():
 
     context = machine_context()
     cpu = None
+    cpu_others = {}
     if not args.no_cpu:
         cpu = cpu_baseline(w)
+        for wo in (workloads.qwen16k(), workloads.varlen()):
+            cpu_others[wo.name] = cpu_baseline(wo)
 
     line = {
         "metric": METRIC,
@@ -555,9 +572,13 @@ def main():
         "gate_grads_128k": grads,
         "random_k_128k": random_k,
         "full_prefill_128k": full,
+        "gated_layer_16k": others.get("16k"),
+        "gated_layer_varlen": others.get("varlen"),
         "sweep_32k": sweep,
         "machine_context": context,
         "cpu_baseline": cpu,
+        "cpu_baseline_16k": cpu_others.get("16k"),
+        "cpu_baseline_varlen": cpu_others.get("varlen"),
     }
     print(json.dumps(line), flush=True)
 
