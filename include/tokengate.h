@@ -25,11 +25,20 @@
  *    HIP call; a failed check returns TG_ERR_INVALID_ARG / TG_ERR_UNSUPPORTED
  *    / TG_ERR_WORKSPACE and launches nothing.  A failed launch returns
  *    TG_ERR_HIP.  Device-resident metadata (cu_seqlens, spans, budgets,
- *    cu_kept, positions) is trusted: inconsistent values are undefined
- *    behaviour.
+ *    cu_kept, kept indices, positions) is trusted: inconsistent values are
+ *    undefined behaviour, unless TG_DEBUG=1 is set in the environment (read
+ *    at every call).  Then each call that takes such metadata first copies it
+ *    to the host, synchronising `stream`, and checks it: offsets start at 0,
+ *    never decrease and end at the stated totals; no sequence is longer than
+ *    max_seqlen / max_kept_seqlen; document spans lie inside their sequences
+ *    and budgets are >= 0; cu_kept equals tg_kept_counts of the rest; kept
+ *    indices lie in their sequences, ascending; positions are >= 0 and
+ *    strictly increase within a sequence.  A violation returns
+ *    TG_ERR_INVALID_ARG and launches nothing.
  *  - Calls are reentrant and thread-safe.  The only global state is, per
  *    kernel, an atomic mask of the devices on which its dynamic LDS limit has
- *    been raised (once per device, at that kernel's first call there).
+ *    been raised (once per device, at that kernel's first call there), and
+ *    the per-device address of tg_topk_select_noalloc's scratch array.
  */
 #ifndef TOKENGATE_H
 #define TOKENGATE_H

@@ -1,5 +1,9 @@
 // C ABI of libtokengate: argument validation (before any HIP call) and launch.
 #include <math.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <vector>
 
 #include "tg_common.hpp"
 
@@ -95,6 +99,85 @@ int scratch_ptr(void** out) {
     return TG_OK;
 }
 
+// ------------------------------------------------------------ TG_DEBUG ----
+// With TG_DEBUG=1 in the environment (read at every call), the entry points
+// that take device metadata copy it to the host (synchronising `stream`) and
+// check what the kernels otherwise trust; a violation returns
+// TG_ERR_INVALID_ARG before anything is launched.
+bool debug_on() {
+    const char* e = getenv("TG_DEBUG");
+    return e && e[0] == '1' && e[1] == 0;
+}
+
+bool fetch_i32(const int32_t* dev, int64_t n, std::vector<int32_t>& h, void* stream) {
+    h.assign((size_t)std::max<int64_t>(n, 0), 0);
+    if (n <= 0) return true;
+    if (!dev) return false;
+    if (hipMemcpyAsync(h.data(), dev, (size_t)n * 4, hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)
+        return false;
+    return hipStreamSynchronize((hipStream_t)stream) == hipSuccess;
+}
+
+// offsets[0] == 0, non-decreasing, offsets[S] == total, every span <= max_len
+bool offsets_ok(const std::vector<int32_t>& cu, int32_t n_seqs, int64_t total, int64_t max_len) {
+    if ((int64_t)cu.size() != (int64_t)n_seqs + 1 || cu[0] != 0 || cu[n_seqs] != total) return false;
+    for (int32_t s = 0; s < n_seqs; ++s)
+        if (cu[s + 1] < cu[s] || (int64_t)cu[s + 1] - cu[s] > max_len) return false;
+    return true;
+}
+
+// The selector's metadata: spans inside their sequences, budgets >= 0, and
+// cu_kept equal to tg_kept_counts of the rest.
+int debug_check_select(int32_t n_seqs, int64_t n_tokens, int32_t max_seqlen, const int32_t* cu_seqlens,
+                       const int32_t* doc_begin, const int32_t* doc_end, const int32_t* k_doc,
+                       const int32_t* cu_kept, int64_t n_kept_total, void* stream) {
+    std::vector<int32_t> cu, b, e, k, ck, ref(n_seqs + 1);
+    if (!fetch_i32(cu_seqlens, n_seqs + 1, cu, stream) || !fetch_i32(doc_begin, n_seqs, b, stream) ||
+        !fetch_i32(doc_end, n_seqs, e, stream) || !fetch_i32(k_doc, n_seqs, k, stream) ||
+        !fetch_i32(cu_kept, n_seqs + 1, ck, stream))
+        return TG_ERR_HIP;
+    if (!offsets_ok(cu, n_seqs, n_tokens, max_seqlen)) return TG_ERR_INVALID_ARG;
+    if (tg_kept_counts(n_seqs, cu.data(), b.data(), e.data(), k.data(), ref.data()) != TG_OK)
+        return TG_ERR_INVALID_ARG;
+    if (ref != ck || (n_kept_total >= 0 && ck[n_seqs] != n_kept_total)) return TG_ERR_INVALID_ARG;
+    return TG_OK;
+}
+
+// kept_idx inside its sequence (so the gather never reads outside x) and
+// ascending there.
+int debug_check_kept(int32_t n_seqs, const int32_t* cu_seqlens, const int32_t* cu_kept, const int32_t* kept_idx,
+                     int64_t n_kept_total, void* stream) {
+    std::vector<int32_t> cu, ck, ki;
+    if (!fetch_i32(cu_seqlens, n_seqs + 1, cu, stream) || !fetch_i32(cu_kept, n_seqs + 1, ck, stream) ||
+        !fetch_i32(kept_idx, n_kept_total, ki, stream))
+        return TG_ERR_HIP;
+    if (cu.empty() || !offsets_ok(cu, n_seqs, cu.back(), INT32_MAX) || !offsets_ok(ck, n_seqs, n_kept_total, INT32_MAX))
+        return TG_ERR_INVALID_ARG;
+    for (int32_t s = 0; s < n_seqs; ++s)
+        for (int32_t m = ck[s]; m < ck[s + 1]; ++m)
+            if (ki[m] < cu[s] || ki[m] >= cu[s + 1] || (m > ck[s] && ki[m] <= ki[m - 1])) return TG_ERR_INVALID_ARG;
+    return TG_OK;
+}
+
+// The attention's metadata: cu_kept offsets of n_kept_total rows with no
+// sequence above max_kept_seqlen (when given), positions >= 0 and strictly
+// increasing within each sequence (the kernels take causality from the kept
+// order).
+int debug_check_attn(int32_t n_seqs, int64_t n_kept_total, int32_t max_kept_seqlen, const int32_t* cu_kept,
+                     const int32_t* pos, void* stream) {
+    std::vector<int32_t> ck, ps;
+    if (!fetch_i32(cu_kept, n_seqs + 1, ck, stream)) return TG_ERR_HIP;
+    if (!offsets_ok(ck, n_seqs, n_kept_total, max_kept_seqlen >= 0 ? max_kept_seqlen : INT32_MAX))
+        return TG_ERR_INVALID_ARG;
+    if (pos) {
+        if (!fetch_i32(pos, n_kept_total, ps, stream)) return TG_ERR_HIP;
+        for (int32_t s = 0; s < n_seqs; ++s)
+            for (int32_t m = ck[s]; m < ck[s + 1]; ++m)
+                if (ps[m] < 0 || (m > ck[s] && ps[m] <= ps[m - 1])) return TG_ERR_INVALID_ARG;
+    }
+    return TG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,6 +252,10 @@ int tg_topk_select(const float* scores, int32_t n_seqs, int64_t n_tokens_total, 
                               cu_kept, kept_idx, workspace, workspace_bytes);
     if (st == -1) return TG_OK;
     if (st != TG_OK) return st;
+    if (debug_on())
+        if (const int e = debug_check_select(n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end,
+                                             k_doc, cu_kept, -1, stream))
+            return e;
     return launch_topk(scores, n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end,
                        k_doc, cu_kept, kept_idx, workspace, (hipStream_t)stream);
 }
@@ -186,6 +273,10 @@ int tg_topk_select_noalloc(const float* scores, int32_t n_seqs, int64_t n_tokens
     if (n_seqs == 0 || n_tokens_total == 0) return TG_OK;
     if (!cu_seqlens || !doc_begin || !doc_end || !k_doc || !cu_kept || !kept_idx || !scores)
         return TG_ERR_INVALID_ARG;
+    if (debug_on())
+        if (const int e = debug_check_select(n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end,
+                                             k_doc, cu_kept, -1, stream))
+            return e;
     void* ws = nullptr;
     if (const int e = scratch_ptr(&ws)) return e;
     return launch_topk(scores, n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept,
@@ -209,6 +300,10 @@ int tg_random_k_select(uint64_t seed, int32_t n_seqs, int64_t n_tokens_total, in
     if (!cu_seqlens || !doc_begin || !doc_end || !k_doc || !cu_kept || !kept_idx) return TG_ERR_INVALID_ARG;
     const size_t need = random_k_workspace_bytes(n_seqs, n_tokens_total, max_seqlen);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return TG_ERR_WORKSPACE;
+    if (debug_on())
+        if (const int e = debug_check_select(n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end,
+                                             k_doc, cu_kept, -1, stream))
+            return e;
     return launch_random_k(seed, n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end, k_doc,
                            cu_kept, kept_idx, workspace, (hipStream_t)stream);
 }
@@ -221,6 +316,8 @@ int tg_gather_kept(const void* x, int32_t x_dtype, int32_t d_model, int64_t x_ro
                                 cu_seqlens, cu_kept, x_kept, scores_kept, pos_kept);
     if (st == -1) return TG_OK;
     if (st != TG_OK) return st;
+    if (debug_on() && cu_seqlens && cu_kept)
+        if (const int e = debug_check_kept(n_seqs, cu_seqlens, cu_kept, kept_idx, n_kept_total, stream)) return e;
     const int esize = x_dtype == TG_BF16 ? 2 : 4;
     return launch_gather(x, esize, d_model, x_row_stride, scores, kept_idx, n_kept_total, n_seqs,
                          cu_seqlens, cu_kept, x_kept, scores_kept, pos_kept, (hipStream_t)stream);
@@ -242,6 +339,10 @@ int tg_gated_select(const void* x, int32_t x_dtype, int64_t n_tokens_total, int3
     const int sga = gather_check(x, x_dtype, d_model, x_row_stride, scores, kept_idx, n_kept_total, n_seqs,
                                  cu_seqlens, cu_kept, x_kept, scores_kept, pos_kept);
     if (sga != TG_OK && sga != -1) return sga;
+    if (debug_on() && stk == TG_OK)
+        if (const int e = debug_check_select(n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end,
+                                             k_doc, cu_kept, n_kept_total, stream))
+            return e;
     if (sg == TG_OK) {
         const int st = gate_launch(x, x_dtype, n_tokens_total, d_model, x_row_stride, w1, b1, w2, b2, d_hid,
                                    scores, stream);
@@ -333,6 +434,8 @@ int tg_attn_prepare(const void* k, const void* v, int64_t kv_row_stride, const f
     if (st == -1) return TG_OK;
     if (st != TG_OK) return st;
     if (!k || !v || !key_score || !pos || !cu_kept || !aligned16(k) || !aligned16(v)) return TG_ERR_INVALID_ARG;
+    if (debug_on())
+        if (const int e = debug_check_attn(n_seqs, n_kept_total, -1, cu_kept, pos, stream)) return e;
     AttnArgs a{};
     attn_fill(a, n_seqs, n_kept_total, n_kv_heads, head_dim, rope_base, workspace);
     a.k = (const bf16*)k;
@@ -354,6 +457,8 @@ int tg_attn_forward(const void* q, int64_t q_row_stride, const float* head_gain,
     if (st == -1) return TG_OK;
     if (st != TG_OK) return st;
     if (!head_gain || !cu_kept) return TG_ERR_INVALID_ARG;
+    if (debug_on())
+        if (const int e = debug_check_attn(n_seqs, n_kept_total, max_kept_seqlen, cu_kept, nullptr, stream)) return e;
     AttnArgs a{};
     attn_fill(a, n_seqs, n_kept_total, n_kv_heads, head_dim, rope_base, workspace);
     a.q = (const bf16*)q;
@@ -416,6 +521,8 @@ int tg_attn_decode(const void* q, int64_t q_row_stride, const int32_t* q_pos, co
     if (n_seqs == 0 && n_kept_total > 0) return TG_ERR_INVALID_ARG;   // kept keys but no sequence
     if (n_seqs == 0) return TG_OK;
     if (!q || !q_pos || !head_gain || !cu_kept || !out || (n_kept_total > 0 && !pos)) return TG_ERR_INVALID_ARG;
+    if (debug_on())
+        if (const int e = debug_check_attn(n_seqs, n_kept_total, max_kept_seqlen, cu_kept, pos, stream)) return e;
     const size_t cache_need = attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, nullptr,
                                                     nullptr, nullptr);
     if (!cache || cache_bytes < cache_need || ((uintptr_t)cache & 255u) != 0) return TG_ERR_WORKSPACE;
@@ -491,6 +598,8 @@ int tg_attn_gate_grads(const void* q, int64_t q_row_stride, const void* v, int64
     if (!q || !v || !key_score || !head_gain || !cu_kept || !out || !lse || !d_out || !d_score)
         return TG_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(v) || !aligned16(out) || !aligned16(d_out)) return TG_ERR_INVALID_ARG;
+    if (debug_on())
+        if (const int e = debug_check_attn(n_seqs, n_kept_total, max_kept_seqlen, cu_kept, nullptr, stream)) return e;
     const size_t cache_need = attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, nullptr,
                                                     nullptr, nullptr);
     if (!cache || cache_bytes < cache_need || ((uintptr_t)cache & 255u) != 0) return TG_ERR_WORKSPACE;

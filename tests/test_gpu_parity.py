@@ -1061,3 +1061,45 @@ def test_gated_layer_end_to_end(name):
                                                  sk.cpu().numpy(), pk.cpu().numpy())
     c = dict(q=q, k=k, v=v, sk=sk_r, pk=pk_r, ck=ck_r, gain=gain, tau=tau)
     _check_attn(c, out.float().cpu().numpy(), lse.cpu().numpy(), w.rope_base, np.arange(int(ck[-1])))
+
+
+# ------------------------------------------------------------------ TG_DEBUG ----
+def test_debug_metadata_checks(monkeypatch):
+    """With TG_DEBUG=1 the calls check their device metadata on the host first:
+    consistent metadata runs as usual (results against the oracle); a wrong
+    cu_kept, a kept index outside its sequence, positions that do not
+    increase, or a sequence longer than max_kept_seqlen return
+    TG_ERR_INVALID_ARG and launch nothing."""
+    _print_case("TG_DEBUG checks")
+    monkeypatch.setenv("TG_DEBUG", "1")
+    w = workloads.custom([300, 200], [20, 10], [100, 50], n_q_heads=4, n_kv_heads=2, head_dim=64, seed=61)
+    s = w.topk_scores()
+    ck = tg.tg_kept_counts(w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+    meta = [_i32(a) for a in (w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr, ck)]
+    m, mx = int(ck[-1]), int(max(w.seqlens))
+    kept = tg.tg_topk_select(_dev(s), *meta, m, mx)
+    torch.cuda.synchronize()
+    ref, _ = oracle.topk_select(s, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+    np.testing.assert_array_equal(kept.cpu().numpy(), ref)
+    bad_ck = ck.copy()
+    bad_ck[1] += 1
+    with pytest.raises(tg.TokenGateError, match="INVALID_ARG"):
+        tg.tg_topk_select(_dev(s), *meta[:4], _i32(bad_ck), int(bad_ck[-1]), mx)
+    x = torch.zeros(w.n_tokens, 64, dtype=torch.bfloat16, device="cuda")
+    bad_kept = kept.clone()
+    bad_kept[0] = w.n_tokens + 5
+    with pytest.raises(tg.TokenGateError, match="INVALID_ARG"):
+        tg.tg_gather_kept(x, None, bad_kept, meta[0], meta[4])
+    c = _attn_case(w)
+    pk_bad = c["pk"].copy()
+    pk_bad[3] = pk_bad[2]
+    with pytest.raises(tg.TokenGateError, match="INVALID_ARG"):
+        tg.tg_attn_prepare(_dev(c["k"]), _dev(c["v"]), _dev(c["sk"]), _i32(pk_bad), _i32(c["ck"]), rope_base=1e6)
+    cache = tg.tg_attn_prepare(_dev(c["k"]), _dev(c["v"]), _dev(c["sk"]), _i32(c["pk"]), _i32(c["ck"]), rope_base=1e6)
+    short = int(np.diff(c["ck"]).max()) - 1
+    with pytest.raises(tg.TokenGateError, match="INVALID_ARG"):
+        tg.tg_attn_forward(_dev(c["q"]), _dev(c["gain"]), c["tau"], _i32(c["ck"]), short, 2, cache, rope_base=1e6)
+    out, lse = tg.tg_attn_forward(_dev(c["q"]), _dev(c["gain"]), c["tau"], _i32(c["ck"]), short + 1, 2, cache,
+                                  rope_base=1e6)
+    torch.cuda.synchronize()
+    _check_attn(c, out.float().cpu().numpy(), lse.cpu().numpy(), 1e6, np.arange(int(c["ck"][-1])))
