@@ -36,6 +36,28 @@ def test_gate_matches_torch_linear_silu():
     np.testing.assert_allclose(got, ref.numpy(), rtol=1e-13, atol=1e-13)
 
 
+def test_gate_matches_scalar_loop():
+    """The gate written out token by token and unit by unit in plain Python
+    floats (math.exp, no arrays): s = b2 + sum_n w2_n a_n / (1 + exp(-a_n)),
+    a_n = b1_n + sum_k W1_nk x_k."""
+    r = np.random.default_rng(13)
+    x = r.standard_normal((9, 7))
+    w1 = r.standard_normal((5, 7)) * 0.4
+    b1 = r.standard_normal(5) * 0.2
+    w2 = r.standard_normal(5)
+    b2 = -0.3
+    ref = []
+    for t in range(x.shape[0]):
+        acc = b2
+        for n in range(w1.shape[0]):
+            a = float(b1[n])
+            for kk in range(x.shape[1]):
+                a += float(w1[n, kk]) * float(x[t, kk])
+            acc += float(w2[n]) * a / (1.0 + math.exp(-a))
+        ref.append(acc)
+    np.testing.assert_allclose(oracle.gate_score(x, w1, b1, w2, b2), ref, rtol=1e-13, atol=1e-14)
+
+
 def test_gate_closed_forms():
     r = np.random.default_rng(12)
     w1 = r.standard_normal((6, 5))
