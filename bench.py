@@ -36,7 +36,7 @@ from learned_token_pruning_05_amd import _lib as tg  # noqa: E402
 METRIC = "ms/gated layer + key-bias attn TFLOP/s (frac bf16 peak) at 32k/128k, 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-PROFILE_PMC = os.path.join(ROOT, "profiles", "attn_fwd_128k_pmc.md")
+PROFILE_PMC = os.path.join(ROOT, "profiles", "gated_layer_hbm_counters.md")
 COPY_BYTES = 256 << 20         # --calibrate-copy: bytes read (and written) per copy
 
 
@@ -498,9 +498,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    t_start = time.perf_counter()
+
+    def progress(what):
+        print(f"[bench] {what} done ({time.perf_counter() - t_start:.1f} s)", file=sys.stderr, flush=True)
+
     w = workloads.long128k()
     layer = Layer(w)
     r = layer.measure(args.steps, args.warmup)
+    progress("128k gated layer")
     head = summarize(layer, r)
     af = layer.attn_work()
     attn_s = r["stage_ms"][Layer.STAGES.index("attn_fwd")] * 1e-3
@@ -513,6 +519,7 @@ def main():
     del layer
     torch.cuda.empty_cache()
     full = measure_full_prefill(w, r["wall_ms"])
+    progress("128k cold cache, graph, decode, gate gradients, random-K, full prefill")
 
     # the other two configurations' layers: 16k (one sequence) and varlen (8 packed sequences)
     others = {}
@@ -524,6 +531,7 @@ def main():
         others[wo.name]["decode"] = measure_decode(lo)
         del lo
         torch.cuda.empty_cache()
+        progress(f"{wo.name} gated layer")
 
     sweep = {}
     if not args.no_sweep:
@@ -535,14 +543,17 @@ def main():
             sweep[ws.name]["cold_cache_stage_us_median"] = ls.measure_cold(max(5, args.steps // 2))["stage_us_median"]
             del ls
             torch.cuda.empty_cache()
+            progress(ws.name)
 
     context = machine_context()
     cpu = None
     cpu_others = {}
     if not args.no_cpu:
         cpu = cpu_baseline(w)
+        progress("CPU oracle 128k")
         for wo in (workloads.qwen16k(), workloads.varlen()):
             cpu_others[wo.name] = cpu_baseline(wo)
+            progress(f"CPU oracle {wo.name}")
 
     line = {
         "metric": METRIC,
