@@ -42,7 +42,10 @@
 //     Causality uses the kept order (positions increase within a sequence, so
 //     pos_j <= pos_i  <=>  j <= i).  Blocks are ordered head-fastest so that,
 //     with workgroups dealt round-robin to the 8 XCDs, each KV head keeps to
-//     one XCD's L2.
+//     one XCD's L2; then by sequence, then by query tile, largest first.  The
+//     workgroups resident on one XCD thus walk the K'/V^T tiles of one or two
+//     sequences at a time, which stay in its L2 (interleaving the sequences
+//     made packed batches re-fetch about 4x the read-once bytes).
 #include <math.h>
 
 #include "tg_common.hpp"
@@ -277,8 +280,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
     const int b = blockIdx.x;
     const int hidx = b % n_hblk;
     const int rest = b / n_hblk;
-    const int s = rest % n_seqs;
-    const int qt = n_qtiles - 1 - rest / n_seqs;
+    const int s = rest / n_qtiles;
+    const int qt = n_qtiles - 1 - rest % n_qtiles;
     const int cs0 = cu_kept[s];
     const int ms = cu_kept[s + 1] - cs0;
     const int q0 = qt * BMT;

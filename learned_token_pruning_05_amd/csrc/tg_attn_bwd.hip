@@ -215,8 +215,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_main_kernel(
     const int b = blockIdx.x;
     const int h = b % hq;
     const int rest = b / hq;
-    const int s = rest % n_seqs;
-    const int kt = rest / n_seqs;
+    const int s = rest / n_kt;
+    const int kt = rest % n_kt;
     const int cs0 = cu_kept[s];
     const int ms = cu_kept[s + 1] - cs0;
     const int key0 = kt * kBwdKeys;
