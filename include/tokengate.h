@@ -35,7 +35,9 @@
  *    indices lie in their sequences, ascending; positions are >= 0 and
  *    strictly increase within a sequence.  A violation returns
  *    TG_ERR_INVALID_ARG and launches nothing.
- *  - Calls are reentrant and thread-safe.  The only global state is, per
+ *  - Calls are reentrant and thread-safe, except that calls of
+ *    tg_topk_select_noalloc on one GPU share its scratch array and must not
+ *    overlap (see there).  The only global state is, per
  *    kernel, an atomic mask of the devices on which its dynamic LDS limit has
  *    been raised (once per device, at that kernel's first call there), and
  *    the per-device address of tg_topk_select_noalloc's scratch array.
