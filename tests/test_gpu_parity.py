@@ -435,6 +435,19 @@ def test_attention_temperature_extremes(tau):
     _check_grads(c, d_out, 1e6, _run_grads(c, d_out, 1e6), scale=max(1.0, 0.9 / tau))
 
 
+def test_attention_1100_short_sequences():
+    """1100 packed sequences of 1-32 kept tokens (a grid of 1100 x 1 query
+    tiles per head block, most of its key tiles padded): every row against the
+    oracle."""
+    r = np.random.default_rng(37)
+    lens = r.integers(1, 33, 1100)
+    w = workloads.custom(list(lens), [0] * 1100, list(lens), n_q_heads=4, n_kv_heads=2, head_dim=64, seed=43)
+    _print_case("attn 1100 sequences")
+    c = _attn_case(w)
+    out, lse = _run_attn(c, 1e6)
+    _check_attn(c, out, lse, 1e6, np.arange(int(c["ck"][-1])))
+
+
 def test_many_short_sequences():
     """300 packed sequences of 0-40 tokens (many empty or one-token ones): the
     selector bit-exact, then attention on every kept row, one decode query per
