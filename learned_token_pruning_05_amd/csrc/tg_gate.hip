@@ -39,9 +39,12 @@ __device__ __forceinline__ float silu_f32(float a) {
 
 // BM tokens per workgroup (BM / 64 row groups of waves x 2 hidden-column
 // groups); CB = 32-wide hidden blocks per wave, d_hid = 64 * CB.  Both operands
-// are K-contiguous and arrive by global_load_lds_dwordx4 (1 KiB of consecutive
-// LDS per instruction; rows padded by one 16-B chunk whose slot reloads chunk
-// 0).  Three slab buffers keep two slabs of loads in flight per workgroup.
+// are K-contiguous, in two LDS slab buffers (one multiplied while the next
+// fills; rows padded by one 16-B chunk).  W1 slabs arrive by
+// global_load_lds_dwordx4 (1 KiB of consecutive LDS per instruction, the pad
+// slot reloading chunk 0).  With 256-token tiles X comes through registers,
+// loaded two slabs ahead and stored to LDS one slab ahead; with 128-token
+// tiles X takes the LDS-direct path as well, one slab ahead.
 template <int CB, int BM>
 __global__ __launch_bounds__(BM * 2, 1) void gate_bf16_kernel(
     const bf16* __restrict__ x, int64_t n, int d_model, int64_t x_stride,
