@@ -554,6 +554,8 @@ def main():
         others[wo.name] = summarize(lo, ro)
         others[wo.name]["cold_cache_stage_us_median"] = lo.measure_cold(args.steps)["stage_us_median"]
         others[wo.name]["decode"] = measure_decode(lo)
+        others[wo.name]["gate_grads"] = measure_gate_grads(lo)
+        others[wo.name]["random_k"] = measure_random_k(lo)
         del lo
         torch.cuda.empty_cache()
         progress(f"{wo.name} gated layer")
