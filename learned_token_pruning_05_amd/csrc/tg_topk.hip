@@ -9,8 +9,10 @@
 // Scores map to order-preserving 32-bit keys (larger score <=> larger key; -0
 // and +0 share a key; NaN is key 0, below -inf).  Per sequence the selector
 // needs the key T of the K_eff-th document token and r, the number of tokens
-// with key == T that are kept (the r lowest-indexed ones).  Four launches, no
-// cross-workgroup waiting:
+// with key == T that are kept (the r lowest-indexed ones).  A batch whose
+// sequences all fit in 16 Ki tokens takes one launch (S, below: one workgroup
+// per sequence).  Longer sequences take four launches, with no cross-workgroup
+// waiting:
 //   C  zero the per-sequence counters (histogram, tickets, list length): a
 //      kernel, not a memset, so that the call can be captured into a graph
 //      and replayed;
@@ -509,6 +511,130 @@ __global__ __launch_bounds__(kWriteThreads) void topk_write_kernel(
         if (kept[j] && slot[j] < m_s) out[slot[j]] = q.start + c0 + j * kWriteThreads + tid;
 }
 
+// ------------------------------------------------------------------ S ----
+// Sequences of at most 16 Ki tokens: one 1024-thread workgroup per sequence
+// does the whole selection in one launch (the chunked passes above spread
+// longer sequences over many CUs, which pays from about 32 Ki tokens on).
+// Wave w holds tokens [64 E w, 64 E (w+1)) in registers, item e of lane l
+// being token 64 (E w + e) + l, so the thread order is the token order.  An
+// item holds the score key of a document token, else 0xffffffff, above every
+// score key (a token outside the document is always kept; an item past the
+// end of the sequence comes after every real token, so it never takes a real
+// slot).  Three radix passes (11, 11 and 10 bits) over LDS histograms of the
+// document keys give T and r; then "key > T" marks the always-kept and
+// "key == T" the tie tokens, and per-wave counts plus a scan over the 16 waves
+// give every kept token its slot, as in the write pass.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / 64;
+constexpr int kSmallMax = kSmallThreads * 16;   // 16 Ki tokens
+
+template <int E>
+__global__ __launch_bounds__(kSmallThreads) void topk_small_kernel(
+    const float* __restrict__ scores, const int* __restrict__ cu, const int* __restrict__ db,
+    const int* __restrict__ de, const int* __restrict__ kd, const int* __restrict__ cu_kept,
+    int* __restrict__ kept_idx) {
+    __shared__ uint32_t h[2048];
+    __shared__ uint32_t sh_scan[kSmallWaves];
+    __shared__ uint32_t sh_out[2];
+    __shared__ uint32_t wcnt[2][kSmallWaves];
+    const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const SeqInfo q(s, cu, db, de, kd);
+    if (q.n <= 0) return;
+    const float* sc = scores + q.start;
+    const int first = w * E * 64 + lane;   // token of item 0; item e adds 64 e
+    constexpr uint32_t kOut = 0xffffffffu;  // no score key is this large (+inf is 0xff800000)
+
+    // every load unconditional (clamped to the last token), all in flight at once
+    uint32_t key[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) key[e] = __float_as_uint(sc[min(first + 64 * e, q.n - 1)]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = first + 64 * e;
+        key[e] = i >= q.db && i < q.de ? score_key(__uint_as_float(key[e])) : kOut;
+    }
+
+    // (T, r) such that "key > T, or key == T among the first r" keeps exactly
+    // the sequence's tokens: T = 0, r = all when the whole document is kept
+    // (NaN scores have key 0); T = 0xfffffffe, r = 0 when none of it is (no
+    // score key equals that)
+    uint32_t T, r;
+    if (q.needs_select()) {
+        uint32_t rem = (uint32_t)q.k, prefix = 0, pmask = 0;
+#pragma unroll
+        for (int pass = 0; pass < 3; ++pass) {
+            const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+            const uint32_t nbm = pass < 2 ? 2047u : 1023u;
+            for (int i = tid; i < 2048; i += kSmallThreads) h[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (key[e] != kOut && (key[e] & pmask) == prefix) atomicAdd(&h[(key[e] >> shift) & nbm], 1u);
+            __syncthreads();
+            uint32_t bk, ab;
+            if (pass < 2) find_bucket<2048, kSmallThreads>(h, rem, sh_scan, sh_out, &bk, &ab);
+            else find_bucket<1024, kSmallThreads>(h, rem, sh_scan, sh_out, &bk, &ab);
+            rem -= ab;
+            prefix |= bk << shift;
+            pmask |= nbm << shift;
+        }
+        T = prefix;
+        r = rem;
+    } else if (q.k > 0) {
+        T = 0u;
+        r = 0xffffffffu;
+    } else {
+        T = 0xfffffffeu;
+        r = 0u;
+    }
+
+    T = __builtin_amdgcn_readfirstlane(T);
+    r = __builtin_amdgcn_readfirstlane(r);
+    // T is re-made opaque for every item, so each item's two compares stay
+    // next to their use instead of 2E lane masks being computed up front
+    // (they would spill)
+    uint32_t na = 0, nb = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        __asm__ volatile("" : "+s"(T));
+        na += (uint32_t)__popcll(__ballot(key[e] > T));
+        nb += (uint32_t)__popcll(__ballot(key[e] == T));
+    }
+    if (lane == 0) {
+        wcnt[0][w] = na;
+        wcnt[1][w] = nb;
+    }
+    __syncthreads();
+    uint32_t ba = 0, bb = 0;
+    for (int x = 0; x < w; ++x) {
+        ba += wcnt[0][x];
+        bb += wcnt[1][x];
+    }
+    int* __restrict__ out = kept_idx + cu_kept[s];
+    const uint32_t m_s = (uint32_t)(cu_kept[s + 1] - cu_kept[s]);
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        __asm__ volatile("" : "+s"(T));
+        const bool fa = key[e] > T, fb = key[e] == T;
+        const uint64_t ma = __ballot(fa), mb = __ballot(fb);
+        const uint32_t pa = ba + (uint32_t)__popcll(ma & below);
+        const uint32_t pb = bb + (uint32_t)__popcll(mb & below);
+        const uint32_t slot = pa + min(pb, r);
+        if ((fa || (fb && pb < r)) && slot < m_s) out[slot] = q.start + first + 64 * e;
+        ba += (uint32_t)__popcll(ma);
+        bb += (uint32_t)__popcll(mb);
+    }
+}
+
+template <int E>
+void launch_small(const float* scores, int n_seqs, const int* cu, const int* db, const int* de, const int* kd,
+                  const int* cu_kept, int* kept_idx, hipStream_t stm) {
+    hipLaunchKernelGGL(topk_small_kernel<E>, dim3(n_seqs), dim3(kSmallThreads), 0, stm, scores, cu, db, de, kd,
+                       cu_kept, kept_idx);
+}
+
 struct TopkLayout {
     size_t ctl, st, sel, a0, ba, bb, cand, total;
 };
@@ -605,6 +731,13 @@ int launch_topk(const float* scores, int n_seqs, int64_t n_tokens, int max_seqle
                 const int* cu_seqlens, const int* doc_begin, const int* doc_end, const int* k_doc,
                 const int* cu_kept, int* kept_idx, void* ws, hipStream_t stm) {
     if (n_seqs == 0 || max_seqlen == 0) return TG_OK;
+    if (max_seqlen <= kSmallMax) {
+        if (max_seqlen <= 4096)
+            launch_small<4>(scores, n_seqs, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, kept_idx, stm);
+        else
+            launch_small<16>(scores, n_seqs, cu_seqlens, doc_begin, doc_end, k_doc, cu_kept, kept_idx, stm);
+        return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
+    }
     const TopkPtrs P = topk_ptrs(ws, n_seqs, n_tokens, max_seqlen);
     const int nch_w = (max_seqlen + kChunk - 1) / kChunk;
     launch_select_passes(scores, n_seqs, max_seqlen, cu_seqlens, doc_begin, doc_end, k_doc, P, stm);

@@ -109,24 +109,37 @@ def test_gate_strided_rows():
 
 
 # ------------------------------------------------------------------ top-K ----
-def _topk_gpu(scores_np, cu, b, e, k):
-    ck = tg.tg_kept_counts(cu, b, e, k)
+# Batches whose sequences all fit in 16 Ki tokens take the one-workgroup
+# selector.  chunked=True appends one 65537-token sequence
+# (workloads.pad_long_sequence), which sends the whole batch through the
+# chunked four-launch selector; the original sequences' kept indices are the
+# first part of its output.  Both selectors are checked on the small cases.
+def _max_seqlen(cu):
     lens = np.diff(np.asarray(cu))
+    return int(lens.max()) if lens.size else 0
+
+
+def _topk_gpu(scores_np, cu, b, e, k, chunked=False):
+    ck = tg.tg_kept_counts(cu, b, e, k)
+    if chunked:
+        scores_np, cu, b, e, k = workloads.pad_long_sequence(scores_np, cu, b, e, k)
+    ckp = tg.tg_kept_counts(cu, b, e, k)
     kept = tg.tg_topk_select(_dev(np.asarray(scores_np, dtype=np.float32)), _i32(cu), _i32(b), _i32(e), _i32(k),
-                             _i32(ck), int(ck[-1]), int(lens.max()) if lens.size else 0)
+                             _i32(ckp), int(ckp[-1]), _max_seqlen(cu))
     torch.cuda.synchronize()
-    return kept.cpu().numpy(), ck
+    return kept.cpu().numpy()[:int(ck[-1])], ck
 
 
 TOPK_CASES = [w.name for w in workloads.all_configs()]
 
 
+@pytest.mark.parametrize("chunked", [False, True], ids=["fit", "chunked"])
 @pytest.mark.parametrize("name", TOPK_CASES)
-def test_topk_configs_bit_exact(name):
-    _print_case(f"topk {name}")
+def test_topk_configs_bit_exact(name, chunked):
+    _print_case(f"topk {name} chunked={chunked}")
     w = workloads.by_name(name)
     s = w.topk_scores()
-    got, ck = _topk_gpu(s, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+    got, ck = _topk_gpu(s, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr, chunked)
     want, ck2 = oracle.topk_select(s, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
     assert ck.tolist() == ck2.tolist()
     np.testing.assert_array_equal(got, want)
@@ -155,15 +168,16 @@ def _edge_scores():
     yield "normal", r.standard_normal(131072).astype(np.float32)
 
 
+@pytest.mark.parametrize("chunked", [False, True], ids=["fit", "chunked"])
 @pytest.mark.parametrize("k_frac", [0.0, 0.001, 0.3, 0.999, 1.0, 1.5])
-def test_topk_edge_values_and_budgets(k_frac):
+def test_topk_edge_values_and_budgets(k_frac, chunked):
     for tag, s in _edge_scores():
         n = s.shape[0]
         q = min(256, n // 4)
         nd = n - q
         k = int(nd * k_frac)
-        _print_case(f"topk edge {tag} n={n} k={k}")
-        got, _ = _topk_gpu(s, [0, n], [0], [nd], [k])
+        _print_case(f"topk edge {tag} n={n} k={k} chunked={chunked}")
+        got, _ = _topk_gpu(s, [0, n], [0], [nd], [k], chunked)
         want, _ = oracle.topk_select(s, [0, n], [0], [nd], [k])
         np.testing.assert_array_equal(got, want, err_msg=tag)
 
@@ -182,7 +196,8 @@ def test_topk_max_seqlen_bit_exact():
     np.testing.assert_array_equal(got, want)
 
 
-def test_topk_ragged_varlen_and_spans():
+@pytest.mark.parametrize("chunked", [False, True], ids=["fit", "chunked"])
+def test_topk_ragged_varlen_and_spans(chunked):
     r = np.random.default_rng(7)
     lens = [1, 0, 2, 63, 64, 65, 4095, 4096, 4097, 9000, 1, 17]
     spans, ks = [], []
@@ -195,18 +210,19 @@ def test_topk_ragged_varlen_and_spans():
     s = np.round(r.standard_normal(cu[-1]) * 4).astype(np.float32) / 4  # many ties
     b = [x for x, _ in spans]
     e = [y for _, y in spans]
-    _print_case("topk ragged varlen")
-    got, _ = _topk_gpu(s, cu, b, e, ks)
+    _print_case(f"topk ragged varlen chunked={chunked}")
+    got, _ = _topk_gpu(s, cu, b, e, ks, chunked)
     want, _ = oracle.topk_select(s, cu, b, e, ks)
     np.testing.assert_array_equal(got, want)
 
 
-def test_topk_deterministic_repeat():
+@pytest.mark.parametrize("chunked", [False, True], ids=["fit", "chunked"])
+def test_topk_deterministic_repeat(chunked):
     w = workloads.varlen()
     s = w.topk_scores()
-    _print_case("topk repeat")
-    a, _ = _topk_gpu(s, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
-    b, _ = _topk_gpu(s, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+    _print_case(f"topk repeat chunked={chunked}")
+    a, _ = _topk_gpu(s, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr, chunked)
+    b, _ = _topk_gpu(s, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr, chunked)
     np.testing.assert_array_equal(a, b)
 
 
@@ -214,43 +230,59 @@ def test_topk_reused_workspace():
     """One workspace, filled with garbage once, serves a run of calls on
     different workloads (sequence counts and lengths change the workspace
     layout; plain and random-K selectors alternate): every call zeroes the
-    counters it needs, so each one is bit-exact against the oracle."""
+    counters it needs, so each one is bit-exact against the oracle.  Calls
+    alternate between the one-workgroup and the chunked selector (every other
+    call gets the appended long sequence)."""
     _print_case("topk reused workspace")
-    names = ["varlen", "tiny", "16k", "32k@5%", "varlen", "16k"]
-    ws_bytes = max(max(tg.tg_topk_workspace_bytes(workloads.by_name(n).n_seqs, workloads.by_name(n).n_tokens,
-                                                  int(max(workloads.by_name(n).seqlens))),
-                       tg.tg_random_k_workspace_bytes(workloads.by_name(n).n_seqs, workloads.by_name(n).n_tokens,
-                                                      int(max(workloads.by_name(n).seqlens))))
-                   for n in set(names))
+    names = ["varlen", "tiny", "16k", "32k@5%", "varlen", "16k", "tiny"]
+
+    def inputs(name, chunked):
+        w = workloads.by_name(name)
+        a = (w.topk_scores(), w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+        return workloads.pad_long_sequence(*a) if chunked else a
+
+    ws_bytes = 0
+    for name in set(names):
+        for c in (False, True):
+            _, cu, *_ = inputs(name, c)
+            ns, nt, mx = len(cu) - 1, int(cu[-1]), _max_seqlen(cu)
+            ws_bytes = max(ws_bytes, tg.tg_topk_workspace_bytes(ns, nt, mx), tg.tg_random_k_workspace_bytes(ns, nt, mx))
     ws = torch.full((ws_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
     for rep, name in enumerate(names):
         w = workloads.by_name(name)
-        s = w.topk_scores()
-        ck = tg.tg_kept_counts(w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
-        meta = [_i32(a) for a in (w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr, ck)]
-        mx = int(max(w.seqlens))
+        m0 = int(tg.tg_kept_counts(w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)[-1])
+        s, cu, b, e, k = inputs(name, rep % 2 == 1)
+        ck = tg.tg_kept_counts(cu, b, e, k)
+        meta = [_i32(a) for a in (cu, b, e, k, ck)]
+        mx = _max_seqlen(cu)
         kept = tg.tg_topk_select(_dev(s), *meta, int(ck[-1]), mx, workspace=ws)
         seed = 1000 + rep
-        kept_r = tg.tg_random_k_select(seed, *meta, w.n_tokens, int(ck[-1]), mx, workspace=ws)
+        kept_r = tg.tg_random_k_select(seed, *meta, int(cu[-1]), int(ck[-1]), mx, workspace=ws)
         torch.cuda.synchronize()
-        ref, _ = oracle.topk_select(s, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
-        np.testing.assert_array_equal(kept.cpu().numpy(), ref, err_msg=f"call {rep} ({name})")
+        ref, _ = oracle.topk_select(w.topk_scores(), w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+        np.testing.assert_array_equal(kept.cpu().numpy()[:m0], ref, err_msg=f"call {rep} ({name})")
         ref_r, _ = oracle.random_k_select(seed, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
-        np.testing.assert_array_equal(kept_r.cpu().numpy(), ref_r, err_msg=f"random-K call {rep} ({name})")
+        np.testing.assert_array_equal(kept_r.cpu().numpy()[:m0], ref_r, err_msg=f"random-K call {rep} ({name})")
 
 
 # ----------------------------------------------------------------- gather ----
-@pytest.mark.parametrize("name,seed", [("tiny", 0), ("16k", 1), ("128k", 2), ("varlen", 3), ("32k@25%", 2 ** 64 - 1)])
-def test_random_k_bit_exact(name, seed):
+@pytest.mark.parametrize("name,seed,chunked", [("tiny", 0, False), ("16k", 1, False), ("128k", 2, False),
+                                                ("varlen", 3, False), ("32k@25%", 2 ** 64 - 1, False),
+                                                ("16k", 5, True), ("varlen", 6, True)])
+def test_random_k_bit_exact(name, seed, chunked):
     """Random-K selector mode: bit-exact against the oracle's SplitMix64 scores
     and selector, every config shape, seeds up to 2^64 - 1."""
-    _print_case(f"random-K {name} seed={seed}")
+    _print_case(f"random-K {name} seed={seed} chunked={chunked}")
     w = workloads.by_name(name)
     kept_ref, ck = oracle.random_k_select(seed, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
-    kept = tg.tg_random_k_select(seed, _i32(w.cu_seqlens), _i32(w.doc_begin), _i32(w.doc_end), _i32(w.k_doc_arr),
-                                 _i32(ck), w.n_tokens, int(ck[-1]), int(max(w.seqlens)))
+    meta = (w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+    if chunked:   # the draws depend on the global token index only, so padding at the end keeps them
+        _, *meta = workloads.pad_long_sequence(None, *meta)
+    ckp = tg.tg_kept_counts(*meta)
+    kept = tg.tg_random_k_select(seed, *[_i32(a) for a in meta], _i32(ckp), int(meta[0][-1]), int(ckp[-1]),
+                                 _max_seqlen(meta[0]))
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(kept.cpu().numpy(), kept_ref)
+    np.testing.assert_array_equal(kept.cpu().numpy()[:int(ck[-1])], kept_ref)
 
 
 @pytest.mark.parametrize("seed", [3, 2 ** 64 - 2])

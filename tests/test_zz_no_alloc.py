@@ -19,11 +19,17 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def _select_both(w, scores_np):
-    ck = tg.tg_kept_counts(w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
-    meta = [_dev(np.asarray(a, dtype=np.int32)) for a in (w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr, ck)]
+def _select_both(w, scores_np, chunked):
+    """chunked: append one 65537-token sequence, so that the chunked selector,
+    whose counters and candidate lists live in the scratch array, runs instead
+    of the one-workgroup selector (which needs no scratch)."""
+    a = (scores_np, w.cu_seqlens, w.doc_begin, w.doc_end, w.k_doc_arr)
+    scores_np, *meta = workloads.pad_long_sequence(*a) if chunked else a
+    ck = tg.tg_kept_counts(*meta)
+    mx = int(np.diff(np.asarray(meta[0])).max())
+    meta = [_dev(np.asarray(x, dtype=np.int32)) for x in (*meta, ck)]
     s = _dev(np.asarray(scores_np, dtype=np.float32))
-    m, mx = int(ck[-1]), int(max(w.seqlens))
+    m = int(ck[-1])
     ref = tg.tg_topk_select(s, *meta, m, mx)
     out = torch.full((m,), -7, dtype=torch.int32, device="cuda")
     got = tg.tg_topk_select_noalloc(s, *meta, m, mx, kept_idx=out)
@@ -33,13 +39,14 @@ def _select_both(w, scores_np):
 
 
 def test_noalloc_matches_workspace_entry_two_calls():
-    """varlen (8 sequences, ties at the threshold), then 16k (one sequence):
-    bit-exact against tg_topk_select both times."""
+    """varlen (8 sequences, ties at the threshold), then 16k (one sequence),
+    both through the chunked selector and its scratch, then 16k through the
+    one-workgroup selector: bit-exact against tg_topk_select every time."""
     print("[case] noalloc varlen then 16k", flush=True)
-    for name in ("varlen", "16k"):
+    for name, chunked in (("varlen", True), ("16k", True), ("16k", False)):
         w = workloads.by_name(name)
-        ref, got = _select_both(w, w.topk_scores())
-        np.testing.assert_array_equal(got, ref, err_msg=name)
+        ref, got = _select_both(w, w.topk_scores(), chunked)
+        np.testing.assert_array_equal(got, ref, err_msg=f"{name} chunked={chunked}")
 
 
 def test_noalloc_rejects_beyond_its_array():

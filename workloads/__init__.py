@@ -251,3 +251,24 @@ def custom(seqlens, q_lens, k_doc, d_model=256, d_hid=64, x_dtype="bf16", n_q_he
     return Workload(name="custom", seed=seed, seqlens=list(seqlens), q_lens=list(q_lens),
                     k_doc=list(k_doc), d_model=d_model, d_hid=d_hid, x_dtype=x_dtype,
                     n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim, **kw)
+
+
+LONG_PAD = 65537   # far above the 16 Ki tokens up to which the one-workgroup selector runs
+
+
+def pad_long_sequence(scores, cu_seqlens, doc_begin, doc_end, k_doc, n=LONG_PAD, seed=99):
+    """The same selector input with one sequence of n tokens appended (its
+    whole length a document, 1% budget, N(0,1) fp32 scores).  The original
+    tokens keep their indices and, since kept indices are stored sequence by
+    sequence, their kept list is the first part of the padded call's output.
+    Used to send small inputs through the chunked selector (max_seqlen > 16 Ki).
+    scores may be None (random-K mode draws its own)."""
+    n0 = int(np.asarray(cu_seqlens)[-1])
+    cu = np.concatenate([np.asarray(cu_seqlens, np.int64), [n0 + n]]).astype(np.int32)
+    b = np.concatenate([np.asarray(doc_begin, np.int64), [0]]).astype(np.int32)
+    e = np.concatenate([np.asarray(doc_end, np.int64), [n]]).astype(np.int32)
+    k = np.concatenate([np.asarray(k_doc, np.int64), [n // 100]]).astype(np.int32)
+    if scores is not None:
+        extra = np.random.default_rng(seed).standard_normal(n).astype(np.float32)
+        scores = np.concatenate([np.asarray(scores, np.float32), extra])
+    return scores, cu, b, e, k
