@@ -127,8 +127,9 @@ size_t tg_topk_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32_t m
  *   max_seqlen    host upper bound of every n_s (sizes the grid); at most 4 Mi
  *                 tokens and at most n_tokens_total.  Up to 16 Ki tokens the
  *                 call is one launch of one workgroup per sequence (the
- *                 workspace is then not touched), beyond that four launches
- *                 over token chunks; both give the same result.
+ *                 workspace is then not touched), up to 64 Ki two launches,
+ *                 beyond that four launches over token chunks; all give the
+ *                 same result.
  *   workspace     [device] >= tg_topk_workspace_bytes(...) bytes, 256-byte
  *                 aligned, contents need not be initialised (the call's first
  *                 kernel zeroes the counters it needs).  Calls that share a

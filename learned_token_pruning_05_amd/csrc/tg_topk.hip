@@ -10,9 +10,9 @@
 // and +0 share a key; NaN is key 0, below -inf).  Per sequence the selector
 // needs the key T of the K_eff-th document token and r, the number of tokens
 // with key == T that are kept (the r lowest-indexed ones).  A batch whose
-// sequences all fit in 16 Ki tokens takes one launch (S, below: one workgroup
-// per sequence).  Longer sequences take four launches, with no cross-workgroup
-// waiting:
+// sequences all fit in 16 Ki tokens takes one launch, in 64 Ki tokens two (S,
+// below: one workgroup per sequence finds T and r, then W).  Longer sequences
+// take four launches, with no cross-workgroup waiting:
 //   C  zero the per-sequence counters (histogram, tickets, list length): a
 //      kernel, not a memset, so that the call can be captured into a graph
 //      and replayed;
@@ -512,53 +512,59 @@ __global__ __launch_bounds__(kWriteThreads) void topk_write_kernel(
 }
 
 // ------------------------------------------------------------------ S ----
-// Sequences of at most 16 Ki tokens: one 1024-thread workgroup per sequence
-// does the whole selection in one launch (the chunked passes above spread
-// longer sequences over many CUs, which pays from about 32 Ki tokens on).
-// Wave w holds tokens [64 E w, 64 E (w+1)) in registers, item e of lane l
-// being token 64 (E w + e) + l, so the thread order is the token order.  An
-// item holds the score key of a document token, else 0xffffffff, above every
-// score key (a token outside the document is always kept; an item past the
-// end of the sequence comes after every real token, so it never takes a real
-// slot).  Three radix passes (11, 11 and 10 bits) over LDS histograms of the
-// document keys give T and r; then "key > T" marks the always-kept and
-// "key == T" the tie tokens, and per-wave counts plus a scan over the 16 waves
-// give every kept token its slot, as in the write pass.
+// Sequences of at most 64 Ki tokens: one 1024-thread workgroup per sequence
+// holds the sequence's keys in registers and finds T and r itself.  Wave w
+// holds tokens [64 E w, 64 E (w+1)), item e of lane l being token
+// 64 (E w + e) + l, so the thread order is the token order.  An item holds
+// the score key of a document token, else 0xffffffff, above every score key
+// (a token outside the document is always kept; an item past the end of the
+// sequence comes after every real token, so it never takes a real slot).
+// Three radix passes (11, 11 and 10 bits) over LDS histograms of the document
+// keys give T and r.
+//   - Up to 16 Ki tokens the same workgroup then places the kept tokens:
+//     "key > T" and "key == T" ballots, per-wave counts and a scan over the 16
+//     waves give every kept token its slot, as in the write pass.  One launch.
+//   - Up to 64 Ki tokens it writes T, r and the per-chunk output offsets (a
+//     wave's items are one or two 2048-token chunks) and the write pass W
+//     places the tokens: two launches.  Placing 32-64 tokens per lane on one
+//     CU would cost more than the second launch.
+// Longer sequences take the chunked passes above, which spread the histogram
+// over many CUs.
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / 64;
-constexpr int kSmallMax = kSmallThreads * 16;   // 16 Ki tokens
+constexpr int kSmallMax = kSmallThreads * 16;   // 16 Ki tokens: one launch
+constexpr int kMidMax = kSmallThreads * 64;     // 64 Ki tokens: two launches
+constexpr uint32_t kOutKey = 0xffffffffu;       // no score key is this large (+inf is 0xff800000)
 
+struct SmallLds {
+    uint32_t h[2048 + 64];   // bins, then one sink slot per lane
+    uint32_t sh_scan[kSmallWaves];
+    uint32_t sh_out[2];
+    uint32_t cnt[2][2 * kSmallWaves];
+};
+
+// Keys of the workgroup's sequence (layout above) and (T, r) such that
+// "key > T, or key == T among the first r" keeps exactly the sequence's
+// tokens: the radix passes when the document is pruned; T = 0, r = all when
+// the whole document is kept (NaN scores have key 0); T = 0xfffffffe, r = 0
+// when none of it is (no score key equals that).  T and r come back uniform.
 template <int E>
-__global__ __launch_bounds__(kSmallThreads) void topk_small_kernel(
-    const float* __restrict__ scores, const int* __restrict__ cu, const int* __restrict__ db,
-    const int* __restrict__ de, const int* __restrict__ kd, const int* __restrict__ cu_kept,
-    int* __restrict__ kept_idx) {
-    __shared__ uint32_t h[2048];
-    __shared__ uint32_t sh_scan[kSmallWaves];
-    __shared__ uint32_t sh_out[2];
-    __shared__ uint32_t wcnt[2][kSmallWaves];
-    const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const SeqInfo q(s, cu, db, de, kd);
-    if (q.n <= 0) return;
-    const float* sc = scores + q.start;
-    const int first = w * E * 64 + lane;   // token of item 0; item e adds 64 e
-    constexpr uint32_t kOut = 0xffffffffu;  // no score key is this large (+inf is 0xff800000)
-
-    // every load unconditional (clamped to the last token), all in flight at once
-    uint32_t key[E];
+__device__ __forceinline__ void small_select(const SeqInfo& q, const float* __restrict__ sc, int first,
+                                             uint32_t (&key)[E], SmallLds& L, uint32_t* T_out, uint32_t* r_out) {
+    const int tid = threadIdx.x;
+    // every load unconditional, all in flight at once: a buffer resource over
+    // the sequence's scores reads zeros past its end, and one offset register
+    // serves every item (item e adds 256 e bytes as the scalar offset)
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sc, (uint32_t)q.n * 4u);
 #pragma unroll
-    for (int e = 0; e < E; ++e) key[e] = __float_as_uint(sc[min(first + 64 * e, q.n - 1)]);
+    for (int e = 0; e < E; ++e)
+        key[e] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, first * 4, 256 * e, 0);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int i = first + 64 * e;
-        key[e] = i >= q.db && i < q.de ? score_key(__uint_as_float(key[e])) : kOut;
+        const uint32_t dm = 0u - (uint32_t)(i >= q.db && i < q.de);   // all ones for a document token
+        key[e] = (score_key(__uint_as_float(key[e])) & dm) | ~dm;     // else kOutKey
     }
-
-    // (T, r) such that "key > T, or key == T among the first r" keeps exactly
-    // the sequence's tokens: T = 0, r = all when the whole document is kept
-    // (NaN scores have key 0); T = 0xfffffffe, r = 0 when none of it is (no
-    // score key equals that)
     uint32_t T, r;
     if (q.needs_select()) {
         uint32_t rem = (uint32_t)q.k, prefix = 0, pmask = 0;
@@ -566,15 +572,21 @@ __global__ __launch_bounds__(kSmallThreads) void topk_small_kernel(
         for (int pass = 0; pass < 3; ++pass) {
             const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
             const uint32_t nbm = pass < 2 ? 2047u : 1023u;
-            for (int i = tid; i < 2048; i += kSmallThreads) h[i] = 0u;
+            for (int i = tid; i < 2048; i += kSmallThreads) L.h[i] = 0u;
             __syncthreads();
+            // a lane whose item is not counted adds to a slot of its own past
+            // the bins: no branch, and no pile-up on one address.  After the
+            // first pass the prefix test alone excludes 0xffffffff: its top
+            // 11 bits (2047) are above those of every score key (+inf: 2044).
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                if (key[e] != kOut && (key[e] & pmask) == prefix) atomicAdd(&h[(key[e] >> shift) & nbm], 1u);
+            for (int e = 0; e < E; ++e) {
+                const bool act = pass == 0 ? key[e] != kOutKey : (key[e] & pmask) == prefix;
+                atomicAdd(&L.h[act ? (key[e] >> shift) & nbm : 2048u + (tid & 63)], 1u);
+            }
             __syncthreads();
             uint32_t bk, ab;
-            if (pass < 2) find_bucket<2048, kSmallThreads>(h, rem, sh_scan, sh_out, &bk, &ab);
-            else find_bucket<1024, kSmallThreads>(h, rem, sh_scan, sh_out, &bk, &ab);
+            if (pass < 2) find_bucket<2048, kSmallThreads>(L.h, rem, L.sh_scan, L.sh_out, &bk, &ab);
+            else find_bucket<1024, kSmallThreads>(L.h, rem, L.sh_scan, L.sh_out, &bk, &ab);
             rem -= ab;
             prefix |= bk << shift;
             pmask |= nbm << shift;
@@ -588,9 +600,25 @@ __global__ __launch_bounds__(kSmallThreads) void topk_small_kernel(
         T = 0xfffffffeu;
         r = 0u;
     }
+    *T_out = __builtin_amdgcn_readfirstlane(T);
+    *r_out = __builtin_amdgcn_readfirstlane(r);
+}
 
-    T = __builtin_amdgcn_readfirstlane(T);
-    r = __builtin_amdgcn_readfirstlane(r);
+template <int E>
+__global__ __launch_bounds__(kSmallThreads) void topk_small_kernel(
+    const float* __restrict__ scores, const int* __restrict__ cu, const int* __restrict__ db,
+    const int* __restrict__ de, const int* __restrict__ kd, const int* __restrict__ cu_kept,
+    int* __restrict__ kept_idx) {
+    __shared__ SmallLds L;
+    const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const SeqInfo q(s, cu, db, de, kd);
+    if (q.n <= 0) return;
+    const int first = w * E * 64 + lane;   // token of item 0; item e adds 64 e
+    uint32_t key[E];
+    uint32_t T, r;
+    small_select<E>(q, scores + q.start, first, key, L, &T, &r);
+
     // T is re-made opaque for every item, so each item's two compares stay
     // next to their use instead of 2E lane masks being computed up front
     // (they would spill)
@@ -602,14 +630,14 @@ __global__ __launch_bounds__(kSmallThreads) void topk_small_kernel(
         nb += (uint32_t)__popcll(__ballot(key[e] == T));
     }
     if (lane == 0) {
-        wcnt[0][w] = na;
-        wcnt[1][w] = nb;
+        L.cnt[0][w] = na;
+        L.cnt[1][w] = nb;
     }
     __syncthreads();
     uint32_t ba = 0, bb = 0;
     for (int x = 0; x < w; ++x) {
-        ba += wcnt[0][x];
-        bb += wcnt[1][x];
+        ba += L.cnt[0][x];
+        bb += L.cnt[1][x];
     }
     int* __restrict__ out = kept_idx + cu_kept[s];
     const uint32_t m_s = (uint32_t)(cu_kept[s + 1] - cu_kept[s]);
@@ -625,6 +653,62 @@ __global__ __launch_bounds__(kSmallThreads) void topk_small_kernel(
         if ((fa || (fb && pb < r)) && slot < m_s) out[slot] = q.start + first + 64 * e;
         ba += (uint32_t)__popcll(ma);
         bb += (uint32_t)__popcll(mb);
+    }
+}
+
+// T, r and the per-chunk output offsets of a pruned sequence of up to 64 Ki
+// tokens, for the write pass.  A wave's 64 E tokens are E / 32 whole chunks.
+template <int E>
+__global__ __launch_bounds__(kSmallThreads) void topk_mid_kernel(
+    const float* __restrict__ scores, const int* __restrict__ cu, const int* __restrict__ db,
+    const int* __restrict__ de, const int* __restrict__ kd, int nch_write, SeqState* __restrict__ st,
+    uint32_t* __restrict__ base_a, uint32_t* __restrict__ base_b) {
+    constexpr int CPW = E * 64 / kChunk;   // chunks per wave
+    static_assert(CPW * kChunk == E * 64 && CPW * kSmallWaves <= 2 * kSmallWaves, "whole chunks per wave");
+    __shared__ SmallLds L;
+    const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const SeqInfo q(s, cu, db, de, kd);
+    if (!q.needs_select()) return;   // the write pass places these from the spans alone
+    const int first = w * E * 64 + lane;
+    uint32_t key[E];
+    uint32_t T, r;
+    small_select<E>(q, scores + q.start, first, key, L, &T, &r);
+    // per chunk: always-kept tokens (key > T) and ties (key == T); items past
+    // the end only ever count in the sequence's last chunk
+    // (per-lane counts, then one sum over the wave: no lane masks kept alive)
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        uint32_t na = 0, nb = 0;
+#pragma unroll
+        for (int e = c * (E / CPW); e < (c + 1) * (E / CPW); ++e) {
+            na += (uint32_t)(key[e] > T);
+            nb += (uint32_t)(key[e] == T);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            na += __shfl_xor(na, o, 64);
+            nb += __shfl_xor(nb, o, 64);
+        }
+        if (lane == 0) {
+            L.cnt[0][w * CPW + c] = na;
+            L.cnt[1][w * CPW + c] = nb;
+        }
+    }
+    __syncthreads();
+    const int nch = (q.n + kChunk - 1) / kChunk;
+    if (tid < nch) {
+        uint32_t ba = 0, bb = 0;
+        for (int x = 0; x < tid; ++x) {
+            ba += L.cnt[0][x];
+            bb += L.cnt[1][x];
+        }
+        base_a[(int64_t)s * nch_write + tid] = ba;
+        base_b[(int64_t)s * nch_write + tid] = bb;
+    }
+    if (tid == 0) {
+        st[s].T = T;
+        st[s].r = (int32_t)r;
     }
 }
 
@@ -740,7 +824,16 @@ int launch_topk(const float* scores, int n_seqs, int64_t n_tokens, int max_seqle
     }
     const TopkPtrs P = topk_ptrs(ws, n_seqs, n_tokens, max_seqlen);
     const int nch_w = (max_seqlen + kChunk - 1) / kChunk;
-    launch_select_passes(scores, n_seqs, max_seqlen, cu_seqlens, doc_begin, doc_end, k_doc, P, stm);
+    if (max_seqlen <= kMidMax) {
+        if (max_seqlen <= kMidMax / 2)
+            hipLaunchKernelGGL(topk_mid_kernel<32>, dim3(n_seqs), dim3(kSmallThreads), 0, stm, scores, cu_seqlens,
+                               doc_begin, doc_end, k_doc, nch_w, P.st, P.ba, P.bb);
+        else
+            hipLaunchKernelGGL(topk_mid_kernel<64>, dim3(n_seqs), dim3(kSmallThreads), 0, stm, scores, cu_seqlens,
+                               doc_begin, doc_end, k_doc, nch_w, P.st, P.ba, P.bb);
+    } else {
+        launch_select_passes(scores, n_seqs, max_seqlen, cu_seqlens, doc_begin, doc_end, k_doc, P, stm);
+    }
     hipLaunchKernelGGL(topk_write_kernel, dim3(nch_w, n_seqs), dim3(kWriteThreads), 0, stm, scores, cu_seqlens,
                        doc_begin, doc_end, k_doc, cu_kept, nch_w, (const SeqState*)P.st, (const uint32_t*)P.ba,
                        (const uint32_t*)P.bb, kept_idx);

@@ -109,11 +109,12 @@ def test_gate_strided_rows():
 
 
 # ------------------------------------------------------------------ top-K ----
-# Batches whose sequences all fit in 16 Ki tokens take the one-workgroup
-# selector.  chunked=True appends one 65537-token sequence
-# (workloads.pad_long_sequence), which sends the whole batch through the
-# chunked four-launch selector; the original sequences' kept indices are the
-# first part of its output.  Both selectors are checked on the small cases.
+# Batches whose sequences all fit in 16 Ki tokens take the one-launch
+# selector, in 64 Ki tokens the two-launch one.  chunked=True appends one
+# 65537-token sequence (workloads.pad_long_sequence), which sends the whole
+# batch through the chunked four-launch selector; the original sequences' kept
+# indices are the first part of its output.  So every small case is checked
+# through two forms of the selector.
 def _max_seqlen(cu):
     lens = np.diff(np.asarray(cu))
     return int(lens.max()) if lens.size else 0
@@ -166,6 +167,11 @@ def _edge_scores():
     yield "nan-heavy", np.where(r.random(2000) < 0.7, np.float32(np.nan), r.standard_normal(2000)).astype(np.float32)
     yield "few-values", r.integers(-3, 3, 70000).astype(np.float32)
     yield "normal", r.standard_normal(131072).astype(np.float32)
+    # between 16 Ki and 64 Ki tokens (the selector's two-launch form)
+    yield "all-equal-mid", np.full(20000, -1.5, np.float32)
+    yield "nan-heavy-mid", np.where(r.random(30000) < 0.7, np.float32(np.nan), r.standard_normal(30000)).astype(np.float32)
+    yield "few-values-mid", r.integers(-3, 3, 40000).astype(np.float32)
+    yield "specials-mid", r.choice(specials, 65536).astype(np.float32)
 
 
 @pytest.mark.parametrize("chunked", [False, True], ids=["fit", "chunked"])
