@@ -255,7 +255,10 @@ int tg_gated_select(const void* x, int32_t x_dtype, int64_t n_tokens_total, int3
                     size_t workspace_bytes, void* stream);
 
 /* Workspace bytes tg_keybias_attn_prefill (and tg_attn_prepare / tg_attn_forward)
- * need for these sizes. */
+ * need for these sizes: the kept-only cache, plus, for 1024 or more kept
+ * tokens with ceil(n_kept_total / 64) * n_kv_heads <= 512, the forward's
+ * key-split scratch (512 tickets and 512 partial slots of 256 (D/2 + 2)
+ * floats: 34.6 MB for D = 128, 17.8 MB for D = 64). */
 size_t tg_attn_workspace_bytes(int32_t n_seqs, int64_t n_kept_total, int32_t n_kv_heads,
                                int32_t head_dim);
 
@@ -327,8 +330,13 @@ int tg_attn_prepare(const void* k, const void* v, int64_t kv_row_stride, const f
  * max_kept_seqlen, n_q_heads, out, lse as there).  cu_kept, n_seqs,
  * n_kept_total, n_kv_heads, head_dim and rope_base must equal those of the
  * tg_attn_prepare call that filled the workspace, and that call must precede
- * this one in stream order; otherwise the results are undefined.  The
- * workspace is only read.
+ * this one in stream order; otherwise the results are undefined.  The cache
+ * is only read.  A grid of at most two workgroups per CU may cut its long
+ * query tiles into key chunks whose partials go to the workspace's key-split
+ * scratch and are merged by the last chunk to finish; the chunk tickets there
+ * are zeroed by tg_attn_prepare and left at zero by every forward.  So
+ * forwards that share a workspace must not overlap, and the results are
+ * deterministic.
  */
 int tg_attn_forward(const void* q, int64_t q_row_stride, const float* head_gain, float tau,
                     const int32_t* cu_kept, int32_t n_seqs, int64_t n_kept_total,

@@ -406,8 +406,8 @@ int attn_check(bool q_side, const void* q, int64_t q_row_stride, int32_t max_kep
 
 void attn_fill(AttnArgs& a, int32_t n_seqs, int64_t n_kept_total, int32_t n_kv_heads,
                int32_t head_dim, double rope_base, const void* workspace) {
-    size_t off_k, off_vt, off_cs;
-    attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, &off_k, &off_vt, &off_cs);
+    size_t off_k, off_vt, off_cs, off_split;
+    attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, &off_k, &off_vt, &off_cs, &off_split);
     a.n_seqs = n_seqs;
     a.m_tot = n_kept_total;
     a.hkv = n_kv_heads;
@@ -419,6 +419,8 @@ void attn_fill(AttnArgs& a, int32_t n_seqs, int64_t n_kept_total, int32_t n_kv_h
     a.ws_vt = (bf16*)(ws + off_vt);
     a.ws_cs = (float2*)(ws + off_cs);
     a.mp = attn_padded_rows(n_seqs, n_kept_total);
+    a.ws_tk = off_split ? (uint32_t*)(ws + off_split) : nullptr;
+    a.ws_part = off_split ? (float*)(ws + off_split + (((size_t)kSplitCap * 4 + 255) & ~(size_t)255)) : nullptr;
 }
 
 }  // namespace

@@ -38,6 +38,13 @@
 //     tile max and rescales O and l (the result is exact either way).  The
 //     loop is a three-stage pipeline (QK of tile j+2 || exponentials of tile
 //     j+1 || P.V of tile j), described at the kernel.
+//     Grids of at most two workgroups per CU start whole and pair block k
+//     with block n_cu + k on one CU; there the second round runs its query
+//     tiles in reverse (largest with smallest), and the longest query tiles
+//     may be cut into key chunks (a plan fitted to measured kernel times
+//     picks the chunk length): each chunk leaves its unnormalised partial
+//     in the workspace's key-split scratch and the last one to finish merges
+//     them in chunk order.
 //     All q heads of a KV group that fit in the workgroup share each K/V tile.
 //     Causality uses the kept order (positions increase within a sequence, so
 //     pos_j <= pos_i  <=>  j <= i).  Blocks are ordered head-fastest so that,
@@ -47,6 +54,11 @@
 //     sequences at a time, which stay in its L2 (interleaving the sequences
 //     made packed batches re-fetch about 4x the read-once bytes).
 #include <math.h>
+
+#include <algorithm>
+#include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "tg_common.hpp"
 
@@ -61,8 +73,13 @@ int64_t attn_padded_rows(int n_seqs, int64_t m_tot) {
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Partial of one key-split forward workgroup: per lane its O^T accumulators
+// (D / 2 floats), then its offset and sum, lane-fastest so that stores and
+// loads are whole 256-B rows.
+static size_t split_slot_floats(int d) { return (size_t)4 * 64 * (d / 2 + 2); }
+
 size_t attn_workspace_layout(int n_seqs, int64_t m_tot, int hkv, int d, size_t* off_k,
-                             size_t* off_vt, size_t* off_cs) {
+                             size_t* off_vt, size_t* off_cs, size_t* off_split) {
     const int64_t mp = attn_padded_rows(n_seqs, m_tot);
     const size_t kb = align256((size_t)hkv * mp * (d + 16) * 2);
     const size_t vb = align256((size_t)hkv * mp * d * 2);
@@ -70,7 +87,13 @@ size_t attn_workspace_layout(int n_seqs, int64_t m_tot, int hkv, int d, size_t* 
     if (off_k) *off_k = 0;
     if (off_vt) *off_vt = kb;
     if (off_cs) *off_cs = kb + vb;
-    return kb + vb + cb;
+    // key-split scratch, only where a forward grid can be small enough to
+    // split (at most kSplitCap workgroups even with one per 64 rows and kv
+    // head) and long enough for splitting to pay (1024 kept tokens or more)
+    const bool split = m_tot >= 1024 && ((m_tot + 63) / 64) * hkv <= kSplitCap;
+    const size_t sb = split ? align256((size_t)kSplitCap * 4) + (size_t)kSplitCap * split_slot_floats(d) * 4 : 0;
+    if (off_split) *off_split = split ? kb + vb + cb : 0;
+    return kb + vb + cb + sb;
 }
 
 namespace {
@@ -108,7 +131,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
     const bf16* __restrict__ k, const bf16* __restrict__ v, int64_t kv_stride,
     const float* __restrict__ key_score, const int* __restrict__ pos, const int* __restrict__ cu_kept,
     int n_seqs, int64_t m_tot, int hkv, int64_t mp, RopeFreqs fr, int rope, bf16* __restrict__ ws_k,
-    bf16* __restrict__ ws_vt, float2* __restrict__ ws_cs) {
+    bf16* __restrict__ ws_vt, float2* __restrict__ ws_cs, uint32_t* __restrict__ ws_tk) {
     constexpr int HALF = D / 2, KD = D + kExtra, NPAIR = D / 16, NC8 = D / 8;
     // V^T tile: row d holds the 64 columns vt_col(r) of this tile; 8-column
     // groups are XOR-swizzled by (d / 8) % 8 so the transposing 2-byte writes
@@ -118,6 +141,8 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
     const int tid = threadIdx.x;
     const int h = blockIdx.y;
     const int64_t p0 = (int64_t)blockIdx.x * 64;
+    if (ws_tk && blockIdx.x == 0 && h == 0)
+        for (int i = tid; i < kSplitCap; i += 256) ws_tk[i] = 0u;   // the forward's split tickets
     if (tid < 64) {
         // last sequence whose padded start is <= row (or 0), then the token
         const int64_t r = p0 + tid;
@@ -262,7 +287,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
     const bf16* __restrict__ q, int64_t q_stride, const bf16* __restrict__ ws_k,
     const bf16* __restrict__ ws_vt, const float2* __restrict__ ws_cs, int rope,
     const float* __restrict__ gain, float qk_scale_log2, const int* __restrict__ cu_kept, int n_seqs,
-    int64_t m_tot, int64_t mp, int hq, int grp, int n_qtiles, int n_hblk, bf16* __restrict__ out,
+    int64_t m_tot, int64_t mp, int hq, int grp, int n_qtiles, int n_hblk, int round2, int split_c,
+    int units_per_seq, int max_kept, uint32_t* __restrict__ tk, float* __restrict__ part, bf16* __restrict__ out,
     float* __restrict__ lse) {
     using L = AttnLds<D>;
     constexpr int WB = NW / HW;
@@ -277,11 +303,40 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int il = lane & 31, half = lane >> 5;
 
-    const int b = blockIdx.x;
+    // With round2 > 0 the whole grid is resident at once, two workgroups per
+    // CU, and the dispatcher gives block round2 + k the CU of block k: the
+    // second round takes its query tiles in reverse, so the CU with the
+    // largest tile of the first round gets the smallest of the second.
+    int b = blockIdx.x;
+    if (round2 > 0 && b >= round2) {
+        const int nu = (int)(gridDim.x - round2) / n_hblk;
+        const int u = (b - round2) / n_hblk;
+        b = round2 + (nu - 1 - u) * n_hblk + (b - round2) % n_hblk;
+    }
     const int hidx = b % n_hblk;
     const int rest = b / n_hblk;
-    const int s = rest / n_qtiles;
-    const int qt = n_qtiles - 1 - rest % n_qtiles;
+    // Unit `rest` of the grid: a query tile, or with split_c > 0 one key chunk
+    // of it.  Per sequence the query tiles come largest first, each with the
+    // chunks the longest sequence needs there (its n key tiles cut into
+    // ceil(n / split_c) nearly equal runs); r0 is the tile's first unit.
+    int s, qt, chunk = 0, r0 = rest;
+    if (split_c == 0) {
+        s = rest / n_qtiles;
+        qt = n_qtiles - 1 - rest % n_qtiles;
+    } else {
+        s = rest / units_per_seq;
+        int u = rest % units_per_seq;
+        qt = n_qtiles - 1;
+        for (;;) {
+            const int nkf = (min((qt + 1) * BMT, max_kept) + kBN - 1) / kBN;
+            const int ncf = (nkf + split_c - 1) / split_c;
+            if (u < ncf) break;
+            u -= ncf;
+            --qt;
+        }
+        chunk = u;
+        r0 = rest - u;
+    }
     const int cs0 = cu_kept[s];
     const int ms = cu_kept[s + 1] - cs0;
     const int q0 = qt * BMT;
@@ -295,7 +350,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
     const bool qvalid = qi < ms;
     const int64_t prow0 = padded_seq_start(cs0, s);
     const int kend = min(ms, q0 + BMT);
-    const int n_kt = (kend + kBN - 1) / kBN;
+    const int n_kt_all = (kend + kBN - 1) / kBN;
+    // this workgroup's key tiles [kt0, kt0 + n_kt), keys from jb; with
+    // split_c >= 2 every chunk starts at or before the tile of the query
+    // tile's first row, so every row sees key jb (it sets the offset)
+    int kt0 = 0, n_kt = n_kt_all, nc = 1;
+    if (split_c > 0) {
+        nc = (n_kt_all + split_c - 1) / split_c;
+        if (chunk >= nc) return;
+        kt0 = chunk * n_kt_all / nc;
+        n_kt = (chunk + 1) * n_kt_all / nc - kt0;
+    }
+    const int jb = kt0 * kBN;
 
     bf16x8 qf[KS + 1];
     {
@@ -358,9 +424,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
     // this head's K' rows and V^T columns from the sequence start, as buffer
     // resources: 32-bit per-lane offsets, the tile offset in a scalar register
     const __amdgpu_buffer_rsrc_t krs =
-        make_rsrc(ws_k + ((int64_t)hk * mp + prow0) * KD, (uint32_t)((mp - prow0) * KD * 2));
+        make_rsrc(ws_k + ((int64_t)hk * mp + prow0 + jb) * KD, (uint32_t)((mp - prow0 - jb) * KD * 2));
     const __amdgpu_buffer_rsrc_t vrs =
-        make_rsrc(ws_vt + (int64_t)hk * D * mp + prow0, (uint32_t)(((int64_t)D * mp - prow0) * 2));
+        make_rsrc(ws_vt + (int64_t)hk * D * mp + prow0 + jb, (uint32_t)(((int64_t)D * mp - prow0 - jb) * 2));
 #pragma unroll
     for (int i = 0; i < KPW; ++i) koff[i] *= 2;   // bytes
 #pragma unroll
@@ -399,7 +465,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
         for (int r = 0; r < 16; ++r)
             if ((r >> 2) * 8 + (r & 3) > thr) acc[r] = -INFINITY;
     };
-    auto needs_mask = [&](int j0) { return j0 + kBN - 1 > qb; };
+    auto needs_mask = [&](int j0) { return j0 + kBN - 1 > qb; };   // j0: the tile's first key
     auto mask_tile = [&](f32x16& a0, f32x16& a1, int j0) {
         mask(a0, j0, 0);
         mask(a1, j0, 1);
@@ -451,8 +517,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
     {
         f32x16 s0, s1;
         qk_tile((const bf16*)kbufs, s0, s1);
-        if (needs_mask(0)) mask_tile(s0, s1, 0);
-        const float m0 = bf16_ceil(tile_max(s0, s1));   // key 0 is visible to every query
+        if (needs_mask(jb)) mask_tile(s0, s1, jb);
+        const float m0 = bf16_ceil(tile_max(s0, s1));   // key jb is visible to every query
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             s0[r] -= m0;
@@ -461,7 +527,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
         set_offset(m0);
         l_run = expo(s0, pb[0]) + expo(s1, pb[1]);
         qk_tile((const bf16*)(kbufs + L::K_BYTES), s1a, s1b);   // stale if n_kt == 1 (unused)
-        if (n_kt > 1 && needs_mask(kBN)) mask_tile(s1a, s1b, kBN);
+        if (n_kt > 1 && needs_mask(jb + kBN)) mask_tile(s1a, s1b, jb + kBN);
     }
     __syncthreads();   // every wave is done with K'(0) before K'(2) replaces it
     if (n_kt > 2) load_k(2, 0);
@@ -479,7 +545,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
         const bf16* ks2 = (const bf16*)(kbufs + (j & 1) * L::K_BYTES);   // K'(j+2); stale past the end
         const bf16* vs = (const bf16*)(vbufs + (j & 1) * L::V_BYTES);
         const bool more1 = j + 1 < n_kt, more2 = j + 2 < n_kt;
-        const int j2 = (j + 2) * kBN;
+        const int j2 = jb + (j + 2) * kBN;
         const bf16* kr0 = ks2 + il * L::KLD + half * 8;
         const bf16* kr1 = kr0 + 32 * L::KLD;
 
@@ -580,6 +646,58 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
         if (j + 1 < n_kt) step(j + 1, s2a, s2b, pb2, s1a, s1b, pb);
     }
 
+    if (nc > 1) {
+        // Key chunk of a split query tile: leave the partial (unnormalised
+        // O^T accumulators, offset, sum) in this unit's slot; the last chunk
+        // of the tile to finish (a ticket taken with release order; the others
+        // just leave) merges all of them and writes the tile.  The partials
+        // move as device-scope atomic stores and loads, which go past the
+        // CU's and XCD's caches to the coherent level, so no acquire fence is
+        // needed: one would invalidate the whole XCD L2, and with it the
+        // K'/V^T tiles every other workgroup there is reading.
+        constexpr int PW = D / 2 + 2;   // floats per lane
+        const size_t slot_floats = (size_t)NW * 64 * PW;
+        auto lane_ptr = [&](int unit) { return part + (size_t)unit * slot_floats + (size_t)wave * 64 * PW + lane; };
+        auto put = [&](float* p, float x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+        auto get = [&](const float* p) {
+            return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        float* mine = lane_ptr(b);
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) put(mine + (bb * 16 + r) * 64, o[bb][r]);
+        put(mine + (D / 2) * 64, m_run);
+        put(mine + (D / 2 + 1) * 64, l_run);
+        __shared__ int sh_last;
+        __syncthreads();   // every wave's stores are done
+        if (tid == 0) {
+            uint32_t* t = tk + r0 * n_hblk + hidx;
+            const bool last = __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) ==
+                              (uint32_t)nc - 1u;
+            if (last) __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // for the next forward
+            sh_last = last;
+        }
+        __syncthreads();
+        if (!sh_last) return;
+        // every chunk, this one included, from its slot and in chunk order, so
+        // the result does not depend on which chunk finished last
+        float mx = -INFINITY;
+        for (int c = 0; c < nc; ++c) mx = fmaxf(mx, get(lane_ptr((r0 + c) * n_hblk + hidx) + (D / 2) * 64));
+        l_run = 0.0f;
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) o[bb] = f32x16{};
+        for (int c = 0; c < nc; ++c) {
+            const float* src = lane_ptr((r0 + c) * n_hblk + hidx);
+            const float f = __builtin_amdgcn_exp2f(get(src + (D / 2) * 64) - mx);
+            l_run += f * get(src + (D / 2 + 1) * 64);
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[bb][r] += f * get(src + (bb * 16 + r) * 64);
+        }
+        m_run = mx;
+    }
     float l_tot;
     {
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
@@ -601,13 +719,125 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
     if (lse && half == 0) lse[(int64_t)h * m_tot + cs0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
+// Grid plan of the forward.  A grid of at most two workgroups per CU starts
+// whole, and the dispatcher gives block n_cu + k the CU of block k (round 2),
+// so the CU's time is that of its two units run side by side.  For such small
+// grids, cutting the long query tiles into key chunks evens out the CUs'
+// work, at the price of each chunk's own prologue and of the partials that
+// split tiles write and merge.  The plan compares the modelled longest CU
+// time, in key-tile steps, of the unsplit grid and of every chunk length,
+// with every sequence taken as long as the longest.  The model's constants
+// are fitted to kernel times measured on MI355X at 16k and 32k@5% with chunk
+// lengths from 8 to 26 tiles (RMS error 1.9 us; its choice lands within
+// 1.6 us of the best measured one): two workgroups on a CU each run 1.5x
+// slower, a unit's prologue costs 4 steps, and every unit of a split tile
+// adds 0.04 steps.
+struct FwdPlan {
+    int split_c = 0;        // key tiles per chunk, 0: no split
+    int units_per_seq = 0;  // grid units per sequence (query tiles or chunks)
+    int64_t nblk = 0;
+    int round2 = 0;         // first block of round 2, 0: no pairing
+};
+
+static FwdPlan plan_fwd_uncached(int n_seqs, int max_kept, int bmt, int n_hblk, int n_cu, bool can_split) {
+    constexpr double kShare = 1.5, kPrologue = 4.0, kSplitUnit = 0.04;
+    const int n_qtiles = (max_kept + bmt - 1) / bmt;
+    auto nkf = [&](int qt) { return (std::min((qt + 1) * bmt, max_kept) + kBN - 1) / kBN; };
+    auto finish = [&](FwdPlan p) {
+        p.round2 = p.nblk > n_cu && p.nblk <= 2 * (int64_t)n_cu && n_cu % n_hblk == 0 ? n_cu : 0;
+        return p;
+    };
+    FwdPlan base;
+    base.units_per_seq = n_qtiles;
+    base.nblk = (int64_t)n_qtiles * n_seqs * n_hblk;
+    if (!can_split || n_cu <= 0 || n_cu % n_hblk != 0 || base.nblk >= 2 * (int64_t)n_cu) return finish(base);
+    const int cap = std::min(2 * n_cu, kSplitCap);
+    std::vector<double> sz;
+    auto cost = [&](int c, int* units) -> double {
+        sz.clear();
+        int per_seq = 0, split_units = 0;
+        for (int qt = n_qtiles - 1; qt >= 0; --qt) {
+            const int nk = nkf(qt), nc = c > 0 ? (nk + c - 1) / c : 1;
+            if (nc > 1) split_units += nc;
+            per_seq += nc;
+            for (int ch = 0; ch < nc; ++ch) {
+                const int len = (ch + 1) * nk / nc - ch * nk / nc;
+                for (int h = 0; h < n_hblk; ++h) sz.push_back(len + kPrologue);
+            }
+        }
+        *units = per_seq;
+        const int64_t nblk = (int64_t)per_seq * n_seqs * n_hblk;
+        if (nblk > cap) return 1e30;
+        const int per = (int)sz.size();   // one sequence; the others repeat it
+        auto size_of = [&](int64_t lb) { return sz[lb % per]; };
+        const bool paired = nblk > n_cu;
+        const int64_t nu = paired ? (nblk - n_cu) / n_hblk : 0;
+        double worst = 0.0;
+        for (int64_t k = 0; k < std::min<int64_t>(nblk, n_cu); ++k) {
+            const double a = size_of(k);
+            double t = a;
+            if (paired && n_cu + k < nblk) {
+                const int64_t lb = n_cu + (nu - 1 - k / n_hblk) * n_hblk + k % n_hblk;
+                const double b = size_of(lb);
+                t = kShare * std::min(a, b) + std::fabs(a - b);
+            }
+            worst = std::max(worst, t);
+        }
+        return worst + kSplitUnit * split_units * n_seqs * n_hblk;
+    };
+    int units = 0;
+    double best = cost(0, &units);
+    FwdPlan p = base;
+    for (int c = 2; c < nkf(n_qtiles - 1); ++c) {
+        const double t = cost(c, &units);
+        if (t < best) {
+            best = t;
+            p.split_c = c;
+            p.units_per_seq = units;
+            p.nblk = (int64_t)units * n_seqs * n_hblk;
+        }
+    }
+    return finish(p);
+}
+
+// Plans are cached (a serving loop repeats the same shapes): the search
+// above takes tens of microseconds of host time.
+static FwdPlan plan_fwd(int n_seqs, int max_kept, int bmt, int n_hblk, int n_cu, bool can_split) {
+    struct Entry {
+        int key[6];
+        FwdPlan plan;
+    };
+    constexpr int kEntries = 16;
+    static std::mutex mu;
+    static Entry cache[kEntries];
+    static int n_used = 0, next = 0;
+    const int key[6] = {n_seqs, max_kept, bmt, n_hblk, n_cu, (int)can_split};
+    {
+        std::lock_guard<std::mutex> g(mu);
+        for (int i = 0; i < n_used; ++i)
+            if (std::equal(key, key + 6, cache[i].key)) return cache[i].plan;
+    }
+    const FwdPlan p = plan_fwd_uncached(n_seqs, max_kept, bmt, n_hblk, n_cu, can_split);
+    std::lock_guard<std::mutex> g(mu);
+    Entry& e = cache[next];
+    std::copy(key, key + 6, e.key);
+    e.plan = p;
+    next = (next + 1) % kEntries;
+    n_used = std::min(n_used + 1, kEntries);
+    return p;
+}
+
 template <int D, int HW, int NW>
 int launch_fwd(const AttnArgs& a, hipStream_t st) {
     constexpr int BMT = 32 * (NW / HW);
+    static_assert(NW == 4, "the key-split slots hold four waves");
     const int grp = a.hq / a.hkv;
     const int n_qtiles = (a.max_kept_seqlen + BMT - 1) / BMT;
     const int n_hblk = a.hkv * (grp / HW);
-    const int64_t nblk = (int64_t)n_qtiles * a.n_seqs * n_hblk;
+    int n_cu = 0;
+    if (const int e = device_cu_count(&n_cu)) return e;
+    const FwdPlan plan = plan_fwd(a.n_seqs, a.max_kept_seqlen, BMT, n_hblk, n_cu, a.ws_tk != nullptr);
+    const int64_t nblk = plan.nblk;
     // buffer offsets into one head's K' rows ((D+16)*2 B each) stay 32-bit
     if (nblk > 0x7fffffff || (int64_t)(D + kExtra) * 2 * a.mp >= ((int64_t)1 << 32)) return TG_ERR_UNSUPPORTED;
     const size_t shm = (size_t)AttnLds<D>::SMEM;
@@ -615,7 +845,8 @@ int launch_fwd(const AttnArgs& a, hipStream_t st) {
     if (const int e = set_dyn_lds_once((const void*)attn_fwd_kernel<D, HW, NW>, (int)shm, lds_set)) return e;
     hipLaunchKernelGGL((attn_fwd_kernel<D, HW, NW>), dim3((unsigned)nblk), dim3(NW * 64), shm, st, a.q,
                        a.q_stride, a.ws_k, a.ws_vt, a.ws_cs, (int)a.rope, a.gain, a.qk_scale_log2,
-                       a.cu_kept, a.n_seqs, a.m_tot, a.mp, a.hq, grp, n_qtiles, n_hblk, a.out, a.lse);
+                       a.cu_kept, a.n_seqs, a.m_tot, a.mp, a.hq, grp, n_qtiles, n_hblk, plan.round2,
+                       plan.split_c, plan.units_per_seq, a.max_kept_seqlen, a.ws_tk, a.ws_part, a.out, a.lse);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 
@@ -627,7 +858,7 @@ int launch_prep(const AttnArgs& a, hipStream_t st) {
     // one group per (64 padded rows, kv head); a.mp is a multiple of 64
     hipLaunchKernelGGL(attn_prep_kernel<D>, dim3((unsigned)(a.mp / 64), a.hkv), dim3(256), 0, st, a.k,
                        a.v, a.kv_stride, a.key_score, a.pos, a.cu_kept, a.n_seqs, a.m_tot, a.hkv, a.mp, fr,
-                       (int)a.rope, a.ws_k, a.ws_vt, a.ws_cs);
+                       (int)a.rope, a.ws_k, a.ws_vt, a.ws_cs, a.ws_tk);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 

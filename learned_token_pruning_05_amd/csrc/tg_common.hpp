@@ -63,10 +63,17 @@ struct AttnArgs {
     bf16* ws_vt;      // [Hkv][D][Mp]  values, transposed
     float2* ws_cs;    // [M][D/2]      (cos, sin) per kept token and frequency
     int64_t mp;       // padded row count
+    // key-split scratch (null when the workspace holds none): one ticket per
+    // split query tile, zeroed by the pre-pass and left at zero by every
+    // forward; one partial (O, offset, sum) slot per forward workgroup
+    uint32_t* ws_tk;
+    float* ws_part;
 };
+constexpr int kSplitCap = 512;   // workgroups of a key-split forward grid, at most
 int64_t attn_padded_rows(int n_seqs, int64_t m_tot);
+// off_split (optional): offset of the key-split scratch, 0 when none is reserved
 size_t attn_workspace_layout(int n_seqs, int64_t m_tot, int hkv, int d, size_t* off_k,
-                             size_t* off_vt, size_t* off_cs);
+                             size_t* off_vt, size_t* off_cs, size_t* off_split = nullptr);
 int launch_attn_prep(const AttnArgs& a, hipStream_t st);
 int launch_attn_fwd(const AttnArgs& a, hipStream_t st);
 
@@ -138,6 +145,26 @@ inline int set_dyn_lds_once(const void* fn, int bytes, std::atomic<uint64_t>& do
     if (bit && (done.load(std::memory_order_acquire) & bit)) return TG_OK;
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess) return TG_ERR_HIP;
     if (bit) done.fetch_or(bit, std::memory_order_release);
+    return TG_OK;
+}
+
+// Compute units of the current device, queried once per device (devices past
+// 63 are queried on every call).
+inline int device_cu_count(int* n_cu) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TG_ERR_HIP;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *n_cu = c;
+            return TG_OK;
+        }
+    }
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return TG_ERR_HIP;
+    if (dev >= 0 && dev < 64) cache[dev].store(c, std::memory_order_relaxed);
+    *n_cu = c;
     return TG_OK;
 }
 

@@ -553,6 +553,34 @@ def test_attention_prepare_forward_split():
     _check_attn(c3, o3.float().cpu().numpy(), l3.cpu().numpy(), 1e6, _sample_rows(ck, 16))
 
 
+@pytest.mark.parametrize("d,hq,hkv,lens", [(64, 4, 4, (2000, 1100)), (128, 8, 4, (2000, 1100)),
+                                           (128, 16, 2, (2000, 1100)), (64, 8, 1, (2000, 1100)),
+                                           (128, 16, 8, (2000,)), (128, 8, 4, (1100, 0, 700))])
+@pytest.mark.parametrize("rope", [0.0, 1e6])
+def test_attention_key_split(d, hq, hkv, lens, rope):
+    """Grids of at most two workgroups per CU (here 1024+ kept tokens in few
+    query tiles) cut their long query tiles into key chunks whose partials the
+    last chunk to finish merges; the chunk tickets left in the workspace must
+    be back at zero for the next forward.  Sampled rows of every sequence
+    (first, last and random ones) against the oracle, and a second forward over
+    the same prepared cache bit-identical to the first."""
+    q_lens = [min(60, n) for n in lens]
+    w = workloads.custom([n + 16 for n in lens], [ql + 16 for ql in q_lens], [n - ql for n, ql in zip(lens, q_lens)],
+                         n_q_heads=hq, n_kv_heads=hkv, head_dim=d, seed=d + hq + len(lens), tau=0.85)
+    _print_case(f"attn key split d={d} hq={hq} hkv={hkv} lens={lens} rope={rope}")
+    c = _attn_case(w)
+    ck = c["ck"]
+    maxlen = int(np.diff(ck).max())
+    q, k, v = _dev(c["q"]), _dev(c["k"]), _dev(c["v"])
+    sk, gain, pk, ckd = _dev(c["sk"]), _dev(c["gain"]), _i32(c["pk"]), _i32(ck)
+    ws = tg.tg_attn_prepare(k, v, sk, pk, ckd, rope_base=rope)
+    o1, l1 = tg.tg_attn_forward(q, gain, c["tau"], ckd, maxlen, hkv, ws, rope_base=rope)
+    o2, l2 = tg.tg_attn_forward(q, gain, c["tau"], ckd, maxlen, hkv, ws, rope_base=rope)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    _check_attn(c, o1.float().cpu().numpy(), l1.cpu().numpy(), rope, _sample_rows(ck, 40))
+
+
 def _padded_start(cu_s, s):
     return (int(cu_s) + 16 * s + 15) & ~15
 
