@@ -11,7 +11,9 @@
 // whole 128-B line of every row) go straight from memory into double-buffered
 // LDS.  With
 // enough tokens, 256 tokens per workgroup keeps the W1 re-reads (all of W1 per
-// workgroup, from L2) equal to the X stream; small inputs use 128.
+// workgroup, from L2) equal to the X stream; smaller inputs use 128, and
+// inputs too small to give every CU a 128-token tile use 64-token tiles whose
+// four waves each take a quarter of the hidden layer.
 //
 // fp32 path: plain FMA (no rounding of the residual), for fp32 residuals.
 #include "tg_common.hpp"
@@ -37,26 +39,30 @@ __device__ __forceinline__ float silu_f32(float a) {
 }
 
 
-// BM tokens per workgroup (BM / 64 row groups of waves x 2 hidden-column
-// groups); CB = 32-wide hidden blocks per wave, d_hid = 64 * CB.  Both operands
+// BM tokens per workgroup (BM / 64 row groups of waves x NCG hidden-column
+// groups); d_hid = 64 * CB, so a wave holds CBW = 2 CB / NCG 32-wide hidden
+// blocks.  Both operands
 // are K-contiguous, in two LDS slab buffers (one multiplied while the next
 // fills; rows padded by one 16-B chunk).  W1 slabs arrive by
 // global_load_lds_dwordx4 (1 KiB of consecutive LDS per instruction, the pad
 // slot reloading chunk 0).  With 256-token tiles X comes through registers,
 // loaded two slabs ahead and stored to LDS one slab ahead; with 128-token
 // tiles X takes the LDS-direct path as well, one slab ahead.
-template <int CB, int BM>
-__global__ __launch_bounds__(BM * 2, 1) void gate_bf16_kernel(
+template <int CB, int BM, int NCG>
+__global__ __launch_bounds__(BM * NCG, 1) void gate_bf16_kernel(
     const bf16* __restrict__ x, int64_t n, int d_model, int64_t x_stride,
     const bf16* __restrict__ w1, const float* __restrict__ b1, const float* __restrict__ w2,
     float b2, float* __restrict__ scores) {
-    constexpr int NT = BM * 2;                         // threads
+    constexpr int NT = BM * NCG;                       // threads
+    constexpr int CBW = 2 * CB / NCG;                  // 32-wide hidden blocks per wave
+    static_assert(CBW * NCG == 2 * CB, "hidden blocks split evenly over the column groups");
     constexpr int NW = NT / 64;                        // waves
     constexpr int NH = 64 * CB;
     constexpr int XI = BM * kRowChunks / 64;           // load instructions per X slab
     constexpr int WI = NH * kRowChunks / 64;           // ... per W1 slab
     constexpr int SLAB = (BM + NH) * kLdk;             // elements per slab buffer
-    constexpr int RED_BYTES = BM * 65 * 4;             // epilogue partial sums
+    constexpr int RED_LD = NCG * 32 + 1;               // epilogue partial sums: per token, one per lane
+    constexpr int RED_BYTES = BM * RED_LD * 4;
     constexpr int LDS_BYTES = kStages * SLAB * 2 > RED_BYTES ? kStages * SLAB * 2 : RED_BYTES;
     static_assert(BM * kRowChunks % 64 == 0 && NH * kRowChunks % 64 == 0, "whole load instructions");
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
@@ -64,7 +70,7 @@ __global__ __launch_bounds__(BM * 2, 1) void gate_bf16_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: wave tests branch on SCC
-    const int wr = wave >> 1, wc = wave & 1;
+    const int wr = wave / NCG, wc = wave % NCG;
     const int il = lane & 31, half = lane >> 5;
     const int64_t row0 = (int64_t)blockIdx.x * BM;
     const int rows = (int)min((int64_t)BM, n - row0);
@@ -129,21 +135,21 @@ __global__ __launch_bounds__(BM * 2, 1) void gate_bf16_kernel(
         for (int i = 0; i < XPT; ++i) *(u32x4*)(dst + xlds[i]) = xr[i];
     };
 
-    f32x16 acc[2][CB];
+    f32x16 acc[2][CBW];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x16{};
+        for (int cb = 0; cb < CBW; ++cb) acc[rb][cb] = f32x16{};
 
     const int nk = d_model / kBK;
-    // One slab: 4 k-steps of 2 x CB MFMAs.  Fragments of k-step ks+1 are read
+    // One slab: 4 k-steps of 2 x CBW MFMAs.  Fragments of k-step ks+1 are read
     // while k-step ks multiplies (two fragment sets); empty volatile asm
     // statements keep those reads ahead of the MFMAs and each MFMA in its
     // slot, so no MFMA waits on a read issued just before it.
     auto mma_slab = [&](int buf) {
         const bf16* xs = lds0 + buf * SLAB + (wr * 64 + il) * kLdk + half * 8;
-        const bf16* ws = lds0 + buf * SLAB + BM * kLdk + (wc * CB * 32 + il) * kLdk + half * 8;
-        constexpr int NF = 2 + CB;   // fragments per k-step: 2 of X, CB of W1
+        const bf16* ws = lds0 + buf * SLAB + BM * kLdk + (wc * CBW * 32 + il) * kLdk + half * 8;
+        constexpr int NF = 2 + CBW;   // fragments per k-step: 2 of X, CBW of W1
         auto frag = [&](int ks, int f) -> bf16x8 {
             return f < 2 ? *(const bf16x8*)(xs + f * 32 * kLdk + ks * 16)
                          : *(const bf16x8*)(ws + (f - 2) * 32 * kLdk + ks * 16);
@@ -155,18 +161,18 @@ __global__ __launch_bounds__(BM * 2, 1) void gate_bf16_kernel(
         for (int ks = 0; ks < kBK / 16; ++ks) {
             const int c = ks & 1;
 #pragma unroll
-            for (int m = 0; m < 2 * CB; ++m) {
+            for (int m = 0; m < 2 * CBW; ++m) {
                 if (ks + 1 < kBK / 16 && m < NF) {
                     fr[c ^ 1][m] = frag(ks + 1, m);
                     __asm__ volatile("" ::: "memory");
                 }
-                const int rb = m / CB, cb = m % CB;
+                const int rb = m / CBW, cb = m % CBW;
                 __asm__ volatile("" : "+v"(fr[c][rb]), "+v"(fr[c][2 + cb]));
                 acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[c][rb], fr[c][2 + cb], acc[rb][cb], 0, 0, 0);
             }
-            // fewer MFMAs than fragments (CB = 1): read the rest now
+            // fewer MFMAs than fragments (CBW = 1): read the rest now
 #pragma unroll
-            for (int f = 2 * CB; f < NF; ++f)
+            for (int f = 2 * CBW; f < NF; ++f)
                 if (ks + 1 < kBK / 16) fr[c ^ 1][f] = frag(ks + 1, f);
         }
     };
@@ -217,61 +223,67 @@ __global__ __launch_bounds__(BM * 2, 1) void gate_bf16_kernel(
     }
 
     // Epilogue: per token, sum over this wave's hidden units of SiLU(a + b1) * w2.
-    // acc[rb][cb][r] = hidden unit n = wc*CB*32 + cb*32 + il of token
+    // acc[rb][cb][r] = hidden unit n = wc*CBW*32 + cb*32 + il of token
     // wr*64 + rb*32 + (r/4)*8 + half*4 + r%4.
-    float bias1[CB], wout[CB];
+    float bias1[CBW], wout[CBW];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        const int nidx = wc * CB * 32 + cb * 32 + il;
+    for (int cb = 0; cb < CBW; ++cb) {
+        const int nidx = wc * CBW * 32 + cb * 32 + il;
         bias1[cb] = b1 ? b1[nidx] : 0.0f;
         wout[cb] = w2[nidx];
     }
-    float* red = (float*)lds_raw;   // [BM][65] partial sums, aliases the slab buffers
+    float* red = (float*)lds_raw;   // [BM][RED_LD] partial sums, aliases the slab buffers
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float p = 0.0f;
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) p += silu_f32(acc[rb][cb][r] + bias1[cb]) * wout[cb];
+            for (int cb = 0; cb < CBW; ++cb) p += silu_f32(acc[rb][cb][r] + bias1[cb]) * wout[cb];
             const int tok = wr * 64 + rb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-            red[tok * 65 + wc * 32 + il] = p;
+            red[tok * RED_LD + wc * 32 + il] = p;
         }
     }
     __syncthreads();
-    // two threads per token, 32 partials each, then one shuffle
+    // NCG threads per token, 32 partials each, then shuffles
     {
-        const int tok = tid >> 1, part = tid & 1;
+        const int tok = tid / NCG, part = tid % NCG;
         float sum = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 32; ++j) sum += red[tok * 65 + part * 32 + j];
-        sum += __shfl_xor(sum, 1, 64);
+        for (int j = 0; j < 32; ++j) sum += red[tok * RED_LD + part * 32 + j];
+#pragma unroll
+        for (int o = 1; o < NCG; o <<= 1) sum += __shfl_xor(sum, o, 64);
         if (part == 0 && row0 + tok < n) scores[row0 + tok] = sum + b2;
     }
 }
 
-template <int CB, int BM>
+template <int CB, int BM, int NCG>
 int launch_gate_tile(const bf16* x, int64_t n, int d_model, int64_t x_stride, const bf16* w1,
                      const float* b1, const float* w2, float b2, float* scores, hipStream_t st) {
     constexpr int NH = 64 * CB;
     constexpr size_t slab = (size_t)(BM + NH) * kLdk * 2;
-    constexpr size_t red = (size_t)BM * 65 * 4;
+    constexpr size_t red = (size_t)BM * (NCG * 32 + 1) * 4;
     constexpr size_t shm = kStages * slab > red ? kStages * slab : red;
     static std::atomic<uint64_t> lds_set{0};
-    if (const int e = set_dyn_lds_once((const void*)gate_bf16_kernel<CB, BM>, (int)shm, lds_set)) return e;
+    if (const int e = set_dyn_lds_once((const void*)gate_bf16_kernel<CB, BM, NCG>, (int)shm, lds_set)) return e;
     const dim3 grid((unsigned)((n + BM - 1) / BM));
-    hipLaunchKernelGGL((gate_bf16_kernel<CB, BM>), grid, dim3(BM * 2), shm, st, x, n, d_model, x_stride, w1,
-                       b1, w2, b2, scores);
+    hipLaunchKernelGGL((gate_bf16_kernel<CB, BM, NCG>), grid, dim3(BM * NCG), shm, st, x, n, d_model, x_stride,
+                       w1, b1, w2, b2, scores);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 
 template <int CB>
 int launch_gate_cb(const bf16* x, int64_t n, int d_model, int64_t x_stride, const bf16* w1,
                    const float* b1, const float* w2, float b2, float* scores, hipStream_t st) {
-    // 256-token tiles once there are at least two per CU (256 CUs), else 128
+    // 256-token tiles once there are at least two per CU (256 CUs); 64-token
+    // tiles of four waves (each 64 tokens x a quarter of the hidden layer)
+    // while 128-token tiles would leave CUs idle; else 128
     if (n >= (int64_t)256 * 256 * 2)
-        return launch_gate_tile<CB, 256>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
-    return launch_gate_tile<CB, 128>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
+        return launch_gate_tile<CB, 256, 2>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
+    if constexpr (CB % 2 == 0)
+        if (n < (int64_t)128 * 256)
+            return launch_gate_tile<CB, 64, 4>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
+    return launch_gate_tile<CB, 128, 2>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
 }
 
 // fp32 residuals: 4 tokens per workgroup staged in LDS, threads stride over
