@@ -33,14 +33,19 @@
  *    max_seqlen / max_kept_seqlen; document spans lie inside their sequences
  *    and budgets are >= 0; cu_kept equals tg_kept_counts of the rest; kept
  *    indices lie in their sequences, ascending; positions are >= 0 and
- *    strictly increase within a sequence.  A violation returns
- *    TG_ERR_INVALID_ARG and launches nothing.
+ *    strictly increase within a sequence; and a call that reads a prepared
+ *    cache (tg_attn_forward, tg_attn_decode, tg_attn_gate_grads) finds in the
+ *    header tg_attn_prepare left in it the same n_seqs, n_kept_total,
+ *    n_kv_heads, head_dim, rotary base and cu_kept (by a hash) as its own.
+ *    A violation returns TG_ERR_INVALID_ARG and launches nothing.
  *  - Calls are reentrant and thread-safe, except that calls of
  *    tg_topk_select_noalloc on one GPU share its scratch array and must not
  *    overlap (see there).  The only global state is, per
  *    kernel, an atomic mask of the devices on which its dynamic LDS limit has
- *    been raised (once per device, at that kernel's first call there), and
- *    the per-device address of tg_topk_select_noalloc's scratch array.
+ *    been raised (once per device, at that kernel's first call there), the
+ *    per-device address of tg_topk_select_noalloc's scratch array, a cache
+ *    of the per-device CU count, and a mutex-guarded cache of recent forward
+ *    grid plans.
  */
 #ifndef TOKENGATE_H
 #define TOKENGATE_H
@@ -258,7 +263,8 @@ int tg_gated_select(const void* x, int32_t x_dtype, int64_t n_tokens_total, int3
  * need for these sizes: the kept-only cache, plus, for 1024 or more kept
  * tokens with ceil(n_kept_total / 64) * n_kv_heads <= 512, the forward's
  * key-split scratch (512 tickets and 512 partial slots of 256 (D/2 + 2)
- * floats: 34.6 MB for D = 128, 17.8 MB for D = 64). */
+ * floats: 34.6 MB for D = 128, 17.8 MB for D = 64), plus a 256-B header in
+ * which the pre-pass records what it prepared. */
 size_t tg_attn_workspace_bytes(int32_t n_seqs, int64_t n_kept_total, int32_t n_kv_heads,
                                int32_t head_dim);
 

@@ -404,10 +404,36 @@ int attn_check(bool q_side, const void* q, int64_t q_row_stride, int32_t max_kep
     return TG_OK;
 }
 
+// Under TG_DEBUG, a call that reads a prepared cache first compares the
+// header the pre-pass left in it with its own arguments: the sizes, the rotary
+// base and a hash of cu_kept must be those the cache was prepared with.
+int debug_check_cache(const void* cache, int32_t n_seqs, int64_t n_kept_total, int32_t n_kv_heads,
+                      int32_t head_dim, double rope_base, const int32_t* cu_kept, void* stream) {
+    size_t off_hdr = 0;
+    attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, nullptr, nullptr, nullptr, nullptr,
+                          &off_hdr);
+    CacheHeader h{};
+    if (hipMemcpyAsync(&h, (const char*)cache + off_hdr, sizeof h, hipMemcpyDeviceToHost, (hipStream_t)stream) !=
+        hipSuccess)
+        return TG_ERR_HIP;
+    std::vector<int32_t> ck;
+    if (!fetch_i32(cu_kept, (int64_t)n_seqs + 1, ck, stream)) return TG_ERR_HIP;   // synchronises the stream
+    uint64_t hash = 0;
+    for (int64_t i = 0; i <= n_seqs; ++i) hash += cu_hash_term(ck[(size_t)i], i);
+    const bool rope = rope_base > 0.0;
+    if (h.magic != kCacheMagic || h.n_seqs != n_seqs || h.m_tot != n_kept_total || h.hkv != n_kv_heads ||
+        h.d != head_dim || (h.rope_base > 0.0) != rope || (rope && h.rope_base != rope_base) || h.cu_hash != hash)
+        return TG_ERR_INVALID_ARG;
+    return TG_OK;
+}
+
 void attn_fill(AttnArgs& a, int32_t n_seqs, int64_t n_kept_total, int32_t n_kv_heads,
                int32_t head_dim, double rope_base, const void* workspace) {
-    size_t off_k, off_vt, off_cs, off_split;
-    attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, &off_k, &off_vt, &off_cs, &off_split);
+    size_t off_k, off_vt, off_cs, off_split, off_hdr;
+    attn_workspace_layout(n_seqs, n_kept_total, n_kv_heads, head_dim, &off_k, &off_vt, &off_cs, &off_split,
+                          &off_hdr);
+    a.ws_hdr = (CacheHeader*)((char*)workspace + off_hdr);
+    a.rope_base = rope_base;
     a.n_seqs = n_seqs;
     a.m_tot = n_kept_total;
     a.hkv = n_kv_heads;
@@ -459,8 +485,12 @@ int tg_attn_forward(const void* q, int64_t q_row_stride, const float* head_gain,
     if (st == -1) return TG_OK;
     if (st != TG_OK) return st;
     if (!head_gain || !cu_kept) return TG_ERR_INVALID_ARG;
-    if (debug_on())
+    if (debug_on()) {
         if (const int e = debug_check_attn(n_seqs, n_kept_total, max_kept_seqlen, cu_kept, nullptr, stream)) return e;
+        if (const int e = debug_check_cache(workspace, n_seqs, n_kept_total, n_kv_heads, head_dim, rope_base, cu_kept,
+                                            stream))
+            return e;
+    }
     AttnArgs a{};
     attn_fill(a, n_seqs, n_kept_total, n_kv_heads, head_dim, rope_base, workspace);
     a.q = (const bf16*)q;
@@ -530,6 +560,10 @@ int tg_attn_decode(const void* q, int64_t q_row_stride, const int32_t* q_pos, co
     if (!cache || cache_bytes < cache_need || ((uintptr_t)cache & 255u) != 0) return TG_ERR_WORKSPACE;
     const size_t need = decode_workspace_bytes(n_seqs, max_kept_seqlen, n_q_heads, head_dim);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return TG_ERR_WORKSPACE;
+    if (debug_on())
+        if (const int e = debug_check_cache(cache, n_seqs, n_kept_total, n_kv_heads, head_dim, rope_base, cu_kept,
+                                            stream))
+            return e;
     const int64_t mp = attn_padded_rows(n_seqs, n_kept_total);
     // buffer offsets into one head's K' rows ((D+16)*2 B each) stay 32-bit
     if ((int64_t)(head_dim + 16) * 2 * mp >= ((int64_t)1 << 32)) return TG_ERR_UNSUPPORTED;
@@ -607,6 +641,10 @@ int tg_attn_gate_grads(const void* q, int64_t q_row_stride, const void* v, int64
     if (!cache || cache_bytes < cache_need || ((uintptr_t)cache & 255u) != 0) return TG_ERR_WORKSPACE;
     const size_t need = bwd_workspace_bytes(n_seqs, n_kept_total, max_kept_seqlen, n_q_heads, head_dim);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return TG_ERR_WORKSPACE;
+    if (debug_on())
+        if (const int e = debug_check_cache(cache, n_seqs, n_kept_total, n_kv_heads, head_dim, rope_base, cu_kept,
+                                            stream))
+            return e;
     const int64_t mp = attn_padded_rows(n_seqs, n_kept_total);
     // buffer offsets into one head's prepared rows stay 32-bit
     if ((int64_t)(head_dim + 16) * 2 * mp >= ((int64_t)1 << 32)) return TG_ERR_UNSUPPORTED;

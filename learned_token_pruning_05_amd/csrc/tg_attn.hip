@@ -79,7 +79,7 @@ static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 static size_t split_slot_floats(int d) { return (size_t)4 * 64 * (d / 2 + 2); }
 
 size_t attn_workspace_layout(int n_seqs, int64_t m_tot, int hkv, int d, size_t* off_k,
-                             size_t* off_vt, size_t* off_cs, size_t* off_split) {
+                             size_t* off_vt, size_t* off_cs, size_t* off_split, size_t* off_hdr) {
     const int64_t mp = attn_padded_rows(n_seqs, m_tot);
     const size_t kb = align256((size_t)hkv * mp * (d + 16) * 2);
     const size_t vb = align256((size_t)hkv * mp * d * 2);
@@ -93,7 +93,9 @@ size_t attn_workspace_layout(int n_seqs, int64_t m_tot, int hkv, int d, size_t* 
     const bool split = m_tot >= 1024 && ((m_tot + 63) / 64) * hkv <= kSplitCap;
     const size_t sb = split ? align256((size_t)kSplitCap * 4) + (size_t)kSplitCap * split_slot_floats(d) * 4 : 0;
     if (off_split) *off_split = split ? kb + vb + cb : 0;
-    return kb + vb + cb + sb;
+    if (off_hdr) *off_hdr = kb + vb + cb + sb;
+    static_assert(sizeof(CacheHeader) <= 256, "header fits its slot");
+    return kb + vb + cb + sb + 256;
 }
 
 namespace {
@@ -131,7 +133,8 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
     const bf16* __restrict__ k, const bf16* __restrict__ v, int64_t kv_stride,
     const float* __restrict__ key_score, const int* __restrict__ pos, const int* __restrict__ cu_kept,
     int n_seqs, int64_t m_tot, int hkv, int64_t mp, RopeFreqs fr, int rope, bf16* __restrict__ ws_k,
-    bf16* __restrict__ ws_vt, float2* __restrict__ ws_cs, uint32_t* __restrict__ ws_tk) {
+    bf16* __restrict__ ws_vt, float2* __restrict__ ws_cs, uint32_t* __restrict__ ws_tk,
+    CacheHeader* __restrict__ hdr, double rope_base) {
     constexpr int HALF = D / 2, KD = D + kExtra, NPAIR = D / 16, NC8 = D / 8;
     // V^T tile: row d holds the 64 columns vt_col(r) of this tile; 8-column
     // groups are XOR-swizzled by (d / 8) % 8 so the transposing 2-byte writes
@@ -141,8 +144,31 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
     const int tid = threadIdx.x;
     const int h = blockIdx.y;
     const int64_t p0 = (int64_t)blockIdx.x * 64;
-    if (ws_tk && blockIdx.x == 0 && h == 0)
-        for (int i = tid; i < kSplitCap; i += 256) ws_tk[i] = 0u;   // the forward's split tickets
+    if (blockIdx.x == 0 && h == 0) {
+        if (ws_tk)
+            for (int i = tid; i < kSplitCap; i += 256) ws_tk[i] = 0u;   // the forward's split tickets
+        // what was prepared, for the readers' checks under TG_DEBUG
+        __shared__ unsigned long long hsum[256];
+        unsigned long long acc = 0;
+        for (int i = tid; i <= n_seqs; i += 256) acc += cu_hash_term(cu_kept[i], i);
+        hsum[tid] = acc;
+        __syncthreads();
+        for (int o = 128; o > 0; o >>= 1) {
+            if (tid < o) hsum[tid] += hsum[tid + o];
+            __syncthreads();
+        }
+        if (tid == 0) {
+            CacheHeader c;
+            c.magic = kCacheMagic;
+            c.n_seqs = n_seqs;
+            c.hkv = hkv;
+            c.d = D;
+            c.m_tot = m_tot;
+            c.rope_base = rope_base;
+            c.cu_hash = hsum[0];
+            *hdr = c;
+        }
+    }
     if (tid < 64) {
         // last sequence whose padded start is <= row (or 0), then the token
         const int64_t r = p0 + tid;
@@ -858,7 +884,7 @@ int launch_prep(const AttnArgs& a, hipStream_t st) {
     // one group per (64 padded rows, kv head); a.mp is a multiple of 64
     hipLaunchKernelGGL(attn_prep_kernel<D>, dim3((unsigned)(a.mp / 64), a.hkv), dim3(256), 0, st, a.k,
                        a.v, a.kv_stride, a.key_score, a.pos, a.cu_kept, a.n_seqs, a.m_tot, a.hkv, a.mp, fr,
-                       (int)a.rope, a.ws_k, a.ws_vt, a.ws_cs, a.ws_tk);
+                       (int)a.rope, a.ws_k, a.ws_vt, a.ws_cs, a.ws_tk, a.ws_hdr, a.rope_base);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 

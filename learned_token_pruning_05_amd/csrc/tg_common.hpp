@@ -40,6 +40,20 @@ int launch_gather(const void* x, int esize, int d_model, int64_t x_stride, const
                   const int* kept_idx, int64_t m_tot, int n_seqs, const int* cu_seqlens,
                   const int* cu_kept, void* x_kept, float* s_kept, int* pos_kept, hipStream_t st);
 
+// What the pre-pass prepared, in the last 256 B of the workspace: the calls
+// that read the cache compare it with their own arguments under TG_DEBUG.
+struct CacheHeader {
+    uint32_t magic;
+    int32_t n_seqs, hkv, d;
+    int64_t m_tot;
+    double rope_base;
+    uint64_t cu_hash;   // sum over i of cu_hash_term(cu_kept[i], i), mod 2^64
+};
+constexpr uint32_t kCacheMagic = 0x4b564754u;
+__host__ __device__ __forceinline__ uint64_t cu_hash_term(int32_t x, int64_t i) {
+    return ((uint64_t)(uint32_t)x + 1u) * (2u * (uint64_t)i + 1u) * 0x9E3779B97F4A7C15ull;
+}
+
 struct AttnArgs {
     const bf16* q;
     const bf16* k;
@@ -68,12 +82,17 @@ struct AttnArgs {
     // forward; one partial (O, offset, sum) slot per forward workgroup
     uint32_t* ws_tk;
     float* ws_part;
+    CacheHeader* ws_hdr;
+    double rope_base;
 };
 constexpr int kSplitCap = 512;   // workgroups of a key-split forward grid, at most
+
 int64_t attn_padded_rows(int n_seqs, int64_t m_tot);
-// off_split (optional): offset of the key-split scratch, 0 when none is reserved
+// off_split (optional): offset of the key-split scratch, 0 when none is reserved;
+// off_hdr (optional): offset of the CacheHeader
 size_t attn_workspace_layout(int n_seqs, int64_t m_tot, int hkv, int d, size_t* off_k,
-                             size_t* off_vt, size_t* off_cs, size_t* off_split = nullptr);
+                             size_t* off_vt, size_t* off_cs, size_t* off_split = nullptr,
+                             size_t* off_hdr = nullptr);
 int launch_attn_prep(const AttnArgs& a, hipStream_t st);
 int launch_attn_fwd(const AttnArgs& a, hipStream_t st);
 

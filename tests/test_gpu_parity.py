@@ -1149,8 +1149,10 @@ def test_debug_metadata_checks(monkeypatch):
     """With TG_DEBUG=1 the calls check their device metadata on the host first:
     consistent metadata runs as usual (results against the oracle); a wrong
     cu_kept, a kept index outside its sequence, positions that do not
-    increase, or a sequence longer than max_kept_seqlen return
-    TG_ERR_INVALID_ARG and launch nothing."""
+    increase, a sequence longer than max_kept_seqlen, or a forward, decode or
+    gradient call whose cu_kept or rotary base differs from the prepare
+    call's (or whose workspace was never prepared) return TG_ERR_INVALID_ARG
+    and launch nothing."""
     _print_case("TG_DEBUG checks")
     monkeypatch.setenv("TG_DEBUG", "1")
     w = workloads.custom([300, 200], [20, 10], [100, 50], n_q_heads=4, n_kv_heads=2, head_dim=64, seed=61)
@@ -1184,3 +1186,28 @@ def test_debug_metadata_checks(monkeypatch):
                                   rope_base=1e6)
     torch.cuda.synchronize()
     _check_attn(c, out.float().cpu().numpy(), lse.cpu().numpy(), 1e6, np.arange(int(c["ck"][-1])))
+    # the readers of a prepared cache check the header the pre-pass left in
+    # it: another split of the same kept rows (valid on its own), another
+    # rotary base, or a workspace that was never prepared is refused
+    ck2 = c["ck"].copy()
+    ck2[1] -= 1
+    q, gain, ckd, ckd2 = _dev(c["q"]), _dev(c["gain"]), _i32(c["ck"]), _i32(ck2)
+    with pytest.raises(tg.TokenGateError, match="INVALID_ARG"):
+        tg.tg_attn_forward(q, gain, c["tau"], ckd2, short + 1, 2, cache, rope_base=1e6)
+    with pytest.raises(tg.TokenGateError, match="INVALID_ARG"):
+        tg.tg_attn_forward(q, gain, c["tau"], ckd, short + 1, 2, cache, rope_base=0.0)
+    with pytest.raises(tg.TokenGateError, match="INVALID_ARG"):
+        tg.tg_attn_forward(q, gain, c["tau"], ckd, short + 1, 2, torch.full_like(cache, 0xA5), rope_base=1e6)
+    qd = q[ckd.cpu().numpy()[1:] - 1].contiguous()          # one query per sequence
+    q_pos = _i32(np.asarray([int(c["pk"][i - 1]) + 1 for i in c["ck"][1:]]))
+    pk = _i32(c["pk"])
+    with pytest.raises(tg.TokenGateError, match="INVALID_ARG"):
+        tg.tg_attn_decode(qd, q_pos, gain, c["tau"], pk, ckd2, short + 1, 2, cache, rope_base=1e6)
+    tg.tg_attn_decode(qd, q_pos, gain, c["tau"], pk, ckd, short + 1, 2, cache, rope_base=1e6)
+    d_out = _dev(w.d_out(int(c["ck"][-1])))
+    with pytest.raises(tg.TokenGateError, match="INVALID_ARG"):
+        tg.tg_attn_gate_grads(q, _dev(c["v"]), _dev(c["sk"]), gain, c["tau"], ckd, short + 1, out, lse, d_out,
+                              cache, rope_base=2e6)
+    tg.tg_attn_gate_grads(q, _dev(c["v"]), _dev(c["sk"]), gain, c["tau"], ckd, short + 1, out, lse, d_out, cache,
+                          rope_base=1e6)
+    torch.cuda.synchronize()
