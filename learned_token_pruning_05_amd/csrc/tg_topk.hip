@@ -13,14 +13,14 @@
 // sequences all fit in 16 Ki tokens takes one launch, in 64 Ki tokens two (S,
 // below: one workgroup per sequence finds T and r, then W).  Longer sequences
 // take four launches, with no cross-workgroup waiting:
-//   C  zero the per-sequence counters (histogram, tickets, list length): a
+//   C  zero the per-sequence counters (histogram, ticket, list length): a
 //      kernel, not a memset, so that the call can be captured into a graph
 //      and replayed;
 //   H  every 4096-token chunk builds the LDS histogram of its document keys'
 //      top 12 bits and adds its non-zero bins to the sequence's histogram with
-//      atomics; the last chunk of the sequence to finish (a ticket taken with
-//      a vector atomic after a release fence) finds the bucket b1 holding T;
-//   F  every 2048-token chunk counts its always-kept tokens (outside the
+//      atomics;
+//   F  every 2048-token chunk finds the bucket b1 holding T from the summed
+//      histogram, counts its always-kept tokens (outside the
 //      document, or top bits above b1) and appends its bucket-b1 keys, with
 //      their indices, to the sequence's candidate list (space reserved with
 //      one atomic per chunk); the last chunk of the sequence to finish finds
@@ -57,10 +57,9 @@ constexpr int kCandCap = 4096;               // candidates the select step keeps
 // Per-sequence counters, zeroed by the C kernel at the start of every call.
 struct SeqCtl {
     uint32_t hist[kBins1];   // document keys' top-12-bit counts, summed by atomics
-    uint32_t ticket_h;       // histogram workgroups done
     uint32_t ticket_f;       // filter workgroups done
     uint32_t n_cand;         // length of the sequence's candidate list
-    uint32_t pad[61];
+    uint32_t pad[62];
 };
 static_assert(sizeof(SeqCtl) % 256 == 0, "counters stay 256-B aligned");
 
@@ -194,12 +193,8 @@ __global__ __launch_bounds__(256) void topk_clear_kernel(const int* __restrict__
 // ------------------------------------------------------------------ H ----
 __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(
     const float* __restrict__ scores, const int* __restrict__ cu, const int* __restrict__ db,
-    const int* __restrict__ de, const int* __restrict__ kd, SeqCtl* __restrict__ ctl,
-    SelState* __restrict__ sel) {
+    const int* __restrict__ de, const int* __restrict__ kd, SeqCtl* __restrict__ ctl) {
     __shared__ uint32_t h[kBins1];
-    __shared__ uint32_t sh_scan[kHistThreads / 64];
-    __shared__ uint32_t sh_out[2];
-    __shared__ int sh_last;
     const int s = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
     const SeqInfo q(s, cu, db, de, kd);
     const int c0 = c * kHistChunk;
@@ -225,15 +220,6 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(
         const uint32_t x = h[i];
         if (x) atomicAdd(&g->hist[i], x);
     }
-    const int nh = (q.n + kHistChunk - 1) / kHistChunk;
-    if (!last_to_arrive(&g->ticket_h, (uint32_t)nh, &sh_last)) return;
-    // the whole sequence's histogram is in: find the bucket of the k-th largest key
-    for (int i = tid; i < kBins1; i += kHistThreads)
-        h[i] = __hip_atomic_load(&g->hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    uint32_t b1, above1;
-    find_bucket<kBins1, kHistThreads>(h, (uint32_t)q.k, sh_scan, sh_out, &b1, &above1);
-    if (tid == 0) sel[s] = SelState{b1, above1};
 }
 
 // ------------------------------------------------------------------ F ----
@@ -342,7 +328,7 @@ __device__ void select_step(const SeqInfo& q, int s, int nch_write, const SelSta
 __global__ __launch_bounds__(kFiltThreads) void topk_filter_kernel(
     const float* __restrict__ scores, const int* __restrict__ cu, const int* __restrict__ db,
     const int* __restrict__ de, const int* __restrict__ kd, int nch_write, SeqCtl* __restrict__ ctl,
-    const SelState* __restrict__ sel, uint32_t* __restrict__ chunk_a0, uint2* __restrict__ cand_g,
+    uint32_t* __restrict__ chunk_a0, uint2* __restrict__ cand_g,
     SeqState* __restrict__ st, uint32_t* __restrict__ base_a, uint32_t* __restrict__ base_b) {
     __shared__ uint32_t cnt[2][kFiltItems * kFiltWaves];
     __shared__ int sh_last;
@@ -354,7 +340,6 @@ __global__ __launch_bounds__(kFiltThreads) void topk_filter_kernel(
     const int c0 = c * kChunk;
     if (!q.needs_select() || c0 >= q.n) return;
     SeqCtl* g = ctl + s;
-    const SelState se = sel[s];
     const float* sc = scores + q.start;
     float v[kFiltItems];
 #pragma unroll
@@ -362,6 +347,10 @@ __global__ __launch_bounds__(kFiltThreads) void topk_filter_kernel(
         const int i = c0 + j * kFiltThreads + tid;
         v[j] = i < q.n ? sc[i] : 0.0f;
     }
+    // the bucket b1 holding T, from the sequence's summed histogram (every
+    // workgroup of the sequence finds the same one)
+    SelState se;
+    find_bucket<kBins1, kFiltThreads>(g->hist, (uint32_t)q.k, L.sh_scan, L.sh_out, &se.b1, &se.above1);
     uint64_t mc[kFiltItems];
     uint32_t keys[kFiltItems];
 #pragma unroll
@@ -720,7 +709,7 @@ void launch_small(const float* scores, int n_seqs, const int* cu, const int* db,
 }
 
 struct TopkLayout {
-    size_t ctl, st, sel, a0, ba, bb, cand, total;
+    size_t ctl, st, a0, ba, bb, cand, total;
 };
 
 inline size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -731,7 +720,6 @@ TopkLayout topk_layout(int n_seqs, int64_t n_tokens, int max_seqlen) {
     size_t o = 0;
     L.ctl = o;  o += al256((size_t)n_seqs * sizeof(SeqCtl));
     L.st = o;   o += al256((size_t)n_seqs * sizeof(SeqState));
-    L.sel = o;  o += al256((size_t)n_seqs * sizeof(SelState));
     L.a0 = o;   o += al256((size_t)n_seqs * nch_w * 4);
     L.ba = o;   o += al256((size_t)n_seqs * nch_w * 4);
     L.bb = o;   o += al256((size_t)n_seqs * nch_w * 4);
@@ -759,7 +747,6 @@ __global__ __launch_bounds__(256) void random_scores_kernel(uint64_t seed, int64
 struct TopkPtrs {
     SeqCtl* ctl;
     SeqState* st;
-    SelState* sel;
     uint32_t *a0, *ba, *bb;
     uint2* cand;
 };
@@ -767,9 +754,8 @@ struct TopkPtrs {
 TopkPtrs topk_ptrs(void* ws, int n_seqs, int64_t n_tokens, int max_seqlen) {
     const TopkLayout L = topk_layout(n_seqs, n_tokens, max_seqlen);
     char* w = (char*)ws;
-    return TopkPtrs{(SeqCtl*)(w + L.ctl),  (SeqState*)(w + L.st), (SelState*)(w + L.sel),
-                    (uint32_t*)(w + L.a0), (uint32_t*)(w + L.ba), (uint32_t*)(w + L.bb),
-                    (uint2*)(w + L.cand)};
+    return TopkPtrs{(SeqCtl*)(w + L.ctl),  (SeqState*)(w + L.st),  (uint32_t*)(w + L.a0),
+                    (uint32_t*)(w + L.ba), (uint32_t*)(w + L.bb), (uint2*)(w + L.cand)};
 }
 
 // C, H, F: after these the per-sequence T, r and chunk offsets are in place.
@@ -781,10 +767,9 @@ void launch_select_passes(const float* scores, int n_seqs, int max_seqlen, const
     hipLaunchKernelGGL(topk_clear_kernel, dim3(n_seqs), dim3(256), 0, stm, cu_seqlens, doc_begin, doc_end, k_doc,
                        P.ctl);
     hipLaunchKernelGGL(topk_hist_kernel, dim3(nch_h, n_seqs), dim3(kHistThreads), 0, stm, scores, cu_seqlens,
-                       doc_begin, doc_end, k_doc, P.ctl, P.sel);
+                       doc_begin, doc_end, k_doc, P.ctl);
     hipLaunchKernelGGL(topk_filter_kernel, dim3(nch_w, n_seqs), dim3(kFiltThreads), 0, stm, scores, cu_seqlens,
-                       doc_begin, doc_end, k_doc, nch_w, P.ctl, (const SelState*)P.sel, P.a0, P.cand, P.st, P.ba,
-                       P.bb);
+                       doc_begin, doc_end, k_doc, nch_w, P.ctl, P.a0, P.cand, P.st, P.ba, P.bb);
 }
 
 }  // namespace

@@ -1009,7 +1009,7 @@ def _check_front_half(w, g, s_gpu, kept_gpu, xk_gpu, sk_gpu, pk_gpu, rows=None):
     return kept_ref, ck, np.asarray(sk_ref, dtype=np.float32), pk_ref
 
 
-@pytest.mark.parametrize("name", ["tiny", "16k", "varlen"])
+@pytest.mark.parametrize("name", ["tiny", "16k", "varlen", "128k"])
 def test_gated_select_against_oracle(name):
     """tg_gated_select (gate -> top-K -> gather in one call) against the oracle:
     scores, kept list, gathered rows, scores and positions."""
@@ -1029,7 +1029,7 @@ def test_gated_select_against_oracle(name):
                       rows)
 
 
-@pytest.mark.parametrize("name", ["tiny", "16k", "varlen"])
+@pytest.mark.parametrize("name", ["tiny", "16k", "varlen", "128k"])
 def test_gated_select_matches_separate_calls(name):
     """tg_gated_select (gate -> top-K -> gather in one call) gives the same bits as
     the three calls made one by one."""
@@ -1047,6 +1047,103 @@ def test_gated_select_matches_separate_calls(name):
     torch.cuda.synchronize()
     for a, b in ((s1, s2), (k1, k2), (xk1, xk2), (sk1, sk2), (pk1, pk2)):
         assert torch.equal(a, b)
+
+
+def _long_ragged_batch(total, seed):
+    """A ragged batch with one sequence beyond 64 Ki tokens: sequence
+    boundaries fall inside the gate's token tiles, and it mixes sequences that
+    select with ones that keep all or none of their document, an empty one and
+    one without a document.  Returns cu, doc_begin, doc_end, k_doc."""
+    r = np.random.default_rng(seed)
+    # (length, doc_begin, doc_end, k_doc); None: a selecting span drawn below
+    spec = [(1, 0, 1, 0), (255, None, None, None), (257, 0, 257, 257), (3, 1, 2, 1), (0, 0, 0, 0),
+            (70001, 0, 69745, 6000), (129, 60, 60, 5), (5000, None, None, None), (2, 0, 2, 1),
+            (1000, 100, 900, 0), (513, 0, 513, 600)]
+    spec.append((total - sum(t[0] for t in spec), None, None, None))
+    lens, b, e, k = [], [], [], []
+    for n, bb, ee, kk in spec:
+        if bb is None:
+            bb = int(r.integers(0, n // 8))
+            ee = n - int(r.integers(1, min(300, n // 2)))
+            kk = int(r.integers(1, ee - bb))
+        lens.append(n)
+        b.append(bb)
+        e.append(ee)
+        k.append(kk)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return cu, np.array(b, np.int32), np.array(e, np.int32), np.array(k, np.int32)
+
+
+@pytest.mark.parametrize("total,d_hid,ties", [(100_000, 64, False), (140_000, 256, False), (140_000, 128, True)],
+                         ids=["128-token-tiles", "256-token-tiles", "all-scores-tied"])
+def test_gated_select_long_ragged(total, d_hid, ties):
+    """tg_gated_select on ragged batches with a sequence beyond 64 Ki tokens
+    (the four-launch selector; gate tiles that span sequences; sequences that
+    keep all, none or part of their document): scores, kept list and gathered
+    rows equal the three separate calls bit for bit, the kept list equals
+    oracle.topk_select on the GPU scores, a garbage-filled workspace serves
+    two calls in a row, and three replays of a HIP graph of the call, on
+    different inputs, equal eager calls.  ties: w2 = 0, so every score is b2
+    and each selecting sequence keeps its first k document tokens."""
+    _print_case(f"gated select long ragged total={total} d_hid={d_hid} ties={ties}")
+    cu, b, e, kd = _long_ragged_batch(total, 21 + d_hid)
+    dev = torch.device("cuda:0")
+    d_model = 128
+    gen = torch.Generator(device="cpu").manual_seed(d_hid)
+    x = torch.randn(total, d_model, generator=gen).to(torch.bfloat16).to(dev)
+    w1 = (0.1 * torch.randn(d_hid, d_model, generator=gen)).to(torch.bfloat16).to(dev)
+    w2 = torch.zeros(d_hid) if ties else torch.randn(d_hid, generator=gen)
+    w2 = w2.to(dev)
+    b2 = 0.5
+    ck = tg.tg_kept_counts(cu, b, e, kd)
+    m, mx = int(ck[-1]), int(np.diff(cu).max())
+    assert mx > 65536
+    meta = [_i32(a) for a in (cu, b, e, kd, ck)]
+    s1 = tg.tg_gate_score(x, w1, None, w2, b2)
+    k1 = tg.tg_topk_select(s1, *meta, m, mx)
+    xk1, sk1, pk1 = tg.tg_gather_kept(x, s1, k1, meta[0], meta[4])
+    ws = torch.full((tg.tg_topk_workspace_bytes(len(cu) - 1, total, mx),), 0xA5, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        got = tg.tg_gated_select(x, w1, None, w2, b2, *meta, m, mx, workspace=ws)
+        torch.cuda.synchronize()
+        for a, c in zip((s1, k1, xk1, sk1, pk1), got):
+            assert torch.equal(a, c)
+    s_np = s1.cpu().numpy()
+    if ties:
+        assert np.all(s_np == np.float32(b2))
+    want, _ = oracle.topk_select(s_np, cu, b, e, kd)
+    np.testing.assert_array_equal(got[1].cpu().numpy(), want)
+
+    # the same call captured into a HIP graph (the counters are cleared by a
+    # kernel inside it), replayed on new inputs with eager calls in between
+    static_x = x.clone()
+    bufs = [torch.empty_like(t) for t in got]
+
+    def call(xin, out, wsp):
+        tg.tg_gated_select(xin, w1, None, w2, b2, *meta, m, mx, scores=out[0], kept_idx=out[1], x_kept=out[2],
+                           scores_kept=out[3], pos_kept=out[4], workspace=wsp)
+
+    ws_g = torch.empty_like(ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(static_x, bufs, ws_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(static_x, bufs, ws_g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        xr = (x.float() + 0.25 * rep * torch.randn(x.shape, generator=gen).to(dev)).to(x.dtype)
+        static_x.copy_(xr)
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = [torch.empty_like(t) for t in got]
+        call(xr, eager, ws)
+        torch.cuda.synchronize()
+        for a, c in zip(bufs, eager):
+            assert torch.equal(a, c), f"replay {rep} differs from the eager call"
 
 
 def test_gated_layer_graph_replay():
