@@ -234,10 +234,12 @@ int tg_gather_kept(const void* x, int32_t x_dtype, int32_t d_model, int64_t x_ro
  * The front half of the gated layer in one call: tg_gate_score, then
  * tg_topk_select on those scores, then tg_gather_kept (spke.com article,
  * gate-module and pruned-forward phases), after all three argument sets are
- * validated (nothing is launched if any check fails): six kernels back to
- * back on `stream` (gate; counter clear, histogram, filter, write of the
- * selection; row copy).  Results are bit-identical to the three calls made
- * one by one.  The call does no host synchronisation, no
+ * validated (nothing is launched if any check fails): the kernels of the
+ * three calls back to back on `stream`, except that with bf16 x and the
+ * four-launch selector (max_seqlen > 65536) the gate kernel also zeroes the
+ * selector's counters, so the selector's clear kernel is not launched (five
+ * kernels: gate; histogram, filter, write of the selection; row copy).
+ * Results are bit-identical to the three calls made one by one.  The call does no host synchronisation, no
  * allocation and no memset, so a caller can capture it (and the attention
  * after it) into one HIP graph and replay the whole layer as a single launch.
  *   x, x_dtype, n_tokens_total, d_model, x_row_stride, w1, b1, w2, b2, d_hid:

@@ -45,11 +45,11 @@ int gate_check(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d_model
 
 int gate_launch(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d_model, int64_t x_row_stride,
                 const void* w1, const float* b1, const float* w2, float b2, int32_t d_hid, float* scores,
-                void* stream) {
+                void* stream, const SelZero* zero = nullptr) {
     hipStream_t st = (hipStream_t)stream;
     if (x_dtype == TG_BF16)
         return launch_gate_bf16((const bf16*)x, n_tokens, d_model, x_row_stride, (const bf16*)w1, b1, w2, b2,
-                                d_hid, scores, st);
+                                d_hid, scores, st, zero);
     return launch_gate_f32((const float*)x, n_tokens, d_model, x_row_stride, (const float*)w1, b1, w2, b2, d_hid,
                            scores, st);
 }
@@ -343,14 +343,20 @@ int tg_gated_select(const void* x, int32_t x_dtype, int64_t n_tokens_total, int3
         if (const int e = debug_check_select(n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end,
                                              k_doc, cu_kept, n_kept_total, stream))
             return e;
+    // where the selector needs counters zeroed first, the bf16 gate does it,
+    // so the selector launches no clear kernel
+    SelZero sz{};
+    const bool gate_zeroes = sg == TG_OK && stk == TG_OK && x_dtype == TG_BF16 &&
+                             topk_sel_zero(n_seqs, n_tokens_total, max_seqlen, doc_begin, doc_end, k_doc, workspace,
+                                           &sz);
     if (sg == TG_OK) {
         const int st = gate_launch(x, x_dtype, n_tokens_total, d_model, x_row_stride, w1, b1, w2, b2, d_hid,
-                                   scores, stream);
+                                   scores, stream, gate_zeroes ? &sz : nullptr);
         if (st != TG_OK) return st;
     }
     if (stk == TG_OK) {
         const int st = launch_topk(scores, n_seqs, n_tokens_total, max_seqlen, cu_seqlens, doc_begin, doc_end,
-                                   k_doc, cu_kept, kept_idx, workspace, (hipStream_t)stream);
+                                   k_doc, cu_kept, kept_idx, workspace, (hipStream_t)stream, gate_zeroes);
         if (st != TG_OK) return st;
     }
     if (sga == TG_OK) {

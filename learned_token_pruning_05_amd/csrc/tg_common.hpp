@@ -20,18 +20,45 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Per-sequence counters that the top-K's four-launch form needs zeroed before
+// its histogram pass: `words` uint32 at base + s * stride for every sequence s
+// that selects (0 < min(k_doc, n_doc) < n_doc).  In tg_gated_select the gate's
+// workgroups zero them at their start, so the selector launches no clear
+// kernel.  base == nullptr: nothing to zero.
+struct SelZero {
+    uint32_t* base;
+    int64_t stride;
+    int words;
+    const int* db;
+    const int* de;
+    const int* kd;
+    int n_seqs;
+};
+
+__device__ __host__ __forceinline__ bool seq_selects(int db, int de, int kd) {
+    const int nd = de - db;
+    const int k = kd < nd ? kd : nd;
+    return k > 0 && k < nd;
+}
+
 // Launchers, one per kernel family.  Each returns TG_OK or TG_ERR_HIP.
 int launch_gate_bf16(const bf16* x, int64_t n, int d_model, int64_t x_stride, const bf16* w1,
                      const float* b1, const float* w2, float b2, int d_hid, float* scores,
-                     hipStream_t st);
+                     hipStream_t st, const SelZero* zero = nullptr);
 int launch_gate_f32(const float* x, int64_t n, int d_model, int64_t x_stride, const float* w1,
                     const float* b1, const float* w2, float b2, int d_hid, float* scores,
                     hipStream_t st);
 size_t topk_workspace_bytes(int n_seqs, int64_t n_tokens, int max_seqlen);
 int topk_max_seqlen();
+// counters_zeroed: the counters of topk_sel_zero are already zero (the gate
+// cleared them), so the four-launch form skips its clear kernel.
 int launch_topk(const float* scores, int n_seqs, int64_t n_tokens, int max_seqlen,
                 const int* cu_seqlens, const int* doc_begin, const int* doc_end, const int* k_doc,
-                const int* cu_kept, int* kept_idx, void* ws, hipStream_t st);
+                const int* cu_kept, int* kept_idx, void* ws, hipStream_t st, bool counters_zeroed = false);
+// Whether the selector for this batch needs counters zeroed beforehand, and
+// where they are in ws (false: it needs none).
+bool topk_sel_zero(int n_seqs, int64_t n_tokens, int max_seqlen, const int* doc_begin, const int* doc_end,
+                   const int* k_doc, void* ws, SelZero* out);
 size_t random_k_workspace_bytes(int n_seqs, int64_t n_tokens, int max_seqlen);
 int launch_random_k(uint64_t seed, int n_seqs, int64_t n_tokens, int max_seqlen, const int* cu_seqlens,
                     const int* doc_begin, const int* doc_end, const int* k_doc, const int* cu_kept,

@@ -15,6 +15,10 @@
 // inputs too small to give every CU a 128-token tile use 64-token tiles whose
 // four waves each take a quarter of the hidden layer.
 //
+// In tg_gated_select the bf16 kernel also zeroes the counters the top-K's
+// four-launch form needs (the workgroups share the sequences out, after their
+// scores are stored), so that form launches no clear kernel of its own.
+//
 // fp32 path: plain FMA (no rounding of the residual), for fp32 residuals.
 #include "tg_common.hpp"
 
@@ -52,7 +56,7 @@ template <int CB, int BM, int NCG>
 __global__ __launch_bounds__(BM * NCG, 1) void gate_bf16_kernel(
     const bf16* __restrict__ x, int64_t n, int d_model, int64_t x_stride,
     const bf16* __restrict__ w1, const float* __restrict__ b1, const float* __restrict__ w2,
-    float b2, float* __restrict__ scores) {
+    float b2, float* __restrict__ scores, SelZero sz) {
     constexpr int NT = BM * NCG;                       // threads
     constexpr int CBW = 2 * CB / NCG;                  // 32-wide hidden blocks per wave
     static_assert(CBW * NCG == 2 * CB, "hidden blocks split evenly over the column groups");
@@ -255,11 +259,19 @@ __global__ __launch_bounds__(BM * NCG, 1) void gate_bf16_kernel(
         for (int o = 1; o < NCG; o <<= 1) sum += __shfl_xor(sum, o, 64);
         if (part == 0 && row0 + tok < n) scores[row0 + tok] = sum + b2;
     }
+    // the selector's counters (the selector's kernels all run after this one)
+    if (sz.base)
+        for (int s = blockIdx.x; s < sz.n_seqs; s += gridDim.x)
+            if (seq_selects(sz.db[s], sz.de[s], sz.kd[s])) {
+                u32x4* p = (u32x4*)(sz.base + (int64_t)s * sz.stride);
+                for (int i = tid; i < sz.words / 4; i += NT) p[i] = u32x4{0u, 0u, 0u, 0u};
+            }
 }
 
 template <int CB, int BM, int NCG>
 int launch_gate_tile(const bf16* x, int64_t n, int d_model, int64_t x_stride, const bf16* w1,
-                     const float* b1, const float* w2, float b2, float* scores, hipStream_t st) {
+                     const float* b1, const float* w2, float b2, float* scores, const SelZero& sz,
+                     hipStream_t st) {
     constexpr int NH = 64 * CB;
     constexpr size_t slab = (size_t)(BM + NH) * kLdk * 2;
     constexpr size_t red = (size_t)BM * (NCG * 32 + 1) * 4;
@@ -268,22 +280,23 @@ int launch_gate_tile(const bf16* x, int64_t n, int d_model, int64_t x_stride, co
     if (const int e = set_dyn_lds_once((const void*)gate_bf16_kernel<CB, BM, NCG>, (int)shm, lds_set)) return e;
     const dim3 grid((unsigned)((n + BM - 1) / BM));
     hipLaunchKernelGGL((gate_bf16_kernel<CB, BM, NCG>), grid, dim3(BM * NCG), shm, st, x, n, d_model, x_stride,
-                       w1, b1, w2, b2, scores);
+                       w1, b1, w2, b2, scores, sz);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 
 template <int CB>
 int launch_gate_cb(const bf16* x, int64_t n, int d_model, int64_t x_stride, const bf16* w1,
-                   const float* b1, const float* w2, float b2, float* scores, hipStream_t st) {
+                   const float* b1, const float* w2, float b2, float* scores, const SelZero& sz,
+                   hipStream_t st) {
     // 256-token tiles once there are at least two per CU (256 CUs); 64-token
     // tiles of four waves (each 64 tokens x a quarter of the hidden layer)
     // while 128-token tiles would leave CUs idle; else 128
     if (n >= (int64_t)256 * 256 * 2)
-        return launch_gate_tile<CB, 256, 2>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
+        return launch_gate_tile<CB, 256, 2>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, sz, st);
     if constexpr (CB % 2 == 0)
         if (n < (int64_t)128 * 256)
-            return launch_gate_tile<CB, 64, 4>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
-    return launch_gate_tile<CB, 128, 2>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
+            return launch_gate_tile<CB, 64, 4>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, sz, st);
+    return launch_gate_tile<CB, 128, 2>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, sz, st);
 }
 
 // fp32 residuals: 4 tokens per workgroup staged in LDS, threads stride over
@@ -338,13 +351,14 @@ __global__ __launch_bounds__(256) void gate_f32_kernel(
 
 int launch_gate_bf16(const bf16* x, int64_t n, int d_model, int64_t x_stride, const bf16* w1,
                      const float* b1, const float* w2, float b2, int d_hid, float* scores,
-                     hipStream_t st) {
+                     hipStream_t st, const SelZero* zero) {
     if (n == 0) return TG_OK;
+    const SelZero sz = zero ? *zero : SelZero{};
     switch (d_hid) {
-        case 64: return launch_gate_cb<1>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
-        case 128: return launch_gate_cb<2>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
-        case 192: return launch_gate_cb<3>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
-        case 256: return launch_gate_cb<4>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, st);
+        case 64: return launch_gate_cb<1>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, sz, st);
+        case 128: return launch_gate_cb<2>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, sz, st);
+        case 192: return launch_gate_cb<3>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, sz, st);
+        case 256: return launch_gate_cb<4>(x, n, d_model, x_stride, w1, b1, w2, b2, scores, sz, st);
         default: return TG_ERR_UNSUPPORTED;
     }
 }

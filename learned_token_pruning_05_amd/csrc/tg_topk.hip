@@ -89,7 +89,7 @@ struct SeqInfo {
         de = e[s];
         k = max(0, min(kd[s], de - db));
     }
-    __device__ bool needs_select() const { return k > 0 && k < de - db; }
+    __device__ bool needs_select() const { return seq_selects(db, de, k); }
 };
 
 // LDS histogram add; a wave whose active lanes all hit one bin adds once.
@@ -758,14 +758,16 @@ TopkPtrs topk_ptrs(void* ws, int n_seqs, int64_t n_tokens, int max_seqlen) {
                     (uint32_t*)(w + L.ba), (uint32_t*)(w + L.bb), (uint2*)(w + L.cand)};
 }
 
-// C, H, F: after these the per-sequence T, r and chunk offsets are in place.
+// C (unless the counters are already zero), H, F: after these the
+// per-sequence T, r and chunk offsets are in place.
 void launch_select_passes(const float* scores, int n_seqs, int max_seqlen, const int* cu_seqlens,
                           const int* doc_begin, const int* doc_end, const int* k_doc, const TopkPtrs& P,
-                          hipStream_t stm) {
+                          bool counters_zeroed, hipStream_t stm) {
     const int nch_h = (max_seqlen + kHistChunk - 1) / kHistChunk;
     const int nch_w = (max_seqlen + kChunk - 1) / kChunk;
-    hipLaunchKernelGGL(topk_clear_kernel, dim3(n_seqs), dim3(256), 0, stm, cu_seqlens, doc_begin, doc_end, k_doc,
-                       P.ctl);
+    if (!counters_zeroed)
+        hipLaunchKernelGGL(topk_clear_kernel, dim3(n_seqs), dim3(256), 0, stm, cu_seqlens, doc_begin, doc_end,
+                           k_doc, P.ctl);
     hipLaunchKernelGGL(topk_hist_kernel, dim3(nch_h, n_seqs), dim3(kHistThreads), 0, stm, scores, cu_seqlens,
                        doc_begin, doc_end, k_doc, P.ctl);
     hipLaunchKernelGGL(topk_filter_kernel, dim3(nch_w, n_seqs), dim3(kFiltThreads), 0, stm, scores, cu_seqlens,
@@ -796,9 +798,19 @@ size_t topk_workspace_bytes(int n_seqs, int64_t n_tokens, int max_seqlen) {
 
 int topk_max_seqlen() { return kMaxChunks * kChunk; }
 
+bool topk_sel_zero(int n_seqs, int64_t n_tokens, int max_seqlen, const int* doc_begin, const int* doc_end,
+                   const int* k_doc, void* ws, SelZero* out) {
+    if (n_seqs == 0 || max_seqlen <= kMidMax) return false;
+    const TopkPtrs P = topk_ptrs(ws, n_seqs, n_tokens, max_seqlen);
+    static_assert(sizeof(SeqCtl) % 16 == 0, "whole 16-B stores");
+    *out = SelZero{(uint32_t*)P.ctl, (int64_t)(sizeof(SeqCtl) / 4), (int)(sizeof(SeqCtl) / 4), doc_begin, doc_end,
+                   k_doc, n_seqs};
+    return true;
+}
+
 int launch_topk(const float* scores, int n_seqs, int64_t n_tokens, int max_seqlen,
                 const int* cu_seqlens, const int* doc_begin, const int* doc_end, const int* k_doc,
-                const int* cu_kept, int* kept_idx, void* ws, hipStream_t stm) {
+                const int* cu_kept, int* kept_idx, void* ws, hipStream_t stm, bool counters_zeroed) {
     if (n_seqs == 0 || max_seqlen == 0) return TG_OK;
     if (max_seqlen <= kSmallMax) {
         if (max_seqlen <= 4096)
@@ -817,7 +829,8 @@ int launch_topk(const float* scores, int n_seqs, int64_t n_tokens, int max_seqle
             hipLaunchKernelGGL(topk_mid_kernel<64>, dim3(n_seqs), dim3(kSmallThreads), 0, stm, scores, cu_seqlens,
                                doc_begin, doc_end, k_doc, nch_w, P.st, P.ba, P.bb);
     } else {
-        launch_select_passes(scores, n_seqs, max_seqlen, cu_seqlens, doc_begin, doc_end, k_doc, P, stm);
+        launch_select_passes(scores, n_seqs, max_seqlen, cu_seqlens, doc_begin, doc_end, k_doc, P, counters_zeroed,
+                             stm);
     }
     hipLaunchKernelGGL(topk_write_kernel, dim3(nch_w, n_seqs), dim3(kWriteThreads), 0, stm, scores, cu_seqlens,
                        doc_begin, doc_end, k_doc, cu_kept, nch_w, (const SeqState*)P.st, (const uint32_t*)P.ba,
