@@ -177,44 +177,74 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
             const int mid = (lo + hi) >> 1;
             if (padded_seq_start(cu_kept[mid], mid) <= r) lo = mid; else hi = mid;
         }
-        const int64_t ps = padded_seq_start(cu_kept[lo], lo);
-        const int len = cu_kept[lo + 1] - cu_kept[lo];
-        tok[tid] = (r >= ps && r < ps + len) ? cu_kept[lo] + (int)(r - ps) : -1;
+        const int c0 = cu_kept[lo], c1 = cu_kept[lo + 1];
+        __asm__ volatile("" ::"v"(c0), "v"(c1));   // both loads issued before either is waited for
+        const int64_t ps = padded_seq_start(c0, lo);
+        tok[tid] = (r >= ps && r < ps + (c1 - c0)) ? c0 + (int)(r - ps) : -1;
     }
     __syncthreads();
 
-    // V rows, coalesced (lanes over 16-B chunks of a row), transposed into LDS
+    // Every global load of the tile is issued before the first is used (one
+    // memory latency per workgroup, not one per loop trip): rows outside the
+    // sequences read row 0 and are replaced by zeros afterwards.
+    // V rows, coalesced (lanes over 16-B chunks of a row); K' items (row,
+    // chunk pair p) take chunks p and p + D/16 (the rotate-half partners),
+    // lanes over p so loads and stores are coalesced.
     constexpr int VIT = 64 * NC8 / 256;
+    constexpr int KIT = 64 * NPAIR / 256;
+    constexpr int KIT1 = KIT > 0 ? KIT : 1;
+    const bool any_rows = m_tot > 0;   // else there is no row 0 to read
+    bf16x8 vx[VIT], kx1[KIT1], kx2[KIT1];
+    int kpos[KIT1];
+    float kscore[KIT1];
+    if (any_rows) {
+#pragma unroll
+        for (int i = 0; i < VIT; ++i) {
+            const int item = tid + 256 * i;
+            const int r = item / NC8, c8 = item % NC8;
+            const int64_t m = max(tok[r], 0);
+            vx[i] = *(const bf16x8*)(v + m * kv_stride + (int64_t)h * D + c8 * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < KIT1; ++i) {
+            const int item = min(tid + 256 * i, 64 * NPAIR - 1);
+            const int r = item / NPAIR, p = item % NPAIR;
+            const int64_t m = max(tok[r], 0);
+            const bf16* src = k + m * kv_stride + (int64_t)h * D;
+            kx1[i] = *(const bf16x8*)(src + p * 8);
+            kx2[i] = *(const bf16x8*)(src + HALF + p * 8);
+            kpos[i] = pos[m];
+            kscore[i] = key_score[m];
+        }
+    }
+
+    // V rows transposed into LDS
 #pragma unroll
     for (int i = 0; i < VIT; ++i) {
         const int item = tid + 256 * i;
         const int r = item / NC8, c8 = item % NC8;
-        const int m = tok[r];
-        const bf16x8 x = m >= 0 ? *(const bf16x8*)(v + (int64_t)m * kv_stride + (int64_t)h * D + c8 * 8) : bf16x8{};
+        const bf16x8 x = tok[r] >= 0 ? vx[i] : bf16x8{};
         const int col = (int)vt_col(r) ^ ((c8 & 7) * 8);   // d / 8 == c8 for all 8 values
 #pragma unroll
         for (int e = 0; e < 8; ++e) vs[(c8 * 8 + e) * 64 + col] = x[e];
     }
 
-    // K' rows: item (row, chunk pair p) rotates chunks p and p + D/16 (the
-    // rotate-half partners), lanes over p so loads and stores are coalesced
-    constexpr int KIT = 64 * NPAIR / 256;
+    // K' rows, rotated
 #pragma unroll
-    for (int i = 0; i < (KIT > 0 ? KIT : 1); ++i) {
+    for (int i = 0; i < KIT1; ++i) {
         const int item = tid + 256 * i;
         if (KIT == 0 && item >= 64 * NPAIR) break;
         const int r = item / NPAIR, p = item % NPAIR;
         const int m = tok[r];
         bf16x8 x1 = bf16x8{}, x2 = bf16x8{};
         if (m >= 0) {
-            const bf16* src = k + (int64_t)m * kv_stride + (int64_t)h * D;
-            x1 = *(const bf16x8*)(src + p * 8);
-            x2 = *(const bf16x8*)(src + HALF + p * 8);
+            x1 = kx1[i];
+            x2 = kx2[i];
             if (rope) {
                 // angle in turns, reduced in fp64 to [-1/2, 1/2]; the hardware
                 // sine and cosine take turns
                 float cn[8], sn[8];
-                const double ppos = (double)pos[m];
+                const double ppos = (double)kpos[i];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const double t = ppos * fr.rev[p * 8 + e];
@@ -248,7 +278,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
             bf16x8 extra = bf16x8{};
             if (m >= 0) {
                 bf16 sh, sl;
-                split_bf16(key_score[m], &sh, &sl);
+                split_bf16(kscore[i], &sh, &sl);
                 extra[0] = sh;
                 extra[1] = sl;
                 extra[2] = sh;
