@@ -394,8 +394,9 @@ int tg_attn_decode(const void* q, int64_t q_row_stride, const int32_t* q_pos, co
                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes tg_attn_gate_grads needs: the prepared queries and dL/dO
- * rows (2 Hq rows of D+16 bf16 per padded kept row) plus one fp32 per q head
- * and kept token and a few per-block partials. */
+ * rows (2 Hq rows of D+16 bf16 per padded kept row) plus four fp32 per q head
+ * and kept token (column sums of up to four query ranges) and a few
+ * per-block partials. */
 size_t tg_attn_gate_grads_workspace_bytes(int32_t n_seqs, int64_t n_kept_total, int32_t max_kept_seqlen,
                                           int32_t n_q_heads, int32_t head_dim);
 
@@ -411,7 +412,10 @@ size_t tg_attn_gate_grads_workspace_bytes(int32_t n_seqs, int64_t n_kept_total, 
  *     d_tau[0]   = -(1/tau) sum_hij dS_hij <R(q_i), R(k_j)> / (sqrt(D) tau)
  * (sums over each sequence's causal pairs).  P is recomputed from the
  * forward's lse; the q.k logits run on bf16 MFMA as in the forward, and
- * every sum is fp32.  Deterministic: no atomics.
+ * every sum is fp32.  Deterministic: no atomics.  When the kept keys give
+ * fewer key blocks than the GPU has CUs, each block's query rows are cut
+ * into up to four ranges (a dispatch model picks the count), and the ranges'
+ * partial sums are added in a fixed order.
  *   q, q_row_stride       the forward's queries
  *   v, kv_row_stride      the values tg_attn_prepare was given (kv head hk of
  *                         token m at v + m*kv_row_stride + hk*D)

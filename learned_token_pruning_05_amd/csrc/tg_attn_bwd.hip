@@ -33,11 +33,18 @@
 //           32x32x16 bf16 MFMA; the accumulator layout puts one key per lane,
 //           so C_hj is an in-lane sum over the query rows (no atomics,
 //           deterministic), and the workgroup leaves C_hj plus its partial
-//           sums of s_j C_hj and of dS Z;
-//   reduce  one launch: dL/ds over heads, and per head dL/dg and dL/dtau.
+//           sums of s_j C_hj and of dS Z.  When the key blocks are fewer than
+//           the CUs, each block's query tiles are cut into up to four ranges,
+//           one workgroup each, so no workgroup walks all of them;
+//   reduce  one launch: dL/ds over heads (and query ranges, in order), and
+//           per head dL/dg and dL/dtau.
 #include <math.h>
 
+#include <algorithm>
+#include <functional>
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "tg_common.hpp"
 
@@ -50,6 +57,7 @@ constexpr int kBwdKeys = 32 * kBwdWaves;   // keys per main workgroup
 constexpr int kBwdSlots = 4;               // LDS ring slots (tiles loaded 3 ahead)
 constexpr int kBwdQ = 64;                  // query rows per tile
 constexpr int kBwdExtra = 16;              // bias columns, as in K'
+constexpr int kBwdMaxSplit = 4;            // query ranges per key block, at most
 
 template <int D>
 struct BwdLds {
@@ -200,7 +208,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_main_kernel(
     const bf16* __restrict__ qc, const bf16* __restrict__ oc, const bf16* __restrict__ ws_k,
     const bf16* __restrict__ v, int64_t kv_stride, const float* __restrict__ key_score,
     const int* __restrict__ cu_kept, int n_seqs, int64_t m_tot, int hq, int grp, int64_t mp, int n_kt,
-    float* __restrict__ colsum, float2* __restrict__ part) {
+    int nsplit, float* __restrict__ colsum, float2* __restrict__ part) {
     using L = BwdLds<D>;
     constexpr int KD = L::KD;
     constexpr int KS = D / 16;   // k-steps of the data columns; one more for the extra columns
@@ -212,15 +220,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_main_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int il = lane & 31, half = lane >> 5;
 
+    // block = ((s * n_kt + kt) * nsplit + split) * hq + h: query range
+    // `split` of the key block kt of sequence s, for q head h (heads fastest)
     const int b = blockIdx.x;
     const int h = b % hq;
     const int rest = b / hq;
-    const int s = rest / n_kt;
-    const int kt = rest % n_kt;
+    const int split = rest % nsplit;
+    const int s = rest / nsplit / n_kt;
+    const int kt = rest / nsplit % n_kt;
     const int cs0 = cu_kept[s];
     const int ms = cu_kept[s + 1] - cs0;
     const int key0 = kt * kBwdKeys;
-    float2* const pout = part + ((int64_t)h * n_seqs + s) * n_kt + kt;
+    // partials split-major: part[h][split][s][kt], colsum[split][h][key]
+    float2* const pout = part + (((int64_t)h * nsplit + split) * n_seqs + s) * n_kt + kt;
+    float* const cout = colsum + ((int64_t)split * hq + h) * m_tot + cs0;
     if (key0 >= ms) {
         if (tid == 0) *pout = make_float2(0.0f, 0.0f);
         return;
@@ -252,14 +265,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_main_kernel(
     // query tiles from the one holding key0 to the end of the sequence; the
     // padded layout keeps every tile row inside this head's rows
     const int q_begin = key0 & ~(kBwdQ - 1);
-    const int n_qt = (ms - q_begin + kBwdQ - 1) / kBwdQ;
+    const int n_qt_all = (ms - q_begin + kBwdQ - 1) / kBwdQ;
+    // this split's tiles [t_lo, t_lo + n_qt), relative to q_begin; a split
+    // with none leaves zero partials
+    const int t_lo = (int)((int64_t)split * n_qt_all / nsplit);
+    const int n_qt = (int)((int64_t)(split + 1) * n_qt_all / nsplit) - t_lo;
     const __amdgpu_buffer_rsrc_t qrs =
         make_rsrc(qc + ((int64_t)h * mp + prow0) * KD, (uint32_t)((mp - prow0) * KD * 2));
     const __amdgpu_buffer_rsrc_t ors =
         make_rsrc(oc + ((int64_t)h * mp + prow0) * KD, (uint32_t)((mp - prow0) * KD * 2));
     const int n_per_tile = L::per_wave(wave);
     auto load_tile = [&](int t, int slot) {
-        const uint32_t so = (uint32_t)(q_begin + t * kBwdQ) * (KD * 2);
+        const uint32_t so = (uint32_t)(q_begin + (t_lo + t) * kBwdQ) * (KD * 2);
         for (int i = wave; i < L::INSTR; i += kBwdWaves) {
             const int sl = i * 64 + lane;
             const int r = sl / L::ROW, c = sl % L::ROW;
@@ -356,7 +373,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_main_kernel(
         wait_vm_le(min(kBwdSlots - 2, n_qt - 1 - t) * n_per_tile);
         __syncthreads();
         if (t + kBwdSlots - 1 < n_qt) load_tile(t + kBwdSlots - 1, (t + kBwdSlots - 1) % kBwdSlots);
-        const int q0 = q_begin + t * kBwdQ;
+        const int q0 = q_begin + (t_lo + t) * kBwdQ;
         const bf16* qt = qs + slot * L::T;
         const bf16* ot = os + slot * L::T;
         if (q0 + 31 >= kb0 && q0 < ms) {
@@ -395,7 +412,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_main_kernel(
     }
     float dgl = 0.0f;
     if (half == 0 && kvalid) {
-        colsum[(int64_t)h * m_tot + cs0 + kj] = cs_tot;
+        cout[kj] = cs_tot;
         dgl = key_score[cs0 + kj] * cs_tot;
     }
 #pragma unroll
@@ -418,19 +435,24 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_main_kernel(
 
 // -------------------------------------------------------------- reduce ----
 // One launch: blocks 0..n_ds-1 write dL/ds_j = sum_h g_h C_hj (every q head
-// sees every key of its sequence); block n_ds reduces the per-block partials
-// of each head to dL/dg_h and A_h, then dL/dtau = -(ln 2 / tau) sum_h A_h.
+// sees every key of its sequence; C_hj summed over the query ranges in
+// order); block n_ds reduces the per-block partials of each head to dL/dg_h
+// and A_h, then dL/dtau = -(ln 2 / tau) sum_h A_h.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ colsum,
                                                          const float2* __restrict__ part,
                                                          const float* __restrict__ gain, int hq, int64_t m_tot,
-                                                         int n_part, float tau, float* __restrict__ ds,
+                                                         int nsplit, int n_part, float tau, float* __restrict__ ds,
                                                          float* __restrict__ dg, float* __restrict__ dtau) {
     const int tid = threadIdx.x;
     if (blockIdx.x + 1 < gridDim.x) {
         const int64_t j = (int64_t)blockIdx.x * 256 + tid;
         if (j >= m_tot) return;
         float t = 0.0f;
-        for (int h = 0; h < hq; ++h) t = fmaf(gain[h], colsum[(int64_t)h * m_tot + j], t);
+        for (int h = 0; h < hq; ++h) {
+            float c = colsum[(int64_t)h * m_tot + j];
+            for (int sp = 1; sp < nsplit; ++sp) c += colsum[((int64_t)sp * hq + h) * m_tot + j];
+            t = fmaf(gain[h], c, t);
+        }
         ds[j] = t;
         return;
     }
@@ -475,10 +497,76 @@ BwdLayout bwd_layout(int n_seqs, int64_t m_tot, int max_kept, int hq, int d) {
     size_t o = 0;
     L.qc = o;     o += al((size_t)hq * mp * (d + kBwdExtra) * 2);
     L.oc = o;     o += al((size_t)hq * mp * (d + kBwdExtra) * 2);
-    L.colsum = o; o += al((size_t)hq * m_tot * 4);
-    L.part = o;   o += al((size_t)hq * n_seqs * (n_kt > 0 ? n_kt : 1) * 8);
+    L.colsum = o; o += al((size_t)kBwdMaxSplit * hq * m_tot * 4);
+    L.part = o;   o += al((size_t)kBwdMaxSplit * hq * n_seqs * (n_kt > 0 ? n_kt : 1) * 8);
     L.total = o;
     return L;
+}
+
+// Query ranges per key block.  A main workgroup fills its CU's LDS, so a
+// grid runs one workgroup per CU and later workgroups take the CUs that free
+// first, in block order.  The plan simulates that dispatch for 1..4 ranges
+// (every sequence taken as long as the longest; a workgroup costs its query
+// tiles plus 6 tiles of start-up) and keeps the count with the shortest
+// modelled finish, the smallest on a tie.  The start-up constant is fitted to
+// the gradient call measured on MI355X at 16k, 32k@5% and 32k@10% with 1-4
+// ranges (RMS error 1.7 us; the model picks the measured best in each case).
+// Grids of 2 n_cu key blocks or more are not cut.
+static int plan_bwd_uncached(int n_seqs, int max_kept, int hq, int n_cu) {
+    constexpr int kStartup = 6;
+    const int n_kt = (max_kept + kBwdKeys - 1) / kBwdKeys;
+    const int64_t nblk1 = (int64_t)n_kt * n_seqs * hq;
+    if (n_cu <= 0 || nblk1 == 0 || nblk1 >= 2 * (int64_t)n_cu) return 1;
+    int best = 1;
+    int64_t best_t = INT64_MAX;
+    std::vector<int64_t> slot;
+    for (int ns = 1; ns <= kBwdMaxSplit; ++ns) {
+        slot.assign(n_cu, 0);   // min-heap of the CUs' finish times
+        int64_t finish = 0;
+        for (int s = 0; s < n_seqs; ++s)
+            for (int kt = 0; kt < n_kt; ++kt) {
+                const int nq = (max_kept - kt * kBwdKeys + kBwdQ - 1) / kBwdQ;
+                for (int sp = 0; sp < ns; ++sp) {
+                    const int len = (sp + 1) * nq / ns - sp * nq / ns + kStartup;
+                    for (int h = 0; h < hq; ++h) {
+                        std::pop_heap(slot.begin(), slot.end(), std::greater<int64_t>());
+                        slot.back() += len;
+                        finish = std::max(finish, slot.back());
+                        std::push_heap(slot.begin(), slot.end(), std::greater<int64_t>());
+                    }
+                }
+            }
+        if (finish < best_t) {
+            best_t = finish;
+            best = ns;
+        }
+    }
+    return best;
+}
+
+static int plan_bwd(int n_seqs, int max_kept, int hq, int n_cu) {
+    struct Entry {
+        int key[4];
+        int nsplit;
+    };
+    constexpr int kEntries = 16;
+    static std::mutex mu;
+    static Entry cache[kEntries];
+    static int n_used = 0, next = 0;
+    const int key[4] = {n_seqs, max_kept, hq, n_cu};
+    {
+        std::lock_guard<std::mutex> g(mu);
+        for (int i = 0; i < n_used; ++i)
+            if (std::equal(key, key + 4, cache[i].key)) return cache[i].nsplit;
+    }
+    const int ns = plan_bwd_uncached(n_seqs, max_kept, hq, n_cu);
+    std::lock_guard<std::mutex> g(mu);
+    Entry& e = cache[next];
+    std::copy(key, key + 4, e.key);
+    e.nsplit = ns;
+    next = (next + 1) % kEntries;
+    n_used = std::min(n_used + 1, kEntries);
+    return ns;
 }
 
 template <int D>
@@ -492,7 +580,12 @@ int launch_bwd_d(const BwdArgs& a, hipStream_t st) {
     float2* part = (float2*)(w + W.part);
     const int grp = a.hq / a.hkv;
     const int n_kt = (a.max_kept_seqlen + kBwdKeys - 1) / kBwdKeys;
-    const int64_t nblk = (int64_t)n_kt * a.n_seqs * a.hq;
+    // small grids cut every key block's query tiles into ranges (plan_bwd);
+    // the reduce kernel adds the ranges' column sums and partials in order
+    int n_cu = 0;
+    if (const int e = device_cu_count(&n_cu)) return e;
+    const int nsplit = plan_bwd(a.n_seqs, a.max_kept_seqlen, a.hq, n_cu);
+    const int64_t nblk = (int64_t)n_kt * a.n_seqs * a.hq * nsplit;
     if (nblk > 0x7fffffff) return TG_ERR_UNSUPPORTED;
     static std::atomic<uint64_t> lds_set{0};   // before the first launch of the call
     if (const int e = set_dyn_lds_once((const void*)bwd_main_kernel<D>, (int)L::SMEM, lds_set)) return e;
@@ -501,11 +594,11 @@ int launch_bwd_d(const BwdArgs& a, hipStream_t st) {
                        a.n_seqs, a.m_tot, a.hq, a.mp, qc, oc);
     hipLaunchKernelGGL(bwd_main_kernel<D>, dim3((unsigned)nblk), dim3(kBwdThreads), L::SMEM, st, (const bf16*)qc,
                        (const bf16*)oc, a.ws_k, a.v, a.kv_stride, a.key_score, a.cu_kept, a.n_seqs, a.m_tot, a.hq,
-                       grp, a.mp, n_kt, colsum, part);
+                       grp, a.mp, n_kt, nsplit, colsum, part);
     const unsigned n_ds = (unsigned)((a.m_tot + 255) / 256);
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3(n_ds + 1), dim3(256), 0, st, (const float*)colsum,
-                       (const float2*)part, a.gain, a.hq, a.m_tot, a.n_seqs * n_kt, a.tau, a.d_score, a.d_gain,
-                       a.d_tau);
+                       (const float2*)part, a.gain, a.hq, a.m_tot, nsplit, nsplit * a.n_seqs * n_kt, a.tau,
+                       a.d_score, a.d_gain, a.d_tau);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 

@@ -775,17 +775,32 @@ def _check_grads(c, d_out, rope_base, got, scale=1.0):
     assert abs(g_t - dtau) <= scale * GRAD_TOL_G * mt + 1e-6
 
 
-@pytest.mark.parametrize("name", ["tiny", "16k", "128k", "varlen"])
+@pytest.mark.parametrize("name", ["tiny", "16k", "32k@10%", "128k", "varlen"])
 def test_gate_grads_configs(name):
     """Every d_score, d_gain and d_tau of the workload against the oracle (128k:
     8448 kept tokens, 16 q heads, the bench's launch; varlen: 8 packed
-    sequences)."""
+    sequences).  The small grids cut each key block's query tiles into ranges
+    (tiny and 16k into three, 32k@10% into two); 128k and varlen are not cut."""
     _print_case(f"gate grads {name}")
     w = workloads.by_name(name)
     c = _attn_case(w)
     d_out = w.d_out(int(c["ck"][-1]))
     got = _run_grads(c, d_out, w.rope_base)
     _check_grads(c, d_out, w.rope_base, got)
+
+
+@pytest.mark.parametrize("lens,q_lens,k_doc,hkv", [([900], [8], [500], 1), ([900, 40, 700], [8, 8, 8], [500, 30, 450], 2)],
+                         ids=["one-sequence", "ragged"])
+def test_gate_grads_four_query_ranges(lens, q_lens, k_doc, hkv):
+    """Grids small enough (2 q heads, at most 508 kept keys a sequence) that the
+    gradient call cuts each key block's query tiles into four ranges, some of
+    them empty for the short sequences: every output against the oracle."""
+    w = workloads.custom(lens, q_lens, k_doc, n_q_heads=2, n_kv_heads=hkv, head_dim=128, seed=29 + hkv, tau=0.9)
+    _print_case(f"gate grads four ranges {lens}")
+    c = _attn_case(w)
+    d_out = w.d_out(int(c["ck"][-1]))
+    got = _run_grads(c, d_out, 1e6)
+    _check_grads(c, d_out, 1e6, got)
 
 
 @pytest.mark.parametrize("d,hq,hkv", [(64, 4, 4), (64, 8, 2), (128, 16, 8), (128, 8, 1), (128, 16, 2)])
