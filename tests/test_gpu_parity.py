@@ -1089,9 +1089,11 @@ def _long_ragged_batch(total, seed):
     return cu, np.array(b, np.int32), np.array(e, np.int32), np.array(k, np.int32)
 
 
-@pytest.mark.parametrize("total,d_hid,ties", [(100_000, 64, False), (140_000, 256, False), (140_000, 128, True)],
-                         ids=["128-token-tiles", "256-token-tiles", "all-scores-tied"])
-def test_gated_select_long_ragged(total, d_hid, ties):
+@pytest.mark.parametrize("total,d_hid,ties,dt", [(100_000, 64, False, torch.bfloat16), (140_000, 256, False, torch.bfloat16),
+                                                 (140_000, 128, True, torch.bfloat16),
+                                                 (100_000, 64, False, torch.float32)],
+                         ids=["128-token-tiles", "256-token-tiles", "all-scores-tied", "fp32-x"])
+def test_gated_select_long_ragged(total, d_hid, ties, dt):
     """tg_gated_select on ragged batches with a sequence beyond 64 Ki tokens
     (the four-launch selector; gate tiles that span sequences; sequences that
     keep all, none or part of their document): scores, kept list and gathered
@@ -1099,14 +1101,16 @@ def test_gated_select_long_ragged(total, d_hid, ties):
     oracle.topk_select on the GPU scores, a garbage-filled workspace serves
     two calls in a row, and three replays of a HIP graph of the call, on
     different inputs, equal eager calls.  ties: w2 = 0, so every score is b2
-    and each selecting sequence keeps its first k document tokens."""
-    _print_case(f"gated select long ragged total={total} d_hid={d_hid} ties={ties}")
+    and each selecting sequence keeps its first k document tokens.  With bf16
+    x the gate kernel clears the selector's counters; with fp32 x the
+    selector's own clear kernel does."""
+    _print_case(f"gated select long ragged total={total} d_hid={d_hid} ties={ties} {dt}")
     cu, b, e, kd = _long_ragged_batch(total, 21 + d_hid)
     dev = torch.device("cuda:0")
     d_model = 128
     gen = torch.Generator(device="cpu").manual_seed(d_hid)
-    x = torch.randn(total, d_model, generator=gen).to(torch.bfloat16).to(dev)
-    w1 = (0.1 * torch.randn(d_hid, d_model, generator=gen)).to(torch.bfloat16).to(dev)
+    x = torch.randn(total, d_model, generator=gen).to(dt).to(dev)
+    w1 = (0.1 * torch.randn(d_hid, d_model, generator=gen)).to(dt).to(dev)
     w2 = torch.zeros(d_hid) if ties else torch.randn(d_hid, generator=gen)
     w2 = w2.to(dev)
     b2 = 0.5
