@@ -110,8 +110,9 @@ int tg_gate_score(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d_mo
                   int64_t x_row_stride, const void* w1, const float* b1, const float* w2,
                   float b2, int32_t d_hid, float* scores, void* stream);
 
-/* Workspace bytes tg_topk_select needs: per-sequence counters and state,
- * per-chunk histogram rows and counts, and 8 bytes per token for threshold
+/* Workspace bytes tg_topk_select needs: per-sequence counters (the
+ * first-level histogram, a ticket, the candidate count) and state, per-chunk
+ * counts and output offsets, and 8 bytes per token for threshold
  * candidates. */
 size_t tg_topk_workspace_bytes(int32_t n_seqs, int64_t n_tokens_total, int32_t max_seqlen);
 
