@@ -238,17 +238,21 @@ __global__ __launch_bounds__(kDecThreads, 2) void attn_decode_split_kernel(
 }
 
 // One workgroup of NT threads per (sequence, q head) merges the partials of
-// the sequence's chunks: the chunk maxima reduce to one m, then batches of NT
-// chunk weights 2^(m_c - m) go to LDS and NT / D lanes per channel sum the
-// weighted partial outputs of interleaved chunks (eight independent loads in
-// flight per lane), reduced through LDS at the end.  Many chunks per sequence
-// take NT = 1024, so fewer round trips per lane.  No visible key: O = 0,
+// the sequence's chunks; SUB = NT / D lanes per channel, lane `sub` of channel
+// d taking the chunks c = sub (mod SUB).  With J > 0 (at most SUB * J <= NT
+// chunks) the merge costs one memory round trip: every lane issues its J O
+// loads, thread c loads chunk c's (max, sum), and while the O loads are in
+// flight the maxima reduce to one m and thread c leaves the chunk weight
+// 2^(m_c - m) in LDS.  With J = 0 (longer sequences) batches of NT chunk
+// weights go through LDS in turn, eight O loads per lane in flight.  Either
+// way every lane sums its chunks in chunk order.  No visible key: O = 0,
 // LSE = -inf.
-template <int D, int NT>
+template <int D, int NT, int J>
 __global__ __launch_bounds__(NT) void attn_decode_combine_kernel(
     const int* __restrict__ cu_kept, int hq, int chunk_keys, int n_chunks, const float* __restrict__ part_o,
     const float2* __restrict__ part_ml, bf16* __restrict__ out, float* __restrict__ lse) {
     constexpr int SUB = NT / D;   // lanes per channel
+    static_assert(SUB * J <= NT, "one (max, sum) load per thread");
     __shared__ float wsh[NT];
     __shared__ float red[NT];
     const int s = blockIdx.x / hq, h = blockIdx.x % hq, tid = threadIdx.x;
@@ -273,29 +277,45 @@ __global__ __launch_bounds__(NT) void attn_decode_combine_kernel(
         return r;
     };
 
-    float m = -INFINITY;
-    for (int c = tid; c < nc; c += NT) m = fmaxf(m, ml[(int64_t)c * hq].x);
-    m = block_reduce(m, true);
-    float l = 0.0f, o = 0.0f;
     const int d = tid % D, sub = tid / D;
-    for (int c0 = 0; c0 < nc; c0 += NT) {
-        const int c = c0 + tid;
-        float wc = 0.0f;
-        if (c < nc && m != -INFINITY) {
-            const float2 v = ml[(int64_t)c * hq];
-            if (v.x != -INFINITY) {
-                wc = __builtin_amdgcn_exp2f(v.x - m);
-                l += wc * v.y;
-            }
+    float m, l = 0.0f, o = 0.0f;
+    if constexpr (J > 0) {
+        float ov[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int c = sub + SUB * j;
+            ov[j] = c < nc ? po[((int64_t)c * hq) * D + d] : 0.0f;
         }
-        wsh[tid] = wc;
-        __syncthreads();
-        const int nb = min(NT, nc - c0);
+        const float2 v = tid < nc ? ml[(int64_t)tid * hq] : make_float2(-INFINITY, 0.0f);
+        m = block_reduce(v.x, true);
+        const float wc = v.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(v.x - m);
+        wsh[tid] = wc;   // 0 past the last chunk
+        l = block_reduce(wc * v.y, false);   // its barriers also publish wsh
+#pragma unroll
+        for (int j = 0; j < J; ++j) o += wsh[sub + SUB * j] * ov[j];
+    } else {
+        float mx = -INFINITY;
+        for (int c = tid; c < nc; c += NT) mx = fmaxf(mx, ml[(int64_t)c * hq].x);
+        m = block_reduce(mx, true);
+        for (int c0 = 0; c0 < nc; c0 += NT) {
+            const int c = c0 + tid;
+            float wc = 0.0f;
+            if (c < nc && m != -INFINITY) {
+                const float2 v = ml[(int64_t)c * hq];
+                if (v.x != -INFINITY) {
+                    wc = __builtin_amdgcn_exp2f(v.x - m);
+                    l += wc * v.y;
+                }
+            }
+            wsh[tid] = wc;
+            __syncthreads();
+            const int nb = min(NT, nc - c0);
 #pragma unroll 8
-        for (int j = sub; j < nb; j += SUB) o += wsh[j] * po[((int64_t)(c0 + j) * hq) * D + d];
-        __syncthreads();
+            for (int j = sub; j < nb; j += SUB) o += wsh[j] * po[((int64_t)(c0 + j) * hq) * D + d];
+            __syncthreads();
+        }
+        l = block_reduce(l, false);
     }
-    l = block_reduce(l, false);
     red[tid] = o;
     __syncthreads();
     if (tid < D) {
@@ -306,6 +326,29 @@ __global__ __launch_bounds__(NT) void attn_decode_combine_kernel(
     }
     const int n_seqs = (int)gridDim.x / hq;
     if (lse && tid == 0) lse[(int64_t)h * n_seqs + s] = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+}
+
+// The combine launch for n_chunks chunks per sequence: 1024 threads from 128
+// chunks on, else 256; the one-round form with the smallest J that covers
+// them, up to 64 per lane.
+template <int D, int NT>
+void launch_combine_nt(const DecodeArgs& a, int chunk_keys, int n_chunks, const float* part_o,
+                       const float2* part_ml, hipStream_t st) {
+    constexpr int SUB = NT / D;
+    const int jn = (n_chunks + SUB - 1) / SUB;
+    const dim3 grid((unsigned)(a.n_seqs * a.hq)), block(NT);
+#define TG_COMBINE(JJ)                                                                                       \
+    hipLaunchKernelGGL((attn_decode_combine_kernel<D, NT, JJ>), grid, block, 0, st, a.cu_kept, a.hq,      \
+                       chunk_keys, n_chunks, part_o, part_ml, a.out, a.lse)
+    if (jn <= 4) TG_COMBINE(4);
+    else if (jn <= 8) TG_COMBINE(8);
+    else if (jn <= 16) TG_COMBINE(16);
+    else if (jn <= 24 && SUB * 24 <= NT) TG_COMBINE(24);
+    else if (jn <= 32 && SUB * 32 <= NT) TG_COMBINE(32);
+    else if (jn <= 48 && SUB * 48 <= NT) TG_COMBINE(48);
+    else if (jn <= 64 && SUB * 64 <= NT) TG_COMBINE(64);
+    else TG_COMBINE(0);
+#undef TG_COMBINE
 }
 
 template <int D>
@@ -335,13 +378,9 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t st) {
                            nsub, n_chunks, part_o, part_ml);
     }
     if (n_chunks >= 128)
-        hipLaunchKernelGGL((attn_decode_combine_kernel<D, 1024>), dim3((unsigned)(a.n_seqs * a.hq)), dim3(1024), 0,
-                           st, a.cu_kept, a.hq, chunk_keys, n_chunks, (const float*)part_o,
-                           (const float2*)part_ml, a.out, a.lse);
+        launch_combine_nt<D, 1024>(a, chunk_keys, n_chunks, part_o, part_ml, st);
     else
-        hipLaunchKernelGGL((attn_decode_combine_kernel<D, kDecThreads>), dim3((unsigned)(a.n_seqs * a.hq)),
-                           dim3(kDecThreads), 0, st, a.cu_kept, a.hq, chunk_keys, n_chunks,
-                           (const float*)part_o, (const float2*)part_ml, a.out, a.lse);
+        launch_combine_nt<D, kDecThreads>(a, chunk_keys, n_chunks, part_o, part_ml, st);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 

@@ -709,6 +709,19 @@ def test_decode_many_partials_ragged():
     _check_decode(c, q_new, q_pos, 1e6, out, lse)
 
 
+def test_decode_long_sequence_batched_merge():
+    """A 40,000-key sequence beside a short one: 625 one-tile partials, more than
+    the one-round merge covers, so the merge takes its batched form."""
+    lens = [40000, 130]
+    w = workloads.custom([n + 8 for n in lens], [8, 8], lens, n_q_heads=2, n_kv_heads=1, head_dim=128, seed=93,
+                         tau=0.93)
+    _print_case("decode long sequence")
+    c = _attn_case(w)
+    q_new, q_pos = _new_queries(c, 31, offset=2)
+    out, lse = _run_decode(c, q_new, q_pos, 1e6)
+    _check_decode(c, q_new, q_pos, 1e6, out, lse)
+
+
 def test_decode_position_mask_and_empty():
     """A query inside a sequence sees only the keys at or before its position; one
     before every key gets O = 0, LSE = -inf; decode at a kept token's own
