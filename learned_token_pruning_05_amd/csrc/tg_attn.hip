@@ -736,23 +736,49 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(
         }
         __syncthreads();
         if (!sh_last) return;
-        // every chunk, this one included, from its slot and in chunk order, so
-        // the result does not depend on which chunk finished last
-        float mx = -INFINITY;
-        for (int c = 0; c < nc; ++c) mx = fmaxf(mx, get(lane_ptr((r0 + c) * n_hblk + hidx) + (D / 2) * 64));
-        l_run = 0.0f;
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) o[bb] = f32x16{};
-        for (int c = 0; c < nc; ++c) {
-            const float* src = lane_ptr((r0 + c) * n_hblk + hidx);
-            const float f = __builtin_amdgcn_exp2f(get(src + (D / 2) * 64) - mx);
-            l_run += f * get(src + (D / 2 + 1) * 64);
+        if (nc == 2) {
+            // Two chunks: this one's partial is still in registers; every load of
+            // the other's is issued before the first is used.  Summed in chunk
+            // order, so the result does not depend on which chunk finished last.
+            const float* src = lane_ptr((r0 + 1 - chunk) * n_hblk + hidx);
+            const float mo = get(src + (D / 2) * 64), lo = get(src + (D / 2 + 1) * 64);
+            f32x16 ox[DB];
 #pragma unroll
             for (int bb = 0; bb < DB; ++bb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[bb][r] += f * get(src + (bb * 16 + r) * 64);
+                for (int r = 0; r < 16; ++r) ox[bb][r] = get(src + (bb * 16 + r) * 64);
+            const float mx = fmaxf(m_run, mo);
+            const float fs = __builtin_amdgcn_exp2f(m_run - mx), fo = __builtin_amdgcn_exp2f(mo - mx);
+            const bool first = chunk == 0;
+            const float f0 = first ? fs : fo, f1 = first ? fo : fs;
+            l_run = fmaf(f1, first ? lo : l_run, f0 * (first ? l_run : lo));
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float x0 = first ? o[bb][r] : ox[bb][r], x1 = first ? ox[bb][r] : o[bb][r];
+                    o[bb][r] = fmaf(f1, x1, f0 * x0);
+                }
+            m_run = mx;
+        } else {
+            // every chunk, this one included, from its slot and in chunk order, so
+            // the result does not depend on which chunk finished last
+            float mx = -INFINITY;
+            for (int c = 0; c < nc; ++c) mx = fmaxf(mx, get(lane_ptr((r0 + c) * n_hblk + hidx) + (D / 2) * 64));
+            l_run = 0.0f;
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb) o[bb] = f32x16{};
+            for (int c = 0; c < nc; ++c) {
+                const float* src = lane_ptr((r0 + c) * n_hblk + hidx);
+                const float f = __builtin_amdgcn_exp2f(get(src + (D / 2) * 64) - mx);
+                l_run += f * get(src + (D / 2 + 1) * 64);
+#pragma unroll
+                for (int bb = 0; bb < DB; ++bb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[bb][r] += f * get(src + (bb * 16 + r) * 64);
+            }
+            m_run = mx;
         }
-        m_run = mx;
     }
     float l_tot;
     {
