@@ -447,11 +447,26 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
     if (blockIdx.x + 1 < gridDim.x) {
         const int64_t j = (int64_t)blockIdx.x * 256 + tid;
         if (j >= m_tot) return;
+        // every column sum of a group of 16 heads is loaded before the first is
+        // used; the sums run in head order, each head's ranges in range order
+        constexpr int HB = 16;
         float t = 0.0f;
-        for (int h = 0; h < hq; ++h) {
-            float c = colsum[(int64_t)h * m_tot + j];
-            for (int sp = 1; sp < nsplit; ++sp) c += colsum[((int64_t)sp * hq + h) * m_tot + j];
-            t = fmaf(gain[h], c, t);
+        for (int h0 = 0; h0 < hq; h0 += HB) {
+            float x[kBwdMaxSplit][HB];
+#pragma unroll
+            for (int sp = 0; sp < kBwdMaxSplit; ++sp)
+#pragma unroll
+                for (int u = 0; u < HB; ++u)
+                    x[sp][u] = sp < nsplit && h0 + u < hq ? colsum[((int64_t)sp * hq + h0 + u) * m_tot + j] : 0.0f;
+#pragma unroll
+            for (int u = 0; u < HB; ++u) {
+                if (h0 + u >= hq) break;
+                float c = x[0][u];
+#pragma unroll
+                for (int sp = 1; sp < kBwdMaxSplit; ++sp)
+                    if (sp < nsplit) c += x[sp][u];
+                t = fmaf(gain[h0 + u], c, t);
+            }
         }
         ds[j] = t;
         return;
