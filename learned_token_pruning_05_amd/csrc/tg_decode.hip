@@ -115,20 +115,38 @@ __global__ __launch_bounds__(kDecThreads, 2) void attn_decode_split_kernel(
     };
     // this wave's load instructions per tile (what may stay in flight)
     const int per_tile = (L::K_INSTR - wave + kDecWaves - 1) / kDecWaves + (L::V_INSTR - wave + kDecWaves - 1) / kDecWaves;
+    // The chunk's key positions and the query elements are loaded before the
+    // tiles, so their round trip overlaps the tiles' (vector-memory counts
+    // retire in order: waiting for them does not wait for the tiles).  A
+    // thread holds at most one position (n_tiles * 64 <= kDecThreads) and two
+    // query items (grp * D / 2 <= 2 kDecThreads).
+    static_assert(kDecMaxSub * kDecKeys <= kDecThreads && kDecMaxGrp * D / 2 <= 2 * kDecThreads, "items per thread");
+    const int pkey = key_begin + tid;
+    const int pv = tid < n_tiles * kDecKeys && pkey < ms ? pos[cs0 + pkey] : INT32_MAX;
+    float qa[2], qb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int it = tid + u * kDecThreads;
+        qa[u] = qb[u] = 0.0f;
+        if (it < grp * HALF) {
+            const bf16* qr = q + (int64_t)s * q_stride + (int64_t)(h0 + it / HALF) * D;
+            qa[u] = (float)qr[it % HALF];
+            qb[u] = (float)qr[it % HALF + HALF];
+        }
+    }
     load_tile(0, 0);
     if (n_tiles > 1) load_tile(1, 1);
 
     // key positions of the chunk, and the rotated, scaled queries (fp32, not
     // rounded): item (head g, rotate-half pair f); the angle is reduced in fp64
     // to [-1/2, 1/2] turns and fed to the hardware sine and cosine
-    for (int i = tid; i < n_tiles * kDecKeys; i += kDecThreads) {
-        const int key = key_begin + i;
-        pk[i] = key < ms ? pos[cs0 + key] : INT32_MAX;
-    }
-    for (int it = tid; it < grp * HALF; it += kDecThreads) {
+    if (tid < n_tiles * kDecKeys) pk[tid] = pv;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int it = tid + u * kDecThreads;
+        if (it >= grp * HALF) break;
         const int g = it / HALF, f = it % HALF;
-        const bf16* qr = q + (int64_t)s * q_stride + (int64_t)(h0 + g) * D;
-        const float a = (float)qr[f], b = (float)qr[f + HALF];
+        const float a = qa[u], b = qb[u];
         float y1 = a, y2 = b;
         if (rope) {
             const double t = (double)qp * fr.rev[f];

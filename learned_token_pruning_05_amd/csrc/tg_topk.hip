@@ -415,6 +415,13 @@ __device__ ChunkKept chunk_kept(const SeqInfo& q, int c0, const float* __restric
     const int nd = q.de - q.db;
     const bool sel = q.needs_select();
     const bool all = !sel && q.k == nd;
+    // every score load issued before T and r are needed (one memory round
+    // trip); items past the sequence end read its last score, unused
+    float v[kWriteItems];
+    if (sel) {
+#pragma unroll
+        for (int j = 0; j < kWriteItems; ++j) v[j] = sc[min(c0 + j * kWriteThreads + tid, q.n - 1)];
+    }
     uint32_t T = 0, r = 0;
     if (sel) {
         T = st[s].T;
@@ -429,7 +436,7 @@ __device__ ChunkKept chunk_kept(const SeqInfo& q, int c0, const float* __restric
             if (i < q.db || i >= q.de) {
                 fa = true;
             } else if (sel) {
-                const uint32_t key = score_key(sc[i]);
+                const uint32_t key = score_key(v[j]);
                 fa = key > T;
                 fb = key == T;
             } else {
