@@ -233,27 +233,46 @@ struct SelectLds {
     uint32_t sh_out[2];
 };
 
-__device__ void select_step(const SeqInfo& q, int s, int nch_write, const SelState& se, uint32_t nc,
-                            const uint32_t* __restrict__ chunk_a0, const uint2* __restrict__ cg,
-                            SeqState* __restrict__ st, uint32_t* __restrict__ base_a,
-                            uint32_t* __restrict__ base_b, SelectLds& L) {
+__device__ void select_step(const SeqInfo& q, int s, int nch_write, const SelState& se,
+                            const uint32_t* __restrict__ n_cand, const uint32_t* __restrict__ chunk_a0,
+                            const uint2* __restrict__ cg, SeqState* __restrict__ st,
+                            uint32_t* __restrict__ base_a, uint32_t* __restrict__ base_b, SelectLds& L) {
     constexpr int NT = kFiltThreads;
     const int tid = threadIdx.x;
     const int nch = (q.n + kChunk - 1) / kChunk;
-    for (int i = tid; i < nch; i += NT) {
-        L.ca[i] = chunk_a0[(int64_t)s * nch_write + i];
-        L.cb[i] = 0u;
+    // One memory round trip for every input: the list length, the per-chunk
+    // counts and the list itself, read ahead up to the LDS capacity (inside
+    // the sequence's list region, which holds a slot per document token;
+    // entries past the length are not used).
+    const uint32_t n_doc = (uint32_t)(q.de - q.db);
+    constexpr int CPT = kMaxChunks / NT;   // per-chunk counts per thread, at most
+    uint32_t a0[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int i = u * NT + tid;
+        a0[u] = i < nch ? chunk_a0[(int64_t)s * nch_write + i] : 0u;
     }
-    // the list, coalesced, into LDS: every thread's loads issued together
+    constexpr int U = kCandCap / NT;
+    uint2 v[U];
+    const uint32_t n_read = min(n_doc, (uint32_t)kCandCap);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t i = u * NT + tid;
+        v[u] = i < n_read ? cg[i] : make_uint2(0u, 0u);
+    }
+    // the length last, so that waiting for it leaves nothing else waiting
+    const uint32_t nc = min(__hip_atomic_load(n_cand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), n_doc);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int i = u * NT + tid;
+        if (i < nch) {
+            L.ca[i] = a0[u];
+            L.cb[i] = 0u;
+        }
+    }
+    // the list, coalesced, into LDS
     const bool in_lds = nc <= kCandCap;
     if (in_lds) {
-        constexpr int U = kCandCap / NT;
-        uint2 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t i = u * NT + tid;
-            if (i < nc) v[u] = cg[i];
-        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t i = u * NT + tid;
@@ -393,9 +412,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_filter_kernel(
     const int nch = (q.n + kChunk - 1) / kChunk;
     if (!last_to_arrive(&g->ticket_f, (uint32_t)nch, &sh_last)) return;
     // every chunk's candidates are in
-    const uint32_t nc = __hip_atomic_load(&g->n_cand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    select_step(q, s, nch_write, se, min(nc, (uint32_t)(q.de - q.db)), chunk_a0, cand_g + q.start, st, base_a,
-                base_b, L);
+    select_step(q, s, nch_write, se, &g->n_cand, chunk_a0, cand_g + q.start, st, base_a, base_b, L);
 }
 
 // ------------------------------------------------------------------ W ----
