@@ -104,30 +104,59 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
             const int mid = (lo + hi) >> 1;
             if (padded_seq_start(cu_kept[mid], mid) <= r) lo = mid; else hi = mid;
         }
-        const int64_t ps = padded_seq_start(cu_kept[lo], lo);
-        const int len = cu_kept[lo + 1] - cu_kept[lo];
-        tok[tid] = (r >= ps && r < ps + len) ? cu_kept[lo] + (int)(r - ps) : -1;
+        const int c0 = cu_kept[lo], c1 = cu_kept[lo + 1];
+        __asm__ volatile("" ::"v"(c0), "v"(c1));   // both loads issued before either is waited for
+        const int64_t ps = padded_seq_start(c0, lo);
+        tok[tid] = (r >= ps && r < ps + (c1 - c0)) ? c0 + (int)(r - ps) : -1;
     }
     __syncthreads();
+    // Every load of the workgroup is issued before the first is used (one
+    // memory round trip after the token lookup): the dO and O row segments,
+    // the LSE, and the Q' items' q chunks and (cos, sin) rows.  The loads take
+    // no branch: a padding row reads row 0 (m_tot > 0 here), whose values are
+    // not used.
+    constexpr int KIT = 64 * NPAIR / 256;
+    constexpr int KIT1 = KIT > 0 ? KIT : 1;
+    const int r = tid >> 2, part = tid & 3;   // four threads per dO / O row
+    const int m = tok[r];
+    const int64_t mr = max(m, 0);
+    bf16x8 dx[NC8 / 4], oy[NC8 / 4];
     {
-        // four threads per row; instruction i of the row's threads covers
-        // chunks 4i..4i+3 (64 contiguous bytes): dO is copied into the data
-        // columns of dO' as it is read for Delta
-        const int r = tid >> 2, part = tid & 3;
-        const int m = tok[r];
+        // instruction i of the row's threads covers chunks 4i..4i+3 (64 contiguous bytes)
+        const bf16* dr = dout + mr * do_stride + (int64_t)h * D;
+        const bf16* orr = o + (mr * hq + h) * D;
+#pragma unroll
+        for (int i = 0; i < NC8 / 4; ++i) {
+            dx[i] = *(const bf16x8*)(dr + (4 * i + part) * 8);
+            oy[i] = *(const bf16x8*)(orr + (4 * i + part) * 8);
+        }
+    }
+    const float lse_r = lse[(int64_t)h * m_tot + mr];
+    bf16x8 qa1[KIT1], qa2[KIT1];
+    float4 csv[KIT1][4];
+#pragma unroll
+    for (int i = 0; i < KIT1; ++i) {
+        const int item = min(tid + 256 * i, 64 * NPAIR - 1);
+        const int r2 = item / NPAIR, p = item % NPAIR;
+        const int64_t m2 = max(tok[r2], 0);
+        const bf16* src = q + m2 * q_stride + (int64_t)h * D;
+        qa1[i] = *(const bf16x8*)(src + p * 8);
+        qa2[i] = *(const bf16x8*)(src + HALF + p * 8);
+        const float4* cs = (const float4*)(ws_cs + m2 * HALF + p * 8);
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2)   // (cos, sin) of frequencies 2 e2, 2 e2 + 1
+            csv[i][e2] = rope ? cs[e2] : make_float4(1.0f, 0.0f, 1.0f, 0.0f);
+    }
+    {
+        // dO is copied into the data columns of dO' as it is used for Delta
         bf16* odst = oc + ((int64_t)h * mp + p0 + r) * KD;
         float acc = 0.0f;
         if (m >= 0) {
-            const bf16* dr = dout + (int64_t)m * do_stride + (int64_t)h * D;
-            const bf16* orr = o + ((int64_t)m * hq + h) * D;
 #pragma unroll
             for (int i = 0; i < NC8 / 4; ++i) {
-                const int c = 4 * i + part;
-                const bf16x8 x = *(const bf16x8*)(dr + c * 8);
-                const bf16x8 y = *(const bf16x8*)(orr + c * 8);
-                *(bf16x8*)(odst + c * 8) = x;
+                *(bf16x8*)(odst + (4 * i + part) * 8) = dx[i];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+                for (int e = 0; e < 8; ++e) acc = fmaf((float)dx[i][e], (float)oy[i][e], acc);
             }
         } else {
 #pragma unroll
@@ -137,55 +166,49 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
         acc += __shfl_xor(acc, 2, 64);
         if (part == 0) {
             rowc[0][r] = acc;
-            rowc[1][r] = m >= 0 ? lse[(int64_t)h * m_tot + m] * kLog2e : 0.0f;
+            rowc[1][r] = m >= 0 ? lse_r * kLog2e : 0.0f;
         }
     }
     __syncthreads();
-    constexpr int KIT = 64 * NPAIR / 256;
 #pragma unroll
-    for (int i = 0; i < (KIT > 0 ? KIT : 1); ++i) {
+    for (int i = 0; i < KIT1; ++i) {
         const int item = tid + 256 * i;
         if (KIT == 0 && item >= 64 * NPAIR) break;
-        const int r = item / NPAIR, p = item % NPAIR;
-        const int m = tok[r];
+        const int r2 = item / NPAIR, p = item % NPAIR;
+        const int m2 = tok[r2];
         bf16x8 x1 = bf16x8{}, x2 = bf16x8{};
-        if (m >= 0) {
-            const bf16* src = q + (int64_t)m * q_stride + (int64_t)h * D;
-            const bf16x8 a1 = *(const bf16x8*)(src + p * 8);
-            const bf16x8 a2 = *(const bf16x8*)(src + HALF + p * 8);
-            const float4* cs = (const float4*)(ws_cs + (int64_t)m * HALF + p * 8);
+        if (m2 >= 0) {
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
-                float4 c = make_float4(1.0f, 0.0f, 1.0f, 0.0f);
-                if (rope) c = cs[e2];   // (cos, sin) of frequencies 2 e2 and 2 e2 + 1 of this chunk
+                const float4 c = csv[i][e2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const int e = 2 * e2 + u;
                     const float cn = u ? c.z : c.x, sn = u ? c.w : c.y;
-                    const float a = (float)a1[e], b = (float)a2[e];
+                    const float a = (float)qa1[i][e], b = (float)qa2[i][e];
                     x1[e] = (bf16)((a * cn - b * sn) * qk_scale_log2);
                     x2[e] = (bf16)((b * cn + a * sn) * qk_scale_log2);
                 }
             }
         }
-        const int64_t row = (int64_t)h * mp + p0 + r;
+        const int64_t row = (int64_t)h * mp + p0 + r2;
         bf16* dst = qc + row * KD;
         *(bf16x8*)(dst + p * 8) = x1;
         *(bf16x8*)(dst + HALF + p * 8) = x2;
         if (p == 0) {
             // Q' (g_hi, g_hi, g_lo, -LSE2_hi, -LSE2_lo), dO' (-Delta_hi, -Delta_lo)
             bf16x8 qx = bf16x8{}, ox = bf16x8{};
-            if (m >= 0) {
+            if (m2 >= 0) {
                 const float g = gain[h] * kLog2e;
                 const bf16 gh = (bf16)g;
                 qx[0] = gh;
                 qx[1] = gh;
                 qx[2] = (bf16)(g - (float)gh);
-                const float l2 = -rowc[1][r];
+                const float l2 = -rowc[1][r2];
                 const bf16 lh = (bf16)l2;
                 qx[3] = lh;
                 qx[4] = (bf16)(l2 - (float)lh);
-                const float dl = -rowc[0][r];
+                const float dl = -rowc[0][r2];
                 const bf16 dh = (bf16)dl;
                 ox[0] = dh;
                 ox[1] = (bf16)(dl - (float)dh);
