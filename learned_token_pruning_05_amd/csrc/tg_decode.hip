@@ -116,10 +116,11 @@ __global__ __launch_bounds__(kDecThreads, 2) void attn_decode_split_kernel(
     // this wave's load instructions per tile (what may stay in flight)
     const int per_tile = (L::K_INSTR - wave + kDecWaves - 1) / kDecWaves + (L::V_INSTR - wave + kDecWaves - 1) / kDecWaves;
     // The chunk's key positions and the query elements are loaded before the
-    // tiles, so their round trip overlaps the tiles' (vector-memory counts
-    // retire in order: waiting for them does not wait for the tiles).  A
-    // thread holds at most one position (n_tiles * 64 <= kDecThreads) and two
-    // query items (grp * D / 2 <= 2 kDecThreads).
+    // tile loads are issued, so they do not queue behind the tiles
+    // (vector-memory counts retire in order: a load issued after the tiles
+    // completes only after them).  A thread holds at most one position
+    // (n_tiles * 64 <= kDecThreads) and two query items (grp * D / 2 <=
+    // 2 kDecThreads).
     static_assert(kDecMaxSub * kDecKeys <= kDecThreads && kDecMaxGrp * D / 2 <= 2 * kDecThreads, "items per thread");
     const int pkey = key_begin + tid;
     const int pv = tid < n_tiles * kDecKeys && pkey < ms ? pos[cs0 + pkey] : INT32_MAX;
@@ -258,8 +259,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void attn_decode_split_kernel(
 // One workgroup of NT threads per (sequence, q head) merges the partials of
 // the sequence's chunks; SUB = NT / D lanes per channel, lane `sub` of channel
 // d taking the chunks c = sub (mod SUB).  With J > 0 (at most SUB * J <= NT
-// chunks) the merge costs one memory round trip: every lane issues its J O
-// loads, thread c loads chunk c's (max, sum), and while the O loads are in
+// chunks) the merge costs one memory round trip: thread c loads chunk c's
+// (max, sum), every lane then issues its J O loads, and while those are in
 // flight the maxima reduce to one m and thread c leaves the chunk weight
 // 2^(m_c - m) in LDS.  With J = 0 (longer sequences) batches of NT chunk
 // weights go through LDS in turn, eight O loads per lane in flight.  Either
@@ -298,13 +299,19 @@ __global__ __launch_bounds__(NT) void attn_decode_combine_kernel(
     const int d = tid % D, sub = tid / D;
     float m, l = 0.0f, o = 0.0f;
     if constexpr (J > 0) {
+        // the (max, sum) load first: vector-memory counts retire in order, so
+        // waiting for it leaves the O loads issued after it in flight
+        const float2 v = tid < nc ? ml[(int64_t)tid * hq] : make_float2(-INFINITY, 0.0f);
+        // straight-line loads (a chunk past the end reads chunk 0's slot, which
+        // every sequence has, and is replaced by 0), so the wait for v can
+        // leave them outstanding
         float ov[J];
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int c = sub + SUB * j;
-            ov[j] = c < nc ? po[((int64_t)c * hq) * D + d] : 0.0f;
+            const float x = po[((int64_t)(c < nc ? c : 0) * hq) * D + d];
+            ov[j] = c < nc ? x : 0.0f;
         }
-        const float2 v = tid < nc ? ml[(int64_t)tid * hq] : make_float2(-INFINITY, 0.0f);
         m = block_reduce(v.x, true);
         const float wc = v.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(v.x - m);
         wsh[tid] = wc;   // 0 past the last chunk
